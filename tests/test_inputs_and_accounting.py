@@ -1,0 +1,61 @@
+"""Input generator determinism and the work accounting against the pages' figures."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import sla2_inputs as I
+from sparse_linear_attention_pool_amd import accounting as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def test_topk_rounding_of_named_workloads():
+    assert [I.CONFIGS[c].topk for c in ("C0", "C1", "C2", "C3")] == [4, 26, 15, 35]
+    assert [I.CONFIGS[c].T for c in ("C0", "C1", "C2", "C3")] == [16, 512, 512, 1182]
+
+
+def test_saving_matches_the_sla2_page():
+    g = json.load(open(GOLDEN))["sla2_saving_at_97pct_sparsity"]
+    w = g["workload"]
+    T = (w["N"] + 63) // 64
+    topk = I.topk_from_fraction(w["sparse_frac"], T)
+    s = A.computation_saving(1, 1, w["N"], w["d"], topk)
+    assert abs(s - g["value"]) <= g["tolerance"]
+    # a linear branch counted at half the work, or the unrounded share, misses it
+    assert abs(1 - (A.sparse_flops_nominal(1, 1, w["N"], w["d"], topk) + A.linear_flops(1, 1, w["N"], w["d"]) / 2)
+               / A.dense_flops(1, 1, w["N"], w["d"]) - g["value"]) > g["tolerance"]
+
+
+def test_lut_flops_count_partial_blocks():
+    N, d = 130, 8          # blocks of 64, 64, 2
+    lut = np.array([[[0, 2], [1, 2], [0, 1]]])
+    got = A.sparse_flops_from_lut(lut, N, d)
+    want = 4 * d * (64 * 64 + 64 * 2 + 64 * 64 + 64 * 2 + 2 * 64 + 2 * 64)
+    assert got == want
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 3.0e38, 1e-40], np.float32)])
+    ours = I.round_to_bf16(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), theirs.view(np.uint32))
+
+
+def test_generator_is_deterministic_and_structured():
+    w = I.make_workload("C2", grid=(2, 4, 16), H=2)
+    a, b = I.generate(w), I.generate(w)
+    for key in ("q", "k", "v", "alpha", "wq", "wk"):
+        assert I.sha256(a[key]) == I.sha256(b[key])
+    assert a["q"].shape == (1, 2, 128, 128)
+    assert np.array_equal(I.round_to_bf16(a["q"]), a["q"])
+    assert np.all((a["alpha"] >= 0.3) & (a["alpha"] < 0.9))
+    # the positional part is shared by Q and K: they correlate strongly
+    c = np.corrcoef(a["q"][0, 0].ravel(), a["k"][0, 0].ravel())[0, 1]
+    assert c > 0.5
+    pe = I.sinusoidal_pe_3d((2, 4, 16), 128)
+    assert pe.shape == (128, 128) and np.all(np.abs(pe) <= 1)
