@@ -1,0 +1,156 @@
+/*
+ * sla2.h - C ABI of the SLA2 sparse-linear attention forward pass on MI355X (gfx950).
+ *
+ * The method is the one described on the pages
+ *   "SLA2: Sparse-Linear Attention with Learnable Routing and QAT" (AI summary page) and
+ *   "SLA: Beyond Sparsity in Diffusion Transformers via Fine-Tunable Sparse-Linear
+ *    Attention" (detailed summary page).
+ * Per (batch b, head h), with blocks of 64 consecutive tokens (T = ceil(N/64), the last
+ * block may be partial):
+ *   1. router (SLA2 page, section 4): mean-pool Q and the smoothed keys K~ = K - mean_N(K)
+ *      over each block, project the pooled rows with d x d matrices W_q, W_k, score every
+ *      (query block, key block) pair and keep the `topk` best key blocks of each query-block
+ *      row (hard Top-k, section 7) as the sparse set; all other key blocks go to the linear
+ *      branch.
+ *   2. sparse branch (SLA2 page, sections 3 and 5): softmax attention of each query over the
+ *      keys of its routed blocks only, online softmax, with Q.K^T optionally in FP8 e4m3
+ *      (one absmax scale per 64-token block) and P.V in the input precision.
+ *   3. linear branch (SLA page, sections 2-4): phi = softmax over the d features,
+ *      h_j = phi(K~_j)^T V_j and z_j = column sums of phi(K~_j) per key block;
+ *      O_l = phi(Q) H_i / (phi(Q) . Z_i + eps) with H_i, Z_i summed over the unrouted blocks.
+ *   4. mix (SLA2 page, section 3): O = alpha * O_s + (1 - alpha) * O_l, alpha in [0,1]^d
+ *      per head.
+ *
+ * Conventions for every entry point below:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronises.  Every call only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns.
+ *   - Token tensors are [B, H, N, d] row-major and contiguous.  Element type: float32
+ *     (SLA2_F32) or bf16 (SLA2_BF16, raw 16-bit patterns).
+ *   - Arguments are checked on the host before anything is launched; on failure the call
+ *     returns a negative sla2_status, launches nothing and sla2_last_error() describes it
+ *     (thread-local).  A failed kernel launch returns SLA2_ERR_HIP.
+ *   - Calls must be made in the order sla2_route -> sla2_linear_precompute ->
+ *     sla2_attention_fwd with the same params and tensors; each reads what the previous
+ *     wrote (k_mean, lut, q8/k8, h, z, h_sum, z_sum and the workspace).
+ *   - Results are deterministic: every reduction has a fixed order.
+ *   - Inputs must be finite.
+ */
+#ifndef SLA2_H
+#define SLA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA2_OK = 0,
+  SLA2_ERR_INVALID_ARG = -1,  /* a size, mode or pointer is out of range; nothing launched  */
+  SLA2_ERR_UNSUPPORTED = -2,  /* a valid combination this build does not implement          */
+  SLA2_ERR_HIP = -3           /* the HIP runtime reported an error                          */
+} sla2_status;
+
+typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
+
+/* Arithmetic of the sparse branch's Q.K^T (SLA2 page, section 5, low-bit attention). */
+typedef enum {
+  SLA2_QK_NATIVE = 0,   /* Q.K^T in the input precision                                    */
+  SLA2_QK_FP8_E4M3 = 1  /* OCP e4m3 codes, one absmax/448 scale per 64-token block (bf16)  */
+} sla2_qk_mode;
+
+typedef struct sla2_params {
+  int32_t B, H, N, d;   /* batch, heads, tokens (>= 1), head dim (64 or 128)                 */
+  int32_t block;        /* token block size b_q = b_kv; must be 64 (SLA page, section 2)     */
+  int32_t topk;         /* routed key blocks per query-block row, 1 <= topk <= T             */
+  int32_t smooth_k;     /* 1: subtract the per-(b,h) token mean from K (SLA2 page, sec. 6)   */
+  int32_t dtype;        /* sla2_dtype of q, k, v, o, h, vt                                   */
+  int32_t qk_mode;      /* sla2_qk_mode; FP8 needs dtype SLA2_BF16                           */
+  float eps;            /* linear-branch denominator guard, 1e-5 (SLA page, section 4)       */
+} sla2_params;
+
+/* Byte sizes of every caller-owned buffer for given params (0 = buffer unused). */
+typedef struct sla2_sizes {
+  size_t q_pool, k_pool, k_mean, lut, mask;
+  size_t q8, k8, q_scale, k_scale;
+  size_t h, z, h_sum, z_sum;
+  size_t o, lse;
+  size_t workspace;
+} sla2_sizes;
+
+typedef struct sla2_tensors {
+  /* ---- inputs ---- */
+  const void *q, *k, *v;   /* [B,H,N,d] dtype                                                */
+  const float *wq, *wk;    /* [d,d] row-major [in][out], shared by all heads; NULL = identity */
+  const float *alpha;      /* [H,d], values in [0,1]                                          */
+  /* ---- written by sla2_route ---- */
+  float *q_pool;           /* [B,H,T,d] block means of Q                                     */
+  float *k_pool;           /* [B,H,T,d] block means of K~ (= block means of K minus k_mean)   */
+  float *k_mean;           /* [B,H,d] token mean of K (zeros when smooth_k = 0)              */
+  int32_t *lut;            /* [B,H,T,topk] routed key blocks of each query block, ascending  */
+  uint8_t *mask;           /* [B,H,T,T] compressed mask: 1 = sparse branch, 0 = linear       */
+  uint8_t *q8;             /* FP8 mode: [B,H,T*64,d] e4m3 codes of Q / q_scale (pad rows 0)  */
+  float *q_scale;          /* FP8 mode: [B,H,T] absmax/448 of each Q block (1 if all zero)   */
+  /* ---- written by sla2_linear_precompute ---- */
+  uint8_t *k8;             /* FP8 mode: [B,H,T*64,d] e4m3 codes of K~ / k_scale              */
+  float *k_scale;          /* FP8 mode: [B,H,T]                                              */
+  void *h;                 /* [B,H,T,d,d] dtype, TRANSPOSED: h[j][c][a] = sum over the valid
+                              tokens t of block j of phi(K~_t)[a] * V_t[c]                   */
+  float *z;                /* [B,H,T,d] z[j][a] = sum_t phi(K~_t)[a]                          */
+  float *h_sum;            /* [B,H,d,d] sum of h over all blocks (same transposed layout)    */
+  float *z_sum;            /* [B,H,d]                                                        */
+  /* ---- written by sla2_attention_fwd ---- */
+  void *o;                 /* [B,H,N,d] dtype                                                */
+  float *lse;              /* [B,H,N] or NULL: natural log of the sum over the routed keys s of
+                              exp(q_t . K~_s / sqrt(d)) (dequantised operands in FP8 mode)   */
+  /* ---- scratch shared by the three calls ---- */
+  void *workspace;         /* sla2_sizes.workspace bytes, 256-byte aligned                    */
+} sla2_tensors;
+
+/* Host only, pure: fills *out with the byte size of every buffer for *p.
+ * Returns SLA2_OK or SLA2_ERR_INVALID_ARG / SLA2_ERR_UNSUPPORTED for params the calls
+ * below would reject. */
+int sla2_buffer_sizes(const sla2_params *p, sla2_sizes *out);
+
+/* Router (SLA2 page, section 4; SLA page, section 2 Q2 step 1) plus the FP8 quantisation
+ * of Q (SLA2 page, section 5).  Reads q, k, wq, wk; writes q_pool, k_pool, k_mean, lut,
+ * mask and, in FP8 mode, q8 and q_scale.  Block scores are
+ * s_ij = (q_pool_i W_q).(k_pool_j W_k) / sqrt(d), computed in fp64; ties in the Top-k go to
+ * the lower block index.  Needs T <= 4096. */
+int sla2_route(const sla2_params *p, const sla2_tensors *t, void *stream);
+
+/* Linear-branch precompute (SLA page, sections 2-3: h_j = phi(K_j)^T V_j, z_j =
+ * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v, k_mean; writes h, z,
+ * h_sum, z_sum, and in FP8 mode k8, k_scale; fills the workspace's staged V tiles. */
+int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *stream);
+
+/* Fused sparse + linear + mix forward (SLA2 page, sections 3 and 6: sparse attention over
+ * the M = 1 blocks, linear-attention statistics over the M = 0 blocks, O = alpha * O_s +
+ * (1 - alpha) * O_l).  Reads q, k (native mode), v, alpha, lut, q8/q_scale, k8/k_scale, h, z,
+ * h_sum, z_sum and the workspace; writes o and, if non-NULL, lse.  The linear statistics of
+ * query block i are formed as H_i = h_sum - sum over its routed j of h_j (and likewise Z_i),
+ * which equals the sum over its unrouted blocks. */
+int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream);
+
+/* Backward pass (SLA2 page, appendix A).  Not implemented: returns SLA2_ERR_UNSUPPORTED. */
+int sla2_attention_bwd(const sla2_params *p, const sla2_tensors *t, const void *dout,
+                       void *dq, void *dk, void *dv, float *dalpha, void *stream);
+
+/* Diagnostic: runs one wave (64 lanes) of one matrix-core instruction the kernels use,
+ * so a test can pin the operand lane layouts the kernels assume.
+ *   which = 0: v_mfma_f32_16x16x32_bf16, a/b = 64 lanes x 8 bf16 (16 bytes per lane)
+ *   which = 1: v_mfma_f32_16x16x128_f8f6f4 with e4m3 operands, 64 lanes x 32 bytes
+ * a, b: device arrays of the lane-major operand registers; d: device float[64*4], lane-major
+ * accumulator registers of the result (C = 0).  Returns SLA2_ERR_INVALID_ARG for other
+ * values of `which`. */
+int sla2_selftest_mfma(int which, const void *a, const void *b, float *d, void *stream);
+
+const char *sla2_status_string(int status);
+const char *sla2_last_error(void);   /* message of the last failed call on this thread */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLA2_H */

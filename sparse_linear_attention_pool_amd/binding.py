@@ -1,0 +1,206 @@
+"""ctypes binding of libsla2.so: argument marshalling only.
+
+Every step of the SLA2 forward runs in the library's HIP kernels; the
+functions here turn torch device tensors into the pointers of the C ABI
+declared in include/sla2.h, pass the current HIP stream, and raise on a
+non-zero status.  torch provides device memory and streams only.
+
+If the library has not been built this module raises at import: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla2.so")
+
+SLA2_OK, SLA2_ERR_INVALID_ARG, SLA2_ERR_UNSUPPORTED, SLA2_ERR_HIP = 0, -1, -2, -3
+SLA2_F32, SLA2_BF16 = 0, 1
+SLA2_QK_NATIVE, SLA2_QK_FP8_E4M3 = 0, 1
+
+ENTRY_POINTS = ("sla2_buffer_sizes", "sla2_route", "sla2_linear_precompute", "sla2_attention_fwd",
+                "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_status_string", "sla2_last_error")
+
+
+class SLA2Error(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("smooth_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("qk_mode", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+SIZE_FIELDS = ("q_pool", "k_pool", "k_mean", "lut", "mask", "q8", "k8", "q_scale", "k_scale",
+               "h", "z", "h_sum", "z_sum", "o", "lse", "workspace")
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in SIZE_FIELDS]
+
+
+TENSOR_FIELDS = ("q", "k", "v", "wq", "wk", "alpha", "q_pool", "k_pool", "k_mean", "lut", "mask",
+                 "q8", "q_scale", "k8", "k_scale", "h", "z", "h_sum", "z_sum", "o", "lse", "workspace")
+
+
+class Tensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in TENSOR_FIELDS]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m sparse_linear_attention_pool_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, T = ctypes.POINTER(Params), ctypes.POINTER(Tensors)
+    lib.sla2_buffer_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
+    for name in ("sla2_route", "sla2_linear_precompute", "sla2_attention_fwd"):
+        getattr(lib, name).argtypes = [P, T, ctypes.c_void_p]
+    lib.sla2_attention_bwd.argtypes = [P, T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sla2_selftest_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.sla2_status_string.restype = ctypes.c_char_p
+    lib.sla2_status_string.argtypes = [ctypes.c_int]
+    lib.sla2_last_error.restype = ctypes.c_char_p
+    lib.sla2_last_error.argtypes = []
+    for name in ENTRY_POINTS[:6]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+LIB_PATH = _LIB_PATH
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SLA2_OK:
+        raise SLA2Error(fn, status, lib.sla2_last_error().decode())
+
+
+def make_params(B: int, H: int, N: int, d: int, topk: int, dtype: str = "bf16", qk_mode: str = "native",
+                smooth_k: bool = True, eps: float = 1e-5) -> Params:
+    return Params(B=B, H=H, N=N, d=d, block=64, topk=topk, smooth_k=int(bool(smooth_k)),
+                  dtype={"f32": SLA2_F32, "bf16": SLA2_BF16}[dtype],
+                  qk_mode={"native": SLA2_QK_NATIVE, "fp8": SLA2_QK_FP8_E4M3}[qk_mode], eps=eps)
+
+
+def sla2_buffer_sizes(params: Params) -> Dict[str, int]:
+    s = Sizes()
+    _check("sla2_buffer_sizes", lib.sla2_buffer_sizes(ctypes.byref(params), ctypes.byref(s)))
+    return {f: int(getattr(s, f)) for f in SIZE_FIELDS}
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("SLA2 tensors must be contiguous")
+    return x.data_ptr()
+
+
+def _tensors(t: dict) -> Tensors:
+    unknown = set(t) - set(TENSOR_FIELDS)
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    return Tensors(**{f: _ptr(t.get(f)) for f in TENSOR_FIELDS})
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def sla2_route(params: Params, tensors: dict, stream=None) -> None:
+    tt = _tensors(tensors)
+    _check("sla2_route", lib.sla2_route(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
+
+
+def sla2_linear_precompute(params: Params, tensors: dict, stream=None) -> None:
+    tt = _tensors(tensors)
+    _check("sla2_linear_precompute",
+           lib.sla2_linear_precompute(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
+
+
+def sla2_attention_fwd(params: Params, tensors: dict, stream=None) -> None:
+    tt = _tensors(tensors)
+    _check("sla2_attention_fwd", lib.sla2_attention_fwd(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
+
+
+def sla2_attention_bwd(params: Params, tensors: dict, dout, dq, dk, dv, dalpha, stream=None) -> None:
+    tt = _tensors(tensors)
+    _check("sla2_attention_bwd",
+           lib.sla2_attention_bwd(ctypes.byref(params), ctypes.byref(tt), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(dalpha), _stream(stream)))
+
+
+def sla2_selftest_mfma(which: int, a, b, d, stream=None) -> None:
+    _check("sla2_selftest_mfma", lib.sla2_selftest_mfma(which, _ptr(a), _ptr(b), _ptr(d), _stream(stream)))
+
+
+# --------------------------------------------------------------------------------------
+# device buffers (torch allocations sized by sla2_buffer_sizes)
+# --------------------------------------------------------------------------------------
+def allocate(params: Params, device="cuda", with_lse: bool = False) -> dict:
+    """Allocate every output and scratch buffer the three calls need, on `device`."""
+    import torch
+    sz = sla2_buffer_sizes(params)
+    B, H, N, d = params.B, params.H, params.N, params.d
+    T = (N + 63) // 64
+    el = torch.bfloat16 if params.dtype == SLA2_BF16 else torch.float32
+    out = {
+        "q_pool": torch.empty((B, H, T, d), dtype=torch.float32, device=device),
+        "k_pool": torch.empty((B, H, T, d), dtype=torch.float32, device=device),
+        "k_mean": torch.empty((B, H, d), dtype=torch.float32, device=device),
+        "lut": torch.empty((B, H, T, params.topk), dtype=torch.int32, device=device),
+        "mask": torch.empty((B, H, T, T), dtype=torch.uint8, device=device),
+        "h": torch.empty((B, H, T, d, d), dtype=el, device=device),
+        "z": torch.empty((B, H, T, d), dtype=torch.float32, device=device),
+        "h_sum": torch.empty((B, H, d, d), dtype=torch.float32, device=device),
+        "z_sum": torch.empty((B, H, d), dtype=torch.float32, device=device),
+        "o": torch.empty((B, H, N, d), dtype=el, device=device),
+        "workspace": torch.empty(max(sz["workspace"], 256), dtype=torch.uint8, device=device),
+    }
+    if params.qk_mode == SLA2_QK_FP8_E4M3:
+        out["q8"] = torch.empty((B, H, T * 64, d), dtype=torch.uint8, device=device)
+        out["k8"] = torch.empty((B, H, T * 64, d), dtype=torch.uint8, device=device)
+        out["q_scale"] = torch.empty((B, H, T), dtype=torch.float32, device=device)
+        out["k_scale"] = torch.empty((B, H, T), dtype=torch.float32, device=device)
+    if with_lse:
+        out["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=device)
+    for name, t in out.items():
+        want = sz[name]
+        have = t.numel() * t.element_size()
+        if name == "workspace":
+            if have < want:
+                raise RuntimeError("workspace too small")
+        elif have != want:
+            raise RuntimeError(f"buffer {name}: {have} bytes allocated, library expects {want}")
+    return out
+
+
+def forward(params: Params, inputs: dict, buffers: Optional[dict] = None, stream=None) -> dict:
+    """Run route -> linear precompute -> fused forward on one stream.
+
+    inputs: device tensors q, k, v [B,H,N,d] (bf16 or fp32), alpha [H,d] fp32,
+    and optionally wq, wk [d,d] fp32.  Returns the buffer dict (o holds the output).
+    """
+    if buffers is None:
+        buffers = allocate(params, inputs["q"].device)
+    t = dict(buffers)
+    for key in ("q", "k", "v", "alpha", "wq", "wk"):
+        t[key] = inputs.get(key)
+    sla2_route(params, t, stream)
+    sla2_linear_precompute(params, t, stream)
+    sla2_attention_fwd(params, t, stream)
+    return buffers

@@ -1,0 +1,234 @@
+// C entry points of libsla2: argument checks, buffer sizes, workspace layout, launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "sla2_internal.hpp"
+
+namespace sla2 {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return SLA2_OK;
+  return fail(SLA2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_params(const sla2_params* p, Geometry* g) {
+  if (p == nullptr) return fail(SLA2_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 1 || p->H < 1 || p->N < 1) return fail(SLA2_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (p->d != 64 && p->d != 128) return fail(SLA2_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", p->d);
+  if (p->block != 64) return fail(SLA2_ERR_INVALID_ARG, "block must be 64 (got %d)", p->block);
+  if (p->dtype != SLA2_F32 && p->dtype != SLA2_BF16) return fail(SLA2_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->qk_mode != SLA2_QK_NATIVE && p->qk_mode != SLA2_QK_FP8_E4M3)
+    return fail(SLA2_ERR_INVALID_ARG, "unknown qk_mode %d", p->qk_mode);
+  if (p->smooth_k != 0 && p->smooth_k != 1) return fail(SLA2_ERR_INVALID_ARG, "smooth_k must be 0 or 1");
+  if (!(p->eps >= 0.f) || p->eps > 1.f) return fail(SLA2_ERR_INVALID_ARG, "eps must be in [0, 1]");
+  const long long T = ((long long)p->N + 63) / 64;
+  if (T > 4096) return fail(SLA2_ERR_UNSUPPORTED, "at most 4096 blocks per sequence (N <= 262144)");
+  if (p->topk < 1 || p->topk > T) return fail(SLA2_ERR_INVALID_ARG, "topk must be in [1, %lld] (got %d)", T, p->topk);
+  if ((long long)p->B * p->H * T > 0x7fffffffLL) return fail(SLA2_ERR_INVALID_ARG, "B*H*T too large");
+  if (p->qk_mode == SLA2_QK_FP8_E4M3 && p->dtype != SLA2_BF16)
+    return fail(SLA2_ERR_UNSUPPORTED, "FP8 Q.K^T needs bf16 inputs");
+  if (p->dtype == SLA2_BF16 && p->d != 128) return fail(SLA2_ERR_UNSUPPORTED, "bf16 kernels need d = 128");
+  g->B = p->B;
+  g->H = p->H;
+  g->N = p->N;
+  g->D = p->d;
+  g->T = (int)T;
+  g->topk = p->topk;
+  g->P = (g->T + kChunk - 1) / kChunk;
+  g->BH = p->B * p->H;
+  g->smooth_k = p->smooth_k != 0;
+  g->fp8 = p->qk_mode == SLA2_QK_FP8_E4M3;
+  g->bf16 = p->dtype == SLA2_BF16;
+  g->eps = p->eps;
+  return SLA2_OK;
+}
+
+}  // namespace
+
+size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
+  const size_t BH = g.BH, T = g.T, D = g.D, P = g.P, P32 = (g.T + 31) / 32;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  Workspace w;
+  w.qsum = (double*)take(BH * T * D * sizeof(double));
+  w.ksum = (double*)take(BH * T * D * sizeof(double));
+  w.mu = (double*)take((BH * P32 * D + BH * D) * sizeof(double));
+  w.qhat = (double*)take(BH * T * D * sizeof(double));
+  w.khatT = (double*)take(BH * D * T * sizeof(double));
+  w.hpart = (float*)take(BH * P * D * D * sizeof(float));
+  w.zpart = (float*)take(BH * P * D * sizeof(float));
+  w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * sizeof(uint16_t) : 0);
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace sla2
+
+using namespace sla2;
+
+namespace {
+
+int fill_sizes(const Geometry& g, sla2_sizes* s) {
+  const size_t BH = g.BH, T = g.T, D = g.D, N = g.N;
+  const size_t es = g.bf16 ? 2 : 4;
+  memset(s, 0, sizeof *s);
+  s->q_pool = BH * T * D * 4;
+  s->k_pool = BH * T * D * 4;
+  s->k_mean = BH * D * 4;
+  s->lut = BH * T * g.topk * 4;
+  s->mask = BH * T * T;
+  if (g.fp8) {
+    s->q8 = BH * T * 64 * D;
+    s->k8 = BH * T * 64 * D;
+    s->q_scale = BH * T * 4;
+    s->k_scale = BH * T * 4;
+  }
+  s->h = BH * T * D * D * es;
+  s->z = BH * T * D * 4;
+  s->h_sum = BH * D * D * 4;
+  s->z_sum = BH * D * 4;
+  s->o = BH * N * D * es;
+  s->lse = BH * N * 4;
+  s->workspace = workspace_layout(g, nullptr, nullptr);
+  return SLA2_OK;
+}
+
+#define REQUIRE(ptr, name) \
+  if ((ptr) == nullptr) return fail(SLA2_ERR_INVALID_ARG, "%s: tensor '%s' is NULL", fn, name)
+
+int prepare(const char* fn, const sla2_params* p, const sla2_tensors* t, Geometry* g, Workspace* ws) {
+  const int st = check_params(p, g);
+  if (st != SLA2_OK) return st;
+  if (t == nullptr) return fail(SLA2_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
+  REQUIRE(t->workspace, "workspace");
+  if (((uintptr_t)t->workspace & 255) != 0) return fail(SLA2_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  workspace_layout(*g, ws, (char*)t->workspace);
+  return SLA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sla2_buffer_sizes(const sla2_params* p, sla2_sizes* out) {
+  Geometry g;
+  const int st = check_params(p, &g);
+  if (st != SLA2_OK) return st;
+  if (out == nullptr) return fail(SLA2_ERR_INVALID_ARG, "sla2_buffer_sizes: out is NULL");
+  return fill_sizes(g, out);
+}
+
+int sla2_route(const sla2_params* p, const sla2_tensors* t, void* stream) {
+  const char* fn = "sla2_route";
+  Geometry g;
+  Workspace ws;
+  int st = prepare(fn, p, t, &g, &ws);
+  if (st != SLA2_OK) return st;
+  REQUIRE(t->q, "q");
+  REQUIRE(t->k, "k");
+  REQUIRE(t->q_pool, "q_pool");
+  REQUIRE(t->k_pool, "k_pool");
+  REQUIRE(t->k_mean, "k_mean");
+  REQUIRE(t->lut, "lut");
+  REQUIRE(t->mask, "mask");
+  if (g.fp8) {
+    REQUIRE(t->q8, "q8");
+    REQUIRE(t->q_scale, "q_scale");
+  }
+  return hip_status(launch_route(g, *t, ws, (hipStream_t)stream), fn);
+}
+
+int sla2_linear_precompute(const sla2_params* p, const sla2_tensors* t, void* stream) {
+  const char* fn = "sla2_linear_precompute";
+  Geometry g;
+  Workspace ws;
+  int st = prepare(fn, p, t, &g, &ws);
+  if (st != SLA2_OK) return st;
+  REQUIRE(t->k, "k");
+  REQUIRE(t->v, "v");
+  REQUIRE(t->k_mean, "k_mean");
+  REQUIRE(t->h, "h");
+  REQUIRE(t->z, "z");
+  REQUIRE(t->h_sum, "h_sum");
+  REQUIRE(t->z_sum, "z_sum");
+  if (g.fp8) {
+    REQUIRE(t->k8, "k8");
+    REQUIRE(t->k_scale, "k_scale");
+  }
+  return hip_status(launch_precompute(g, *t, ws, (hipStream_t)stream), fn);
+}
+
+int sla2_attention_fwd(const sla2_params* p, const sla2_tensors* t, void* stream) {
+  const char* fn = "sla2_attention_fwd";
+  Geometry g;
+  Workspace ws;
+  int st = prepare(fn, p, t, &g, &ws);
+  if (st != SLA2_OK) return st;
+  REQUIRE(t->q, "q");
+  if (!g.bf16 || !g.fp8) REQUIRE(t->k, "k");
+  REQUIRE(t->v, "v");
+  REQUIRE(t->alpha, "alpha");
+  REQUIRE(t->lut, "lut");
+  REQUIRE(t->h, "h");
+  REQUIRE(t->z, "z");
+  REQUIRE(t->h_sum, "h_sum");
+  REQUIRE(t->z_sum, "z_sum");
+  REQUIRE(t->o, "o");
+  REQUIRE(t->k_mean, "k_mean");
+  if (g.fp8) {
+    REQUIRE(t->q8, "q8");
+    REQUIRE(t->k8, "k8");
+    REQUIRE(t->q_scale, "q_scale");
+    REQUIRE(t->k_scale, "k_scale");
+  }
+  return hip_status(launch_fwd(g, *t, ws, (hipStream_t)stream), fn);
+}
+
+int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* dout, void* dq, void* dk,
+                       void* dv, float* dalpha, void* stream) {
+  (void)p; (void)t; (void)dout; (void)dq; (void)dk; (void)dv; (void)dalpha; (void)stream;
+  return fail(SLA2_ERR_UNSUPPORTED, "sla2_attention_bwd: the backward pass is not implemented");
+}
+
+int sla2_selftest_mfma(int which, const void* a, const void* b, float* d, void* stream) {
+  if (which != 0 && which != 1) return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: which must be 0 or 1");
+  if (a == nullptr || b == nullptr || d == nullptr)
+    return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: NULL operand");
+  return hip_status(launch_selftest_mfma(which, a, b, d, (hipStream_t)stream), "sla2_selftest_mfma");
+}
+
+const char* sla2_status_string(int status) {
+  switch (status) {
+    case SLA2_OK: return "ok";
+    case SLA2_ERR_INVALID_ARG: return "invalid argument";
+    case SLA2_ERR_UNSUPPORTED: return "unsupported";
+    case SLA2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sla2_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device helpers shared by the SLA2 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla2 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 64;           // b_q = b_kv (SLA page, section 2 Q2)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kFp8Max = 448.0f;    // largest finite OCP e4m3 magnitude
+
+// E8M0 exponent passed to the scaled fp8 matrix-core instruction for "no extra scaling".
+#ifndef SLA2_FP8_MFMA_SCALE
+#define SLA2_FP8_MFMA_SCALE 0
+#endif
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Round to nearest even into a packed pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Four floats -> four e4m3 codes (round to nearest even) in one dword, byte k = value k.
+// Callers clamp to +-448 first.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__device__ __forceinline__ float clamp_fp8(float y) { return fminf(fmaxf(y, -kFp8Max), kFp8Max); }
+
+// ---------------------------------------------------------------- matrix cores
+// D(16x16) += A(16x32) * B(32x16), bf16 in, fp32 accumulate.  Lane l holds A[l%16][8(l/16)+e]
+// and B[8(l/16)+e][l%16] (e = 0..7); D[4(l/16)+r][l%16] in accumulator r.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// D(16x16) += A(16x128) * B(128x16), e4m3 in (32 bytes per lane), fp32 accumulate; the same
+// lane/row/column mapping as above with 32 k-values per lane.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, SLA2_FP8_MFMA_SCALE, 0,
+                                                          SLA2_FP8_MFMA_SCALE);
+}
+
+// ---------------------------------------------------------------- cross-lane
+// All-reduce over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows4_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// All-reduce within each 16-lane row: rotate by 8 and 4, then swap pairs and neighbours.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
+  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp<0x128>(v);
+  v = v + dpp<0x124>(v);
+  v = v + dpp<0x4E>(v);
+  v = v + dpp<0xB1>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return rows4_max(row16_max(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return rows4_sum(row16_sum(v));
+}
+
+// ---------------------------------------------------------------- launch order
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup id w runs on XCD w % 8).
+// Returns a logical id such that consecutive logical ids run on the same XCD, so that
+// neighbouring query blocks of a head share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int X = 8;
+  const int per = nblocks / X, rem = nblocks % X;
+  const int xcd = bid % X, idx = bid / X;
+  const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return start + idx;
+}
+
+}  // namespace sla2

@@ -1,0 +1,40 @@
+// Host-side launch interface shared by the SLA2 translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sla2.h"
+
+namespace sla2 {
+
+// Key blocks summed into one partial of h_sum / z_sum by the precompute kernels.
+constexpr int kChunk = 8;
+
+struct Geometry {
+  int B, H, N, D, T, topk, P;   // P = ceil(T / kChunk)
+  int BH;
+  bool smooth_k, fp8, bf16;
+  float eps;
+};
+
+// Views into the caller's workspace (layout fixed by workspace_layout()).
+struct Workspace {
+  double* qsum;    // [BH, T, D]  column sums of each Q block (fp64)
+  double* ksum;    // [BH, T, D]  column sums of each K block
+  double* mu;      // [BH, D]     token mean of K (fp64)
+  double* qhat;    // [BH, T, D]  projected pooled Q
+  double* khatT;   // [BH, D, T]  projected pooled K~, transposed
+  float* hpart;    // [BH, P, D, D] chunk partials of h_sum (transposed like h)
+  float* zpart;    // [BH, P, D]
+  uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted
+};
+
+size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);
+
+hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_selftest_mfma(int which, const void* a, const void* b, float* d, hipStream_t s);
+
+}  // namespace sla2

@@ -1,0 +1,196 @@
+"""GPU parity of the HIP path against the CPU oracle, called through the C ABI.
+
+Every case runs route -> linear precompute -> fused forward on seeded inputs
+and compares, element by element, with the fp64 oracle:
+* integer / byte results bit-exact: LUT and mask (outside rows whose k-th and
+  (k+1)-th block scores are within 1e-5), FP8 codes and scales, k_mean;
+* the output within max-abs 2e-2 and mean-rel 1e-2 (bf16 and FP8 paths) or
+  max-abs 1e-4 (fp32 path).
+Tie rows are judged with the oracle re-run on the GPU's LUT.
+"""
+import numpy as np
+import pytest
+
+import sla2_inputs as I
+from tests.gpu_util import (TOL_F32, TOL_LOWP, check_head, compare, oracle_head, run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_linear_attention_pool_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+    yield
+
+
+# ----------------------------------------------------------------------------- matrix cores
+def _bf16_bits(x):
+    return I.bf16_bits(I.round_to_bf16(x.astype(np.float32)))
+
+
+def test_mfma_bf16_operand_layout():
+    import torch
+    from sparse_linear_attention_pool_amd import binding as Bn
+    rng = np.random.default_rng(0)
+    A = I.round_to_bf16(rng.standard_normal((16, 32)).astype(np.float32))
+    Bm = I.round_to_bf16(rng.standard_normal((32, 16)).astype(np.float32))
+    a = np.zeros((64, 8), np.uint16)
+    b = np.zeros((64, 8), np.uint16)
+    for l in range(64):
+        for e in range(8):
+            a[l, e] = I.bf16_bits(A[l % 16, 8 * (l // 16) + e:8 * (l // 16) + e + 1])[0]
+            b[l, e] = I.bf16_bits(Bm[8 * (l // 16) + e, l % 16:l % 16 + 1])[0]
+    da = torch.from_numpy(a.view(np.int16)).cuda()
+    db = torch.from_numpy(b.view(np.int16)).cuda()
+    dd = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    Bn.sla2_selftest_mfma(0, da, db, dd)
+    d = dd.cpu().numpy()
+    ref = A.astype(np.float64) @ Bm.astype(np.float64)
+    got = np.zeros((16, 16))
+    for l in range(64):
+        for r in range(4):
+            got[4 * (l // 16) + r, l % 16] = d[l, r]
+    assert np.max(np.abs(got - ref)) < 1e-4
+
+
+def test_mfma_fp8_operand_layout_and_scale():
+    import torch
+    from oracle import fp8_e4m3 as F8
+    from sparse_linear_attention_pool_amd import binding as Bn
+    rng = np.random.default_rng(1)
+    ca = rng.integers(0, 256, (16, 128)).astype(np.uint8)
+    cb = rng.integers(0, 256, (128, 16)).astype(np.uint8)
+    ca[(ca & 0x7F) == 0x7F] = 0x38   # avoid NaN codes
+    cb[(cb & 0x7F) == 0x7F] = 0x38
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = ca[l % 16, 32 * (l // 16):32 * (l // 16) + 32]
+        b[l] = cb[32 * (l // 16):32 * (l // 16) + 32, l % 16]
+    dd = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    Bn.sla2_selftest_mfma(1, torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), dd)
+    d = dd.cpu().numpy()
+    ref = F8.decode(ca) @ F8.decode(cb)
+    got = np.zeros((16, 16))
+    for l in range(64):
+        for r in range(4):
+            got[4 * (l // 16) + r, l % 16] = d[l, r]
+    # a wrong lane layout pairs unrelated codes and gives O(1) relative errors; the
+    # instruction's own accumulation is measured here at below 2^-12 of sum |a||b|
+    absum = np.abs(F8.decode(ca)) @ np.abs(F8.decode(cb))
+    rel = np.max(np.abs(got - ref) / (absum + 1e-30))
+    say(f"    fp8 mfma: max |err| / sum|a||b| = {rel:.3e}")
+    assert rel <= 2.0 ** -12
+
+
+# ----------------------------------------------------------------------------- whole path
+SMALL = [
+    # (base, overrides)
+    ("C0", dict()),                                          # fp32, d=64, 16x16 blocks, topk 4
+    ("C0", dict(N=1000, seed=10, name="C0 ragged N=1000")),  # partial last block (40 tokens)
+    ("C0", dict(N=50, seed=11, name="C0 single partial block")),
+    ("C0", dict(d=128, N=700, H=3, seed=12, name="fp32 d=128 ragged")),
+    ("C1", dict(grid=(4, 16, 64), seed=21, name="C1-shaped bf16 N=4096")),
+    ("C1", dict(grid=(3, 10, 37), seed=22, name="C1-shaped bf16 ragged N=1110")),
+    ("C2", dict(grid=(4, 16, 64), seed=31, name="C2-shaped fp8 N=4096")),
+    ("C2", dict(grid=(5, 9, 41), H=3, seed=32, name="C2-shaped fp8 ragged N=1845")),
+    ("C2", dict(N=2000, seed=33, name="C2 fp8 unstructured ragged", B=2, H=2)),
+]
+
+
+@pytest.mark.parametrize("base,kw", SMALL, ids=[k.get("name", b) for b, k in SMALL])
+def test_small_workloads_match_oracle(base, kw):
+    w = I.make_workload(base, **kw)
+    inp = I.generate(w)
+    out = run_gpu(w, inp)
+    for b in range(w.B):
+        for h in range(w.H):
+            say(f"  head ({b},{h})")
+            check_head(w, inp, out, b, h)
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16", "fp8"])
+def test_every_block_routed_is_softmax_attention(mode):
+    base = {"f32": "C0", "bf16": "C1", "fp8": "C2"}[mode]
+    w = I.make_workload(base, grid=None, N=900, H=2, seed=40, d=(64 if mode == "f32" else 128),
+                        name=f"all routed {mode}")
+    inp = I.generate(w)
+    inp["alpha"][:] = 1.0
+    T = w.T
+    out = run_gpu(w, inp, topk=T)
+    for h in range(w.H):
+        check_head(w, inp, out, 0, h, topk=T)
+
+
+def test_smoothing_off_and_topk_one():
+    w = I.make_workload("C2", grid=(2, 16, 64), seed=41, name="fp8 smooth_k=0 topk=1")
+    inp = I.generate(w)
+    out = run_gpu(w, inp, topk=1, smooth_k=False)
+    assert not out["k_mean"].any()
+    check_head(w, inp, out, 0, 0, topk=1, smooth_k=False)
+    out = run_gpu(w, inp, topk=1, smooth_k=True)
+    check_head(w, inp, out, 0, 5, topk=1, smooth_k=True)
+
+
+def test_runs_are_deterministic():
+    w = I.make_workload("C2", grid=(4, 16, 64), seed=42, name="determinism")
+    inp = I.generate(w)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for key in ("lut", "mask", "q8", "k8", "o", "h", "h_sum", "lse"):
+        assert np.array_equal(a[key].all(), b[key].all()), key
+
+
+def test_fp8_encoder_on_every_bf16_value():
+    """Every finite bf16 value in [-448, 448] through the Q quantiser with scale exactly 1."""
+    from oracle import fp8_e4m3 as F8
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    per_block = 64 * 128 - 1
+    nblk = -(-len(vals) // per_block)
+    q = np.zeros((nblk, 64 * 128), np.float32)
+    for bi in range(nblk):
+        chunk = vals[bi * per_block:(bi + 1) * per_block]
+        q[bi, 0] = 448.0
+        q[bi, 1:1 + len(chunk)] = chunk
+    N = nblk * 64
+    q = q.reshape(1, 1, N, 128)
+    w = I.make_workload("C2", N=N, H=1, seed=43, name="fp8 encoder sweep", sparse_frac=1.0 / nblk)
+    inp = I.generate(w)
+    inp["q"] = q
+    out = run_gpu(w, inp, topk=1)
+    assert np.all(out["q_scale"].all() == 1.0)
+    want = F8.encode(q.astype(np.float64)).reshape(1, 1, N, 128)
+    got = out["q8"].all()
+    bad = np.nonzero(got != want)
+    assert len(bad[0]) == 0, f"{len(bad[0])} codes differ, e.g. value {q[bad][:5]} gpu {got[bad][:5]} want {want[bad][:5]}"
+
+
+# ----------------------------------------------------------------------------- full sizes
+def _sampled_full(base, heads, blocks_per_head=6):
+    w = I.CONFIGS[base]
+    say(f"[full] generating {w.name}")
+    inp = I.generate(w)
+    out = run_gpu(w, inp, with_lse=True)
+    T = w.T
+    rng = np.random.default_rng(123)
+    for (b, h) in heads:
+        qb = sorted(set([0, T - 1] + rng.integers(0, T, blocks_per_head - 2).tolist()))
+        say(f"  head ({b},{h}) query blocks {qb}")
+        check_head(w, inp, out, b, h, query_blocks=qb, check_stats=(h == heads[0][1]))
+
+
+def test_full_size_c1_sampled():
+    _sampled_full("C1", [(0, 0), (0, 7)])
+
+
+def test_full_size_c2_sampled():
+    _sampled_full("C2", [(0, 0), (0, 5), (0, 11)])
+
+
+def test_full_size_c3_sampled():
+    _sampled_full("C3", [(0, 0), (0, 39)], blocks_per_head=4)

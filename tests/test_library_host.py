@@ -1,0 +1,84 @@
+"""Host-side checks of libsla2.so that need no GPU: symbols, sizes, argument errors."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla2.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla2_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from sparse_linear_attention_pool_amd import binding
+    return binding
+
+
+def test_library_exports_every_declared_function(B):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(B.lib, n), n
+    assert set(B.ENTRY_POINTS) == set(names)
+
+
+def test_buffer_sizes_c2(B):
+    p = B.make_params(1, 12, 32760, 128, 15, "bf16", "fp8")
+    s = B.sla2_buffer_sizes(p)
+    T = 512
+    assert s["lut"] == 12 * T * 15 * 4
+    assert s["mask"] == 12 * T * T
+    assert s["q8"] == 12 * T * 64 * 128 == s["k8"]
+    assert s["h"] == 12 * T * 128 * 128 * 2
+    assert s["o"] == 12 * 32760 * 128 * 2
+    assert s["workspace"] % 256 == 0 and s["workspace"] > 0
+    p32 = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
+    s32 = B.sla2_buffer_sizes(p32)
+    assert s32["q8"] == 0 and s32["h"] == 2 * 16 * 64 * 64 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), -1), (dict(topk=0), -1), (dict(topk=17), -1), (dict(N=0), -1),
+    (dict(block=32), -1), (dict(dtype=7), -1), (dict(qk_mode=5), -1), (dict(smooth_k=2), -1),
+    (dict(eps=-1.0), -1), (dict(dtype=0, qk_mode=1), -2), (dict(d=64, dtype=1, qk_mode=0), -2),
+    (dict(N=64 * 4097, topk=4), -2),
+])
+def test_invalid_params_are_rejected_before_any_launch(B, kw, status):
+    base = dict(B=1, H=2, N=1024, d=64, block=64, topk=4, smooth_k=1, dtype=0, qk_mode=0, eps=1e-5)
+    base.update(kw)
+    p = B.Params(**base)
+    s = B.Sizes()
+    rc = B.lib.sla2_buffer_sizes(ctypes.byref(p), ctypes.byref(s))
+    assert rc == status
+    assert len(B.lib.sla2_last_error()) > 0
+    t = B.Tensors()
+    for fn in (B.lib.sla2_route, B.lib.sla2_linear_precompute, B.lib.sla2_attention_fwd):
+        assert fn(ctypes.byref(p), ctypes.byref(t), None) == status
+
+
+def test_missing_tensors_are_rejected(B):
+    p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
+    t = B.Tensors()
+    assert B.lib.sla2_route(ctypes.byref(p), ctypes.byref(t), None) == B.SLA2_ERR_INVALID_ARG
+    assert b"workspace" in B.lib.sla2_last_error()
+    t.workspace = 256 * 7 + 3          # misaligned pointer, never dereferenced
+    assert B.lib.sla2_route(ctypes.byref(p), ctypes.byref(t), None) == B.SLA2_ERR_INVALID_ARG
+    assert b"aligned" in B.lib.sla2_last_error()
+    t.workspace = 256 * 7
+    assert B.lib.sla2_route(ctypes.byref(p), ctypes.byref(t), None) == B.SLA2_ERR_INVALID_ARG
+    assert b"'q'" in B.lib.sla2_last_error()
+
+
+def test_backward_reports_unsupported(B):
+    p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
+    with pytest.raises(B.SLA2Error) as e:
+        B.sla2_attention_bwd(p, {}, None, None, None, None, None, stream=0)
+    assert e.value.status == B.SLA2_ERR_UNSUPPORTED
+    assert B.lib.sla2_status_string(-2) == b"unsupported"
