@@ -1,0 +1,200 @@
+"""Benchmark of the SLA2 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
+
+One step is the whole forward over one batch whose inputs are already in HBM:
+sla2_route (pooling, FP8 quantisation of Q, projections, Top-k) ->
+sla2_linear_precompute (phi(K~), h_j, z_j, sums, FP8 codes of K~) ->
+sla2_attention_fwd (routed-block attention + linear complement + mix).
+The default workload is the Wan2.1-1.3B-shaped layer at 97% sparsity
+(B=1, H=12, N=32760 on a 21x30x52 latent grid, d=128, 15 of 512 key blocks
+routed per query block, FP8 e4m3 Q.K^T, bf16 P.V, seeded d x d router
+projections), with synthetic seeded inputs.
+
+Prints one JSON line: effective TFLOPS of the step (routed-block FLOPs plus
+linear-branch FLOPs over the step time), the step latency, the dominant
+kernel's roofline figures measured with HIP events on its stream, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import sla2_inputs as I  # noqa: E402
+from sparse_linear_attention_pool_amd import accounting as A  # noqa: E402
+
+METRIC = "attn fwd latency (ms) + effective TFLOPS, N=32760 H=12 d=128, 97% sparse"
+
+# MI355X published peaks (dense)
+PEAK_BF16 = 2500.0     # TFLOP/s
+PEAK_FP8 = 5000.0      # TFLOP/s
+PEAK_HBM = 8000.0      # GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(w: I.Workload):
+    """Algorithmic HBM bytes of each call (what the method must move), per step."""
+    BH, N, d, T = w.B * w.H, w.N, w.d, w.T
+    el = 2 if w.dtype == "bf16" else 4
+    fp8 = w.qk_mode == "fp8"
+    tok = BH * N * d * el
+    route = 2 * tok + (BH * T * 64 * d if fp8 else 0) + 2 * BH * T * d * 4
+    pre = 2 * tok + BH * T * d * d * el + BH * T * d * 4 + (BH * T * 64 * d if fp8 else 0)
+    return {"route": route, "precompute": pre}
+
+
+def cpu_baseline(w: I.Workload, inp: dict, heads: int):
+    """The oracle as it stands, timed on the host on `heads` heads of the workload."""
+    from oracle import sla2_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    lut_flops = 0
+    for h in range(heads):
+        r = O.forward_head(inp["q"][0, h], inp["k"][0, h], inp["v"][0, h], inp["alpha"][h], inp["wq"],
+                           inp["wk"], topk=w.topk, qk_fp8=(w.qk_mode == "fp8"))
+        lut_flops += A.sparse_flops_from_lut(r["lut"][None], w.N, w.d)
+    dt = time.perf_counter() - t0
+    flops = lut_flops + A.linear_flops(1, heads, w.N, w.d)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS (effective)", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{heads} of {w.H} heads of the same workload (batch 0), full sequence, fp64 numpy",
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2", choices=sorted(I.CONFIGS))
+    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path (heads would shard across GPUs with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_linear_attention_pool_amd import binding as Bn
+
+    w = I.CONFIGS[args.config]
+    log(f"[bench] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} T={w.T} topk={w.topk}")
+    inp = I.generate(w)
+    dev = torch.device("cuda:0")
+    el = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d_in = {k: torch.from_numpy(inp[k]).to(el).to(dev) for k in ("q", "k", "v")}
+    d_in["alpha"] = torch.from_numpy(inp["alpha"]).to(dev)
+    d_in["wq"] = None if inp["wq"] is None else torch.from_numpy(inp["wq"]).to(dev)
+    d_in["wk"] = None if inp["wk"] is None else torch.from_numpy(inp["wk"]).to(dev)
+    p = Bn.make_params(w.B, w.H, w.N, w.d, w.topk, w.dtype, w.qk_mode)
+    bufs = Bn.allocate(p, dev)
+    t = dict(bufs)
+    t.update(d_in)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        Bn.sla2_route(p, t, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        Bn.sla2_linear_precompute(p, t, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        Bn.sla2_attention_fwd(p, t, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup {args.warmup} done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    t_route = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_pre = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_fwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms); "
+        f"route {t_route:.4f} precompute {t_pre:.4f} fwd {t_fwd:.4f} ms")
+
+    lut = bufs["lut"].cpu().numpy()
+    f_sparse = A.sparse_flops_from_lut(lut, w.N, w.d)
+    f_lin = A.linear_flops(w.B, w.H, w.N, w.d)
+    f_eff = f_sparse + f_lin
+    tflops = f_eff / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the fused forward.  Its routed-block work is half FP8 (Q.K^T) and half
+    # bf16 (P.V); the peak for that mix is F / (F/2 / P_fp8 + F/2 / P_bf16).
+    fp8 = w.qk_mode == "fp8"
+    peak = (1.0 / (0.5 / PEAK_FP8 + 0.5 / PEAK_BF16)) if fp8 else PEAK_BF16
+    achieved = f_sparse / (t_fwd * 1e-3) / 1e12
+    kb = kernel_bytes(w)
+    passes = {
+        "route_ms": round(float(t_route), 5),
+        "route_GBps": round(kb["route"] / (t_route * 1e-3) / 1e9, 1),
+        "precompute_ms": round(float(t_pre), 5),
+        "precompute_GBps": round(kb["precompute"] / (t_pre * 1e-3) / 1e9, 1),
+        "fwd_ms": round(float(t_fwd), 5),
+        "fwd_routed_TFLOPS": round(achieved, 2),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOPS (effective: routed-block + linear-branch FLOPs per step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 QK^T + bf16" if fp8 else w.dtype,
+        "data": "synthetic (seeded 3D sinusoidal PE + 0.5 N(0,1) for Q,K; N(0,1) V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "block": 64,
+                   "topk": w.topk, "T": w.T, "sparsity": round(1 - w.topk / w.T, 4),
+                   "grid": list(w.grid) if w.grid else None, "seed": w.seed,
+                   "effective_GFLOP": round(f_eff / 1e9, 3), "routed_GFLOP": round(f_sparse / 1e9, 3),
+                   "linear_GFLOP": round(f_lin / 1e9, 3)},
+        "roofline": {"kernel": "fwd_mfma_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None},
+        "passes": passes,
+    }
+    if args.cpu_heads > 0:
+        log(f"[bench] timing the CPU oracle on {args.cpu_heads} heads")
+        out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_heads, w.H))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
