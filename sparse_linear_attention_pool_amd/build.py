@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libsla2.so")
 ARCH = "gfx950"
 
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # packed fp32 VALU forms stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

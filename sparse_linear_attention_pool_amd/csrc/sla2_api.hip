@@ -80,6 +80,8 @@ size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
   w.hpart = (float*)take(BH * P * D * D * sizeof(float));
   w.zpart = (float*)take(BH * P * D * sizeof(float));
   w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * sizeof(uint16_t) : 0);
+  w.phik8 = (uint8_t*)take(g.bf16 ? BH * T * 64 * D : 0);
+  w.phik_scale = (float*)take(g.bf16 ? BH * T * sizeof(float) : 0);
   if (ws) *ws = w;
   return off;
 }
@@ -169,8 +171,10 @@ int sla2_linear_precompute(const sla2_params* p, const sla2_tensors* t, void* st
   REQUIRE(t->k, "k");
   REQUIRE(t->v, "v");
   REQUIRE(t->k_mean, "k_mean");
-  REQUIRE(t->h, "h");
-  REQUIRE(t->z, "z");
+  if (!g.bf16) {          // the fp32 forward reads the per-block statistics
+    REQUIRE(t->h, "h");
+    REQUIRE(t->z, "z");
+  }
   REQUIRE(t->h_sum, "h_sum");
   REQUIRE(t->z_sum, "z_sum");
   if (g.fp8) {
@@ -191,8 +195,10 @@ int sla2_attention_fwd(const sla2_params* p, const sla2_tensors* t, void* stream
   REQUIRE(t->v, "v");
   REQUIRE(t->alpha, "alpha");
   REQUIRE(t->lut, "lut");
-  REQUIRE(t->h, "h");
-  REQUIRE(t->z, "z");
+  if (!g.bf16) {
+    REQUIRE(t->h, "h");
+    REQUIRE(t->z, "z");
+  }
   REQUIRE(t->h_sum, "h_sum");
   REQUIRE(t->z_sum, "z_sum");
   REQUIRE(t->o, "o");

@@ -3,9 +3,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace sla2 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// native 16-byte vector (HIP's uint4 is a struct; copying it goes through memcpy, which keeps
+// register arrays of it in stack memory)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -111,6 +117,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int xcd = bid % X, idx = bid / X;
   const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
   return start + idx;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1, so that array indices
+// inside f are constants from the start (register arrays then never become stack memory).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace sla2

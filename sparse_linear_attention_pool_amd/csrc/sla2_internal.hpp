@@ -28,6 +28,8 @@ struct Workspace {
   float* hpart;    // [BH, P, D, D] chunk partials of h_sum (transposed like h)
   float* zpart;    // [BH, P, D]
   uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted
+  uint8_t* phik8;  // bf16 modes: [BH, T*64, D] e4m3 codes of phi(K~) / phik_scale (pad rows 0)
+  float* phik_scale;  // bf16 modes: [BH, T] max of phi(K~) over the block / 448 (1 if 0)
 };
 
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);

@@ -4,8 +4,9 @@
 //   z_j = sum_t phi(K~_t),
 // plus h_sum = sum_j h_j and z_sum = sum_j z_j (chunk partials, then a fixed-order sum).
 // In FP8 mode the same pass quantises K~ per 64-token block (absmax/448 scale, e4m3 codes).
-// The bf16 pass also writes each block's V transposed, with the key order the fused forward
-// kernel's matrix-core operands use.
+// The bf16 pass also writes, for the fused forward kernel, each block's V transposed (with
+// the key order of its matrix-core operands) and the e4m3 codes of phi(K~) with one
+// max/448 scale per block; h_j and z_j themselves are stored only if asked for.
 //
 // Pages: "SLA: Beyond Sparsity in Diffusion Transformers...", section 2 Q2 step 3 and the
 // section 3 figure (h_j = phi(K_j)^T V_j, z_j = rowsum(phi(K_j)^T), phi = softmax), section 4
@@ -33,7 +34,8 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
     int N, int T, int P, uint8_t* __restrict__ k8, float* __restrict__ k_scale,
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
-    float* __restrict__ zpart, uint16_t* __restrict__ vt) {
+    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8,
+    float* __restrict__ phik_scale) {
   constexpr int D = 128;
   constexpr int SW = 65;  // LDS row stride in 32-bit words
   __shared__ uint32_t phiS[64 * SW];
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
   __shared__ uint32_t vS[64 * SW];
   __shared__ float zred[16 * D];
   __shared__ float wmax[4];
+  __shared__ float pmax[4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -118,6 +121,8 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
+    float phv[4][8];
+    float phmax = 0.f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float mx = kt[p][0];
@@ -138,6 +143,8 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
       for (int e = 0; e < 8; ++e) {
         ph[e] = ex[e] * inv;
         zp[e] += ph[e];
+        phv[p][e] = ph[e];
+        phmax = fmaxf(phmax, ph[e]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -154,14 +161,34 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
+    phmax = wave_max(phmax);
+    if (lane == 0) pmax[w] = phmax;
     __syncthreads();
 
     if (tid < D) {
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s += zred[r * D + tid];
-      z[((size_t)bh * T + j) * D + tid] = s;
+      if (z != nullptr) z[((size_t)bh * T + j) * D + tid] = s;
       zs += s;
+    }
+    // e4m3 codes of phi(K~) for the fused forward kernel: one max/448 scale per block
+    {
+      const float bm = fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]));
+      float sp = __fdiv_rn(bm, kFp8Max);
+      if (sp == 0.f) sp = 1.f;
+      if (tid == 0) phik_scale[(size_t)bh * T + j] = sp;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(phv[p][e], sp));
+        uint2 codes;
+        codes.x = pack_fp8x4(y[0], y[1], y[2], y[3]);
+        codes.y = pack_fp8x4(y[4], y[5], y[6], y[7]);
+        const int row = kBlock * j + r0 + 16 * p;
+        *reinterpret_cast<uint2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
+      }
     }
 
     // h^T tiles on the matrix cores
@@ -202,7 +229,7 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
           acc[mi][ni] = mfma_bf16(A[mi], Bv[ni], acc[mi][ni]);
         }
     }
-    // D[a = 16m + 4g + r][c = 16n + l16] -> h[j][c][a .. a+3]
+    // D[a = 16m + 4g + r][c = 16n + l16] -> h[j][c][a .. a+3] (if stored)
     uint16_t* hj = h + ((size_t)bh * T + j) * D * D;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -210,10 +237,12 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
       for (int ni = 0; ni < 4; ++ni) {
         const int a0 = 16 * (mbase + mi) + 4 * g;
         const int cc = 16 * (nbase + ni) + l16;
-        uint2 st;
-        st.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-        st.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
-        *reinterpret_cast<uint2*>(hj + (size_t)cc * D + a0) = st;
+        if (h != nullptr) {
+          uint2 st;
+          st.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+          st.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+          *reinterpret_cast<uint2*>(hj + (size_t)cc * D + a0) = st;
+        }
         hs[mi][ni] += acc[mi][ni];
       }
 
@@ -348,11 +377,12 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
     if (g.fp8)
       hipLaunchKernelGGL(precompute_bf16_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)t.k,
                          (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale,
-                         (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt);
+                         (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt, ws.phik8, ws.phik_scale);
     else
       hipLaunchKernelGGL(precompute_bf16_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)t.k,
                          (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, (uint8_t*)nullptr,
-                         (float*)nullptr, (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt);
+                         (float*)nullptr, (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt, ws.phik8,
+                         ws.phik_scale);
   } else if (g.D == 128) {
     hipLaunchKernelGGL(precompute_f32_kernel<128>, grid, dim3(256), 0, s, (const float*)t.k,
                        (const float*)t.v, t.k_mean, g.N, g.T, g.P, (float*)t.h, t.z, ws.hpart,
