@@ -106,7 +106,7 @@ def main():
     d_in["wq"] = None if inp["wq"] is None else torch.from_numpy(inp["wq"]).to(dev)
     d_in["wk"] = None if inp["wk"] is None else torch.from_numpy(inp["wk"]).to(dev)
     p = Bn.make_params(w.B, w.H, w.N, w.d, w.topk, w.dtype, w.qk_mode)
-    bufs = Bn.allocate(p, dev)
+    bufs = Bn.allocate(p, dev, per_block_stats=(w.dtype != "bf16"))
     t = dict(bufs)
     t.update(d_in)
     stream = torch.cuda.current_stream(dev)

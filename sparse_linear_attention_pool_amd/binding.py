@@ -151,8 +151,12 @@ def sla2_selftest_mfma(which: int, a, b, d, stream=None) -> None:
 # --------------------------------------------------------------------------------------
 # device buffers (torch allocations sized by sla2_buffer_sizes)
 # --------------------------------------------------------------------------------------
-def allocate(params: Params, device="cuda", with_lse: bool = False) -> dict:
-    """Allocate every output and scratch buffer the three calls need, on `device`."""
+def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_stats: bool = True) -> dict:
+    """Allocate every output and scratch buffer the three calls need, on `device`.
+
+    per_block_stats=False leaves out h and z (bf16 modes only): the forward pass reads
+    only their sums, and the precompute then skips storing them.
+    """
     import torch
     sz = sla2_buffer_sizes(params)
     B, H, N, d = params.B, params.H, params.N, params.d
@@ -164,8 +168,6 @@ def allocate(params: Params, device="cuda", with_lse: bool = False) -> dict:
         "k_mean": torch.empty((B, H, d), dtype=torch.float32, device=device),
         "lut": torch.empty((B, H, T, params.topk), dtype=torch.int32, device=device),
         "mask": torch.empty((B, H, T, T), dtype=torch.uint8, device=device),
-        "h": torch.empty((B, H, T, d, d), dtype=el, device=device),
-        "z": torch.empty((B, H, T, d), dtype=torch.float32, device=device),
         "h_sum": torch.empty((B, H, d, d), dtype=torch.float32, device=device),
         "z_sum": torch.empty((B, H, d), dtype=torch.float32, device=device),
         "o": torch.empty((B, H, N, d), dtype=el, device=device),
@@ -176,6 +178,9 @@ def allocate(params: Params, device="cuda", with_lse: bool = False) -> dict:
         out["k8"] = torch.empty((B, H, T * 64, d), dtype=torch.uint8, device=device)
         out["q_scale"] = torch.empty((B, H, T), dtype=torch.float32, device=device)
         out["k_scale"] = torch.empty((B, H, T), dtype=torch.float32, device=device)
+    if per_block_stats or params.dtype != SLA2_BF16:
+        out["h"] = torch.empty((B, H, T, d, d), dtype=el, device=device)
+        out["z"] = torch.empty((B, H, T, d), dtype=torch.float32, device=device)
     if with_lse:
         out["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=device)
     for name, t in out.items():

@@ -22,15 +22,19 @@ namespace sla2 {
 
 // ---------------------------------------------------------------------------------------
 // bf16, d = 128: one workgroup per (chunk of kChunk key blocks, head), 256 threads.
-// Thread (c = tid % 16, r0 = tid / 16) holds columns 8c..8c+7 of rows r0 + 16p, p = 0..3.
+// Thread (c = tid % 16, r0 = tid / 16) holds columns 8c..8c+7 of rows r0 + 16p, p = 0..3
+// (a 16-lane row of a wave holds one token); the next block's K and V are loaded while the
+// current one is processed.
 // phi and V go to LDS row-major (row stride 65 words, conflict-free 16-bit column gathers);
 // wave w computes the 4 x 4 tiles (a-tiles 4*(w/2).., c-tiles 4*(w%2)..) of
 // D[a][c] = sum_t phi[t][a] V[t][c] with v_mfma_f32_16x16x32_bf16 over 64 tokens.  phi is
 // split into bf16 hi + lo parts (phi - hi rounded again), so the product carries phi to about
 // 2^-16 relative although the matrix cores take bf16; V is bf16 already.
+// The largest phi of a block is max over its rows of 1 / (sum of exp), since the row maximum
+// has exp(0) = 1; it is reduced together with |K~| before the codes are written.
 // ---------------------------------------------------------------------------------------
-template <bool FP8>
-__global__ __launch_bounds__(256) void precompute_bf16_kernel(
+template <bool FP8, bool STORE>
+__global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
     int N, int T, int P, uint8_t* __restrict__ k8, float* __restrict__ k_scale,
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
@@ -42,8 +46,7 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
   __shared__ uint32_t phiLoS[64 * SW];
   __shared__ uint32_t vS[64 * SW];
   __shared__ float zred[16 * D];
-  __shared__ float wmax[4];
-  __shared__ float pmax[4];
+  __shared__ float wred[2][4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -54,10 +57,13 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
 
   float mu[8];
   {
-    const float4 m0 = *reinterpret_cast<const float4*>(k_mean + (size_t)bh * D + 8 * c);
-    const float4 m1 = *reinterpret_cast<const float4*>(k_mean + (size_t)bh * D + 8 * c + 4);
-    mu[0] = m0.x; mu[1] = m0.y; mu[2] = m0.z; mu[3] = m0.w;
-    mu[4] = m1.x; mu[5] = m1.y; mu[6] = m1.z; mu[7] = m1.w;
+    const f32x4 m0 = *reinterpret_cast<const f32x4*>(k_mean + (size_t)bh * D + 8 * c);
+    const f32x4 m1 = *reinterpret_cast<const f32x4*>(k_mean + (size_t)bh * D + 8 * c + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mu[e] = m0[e];
+      mu[4 + e] = m1[e];
+    }
   }
   const int mbase = 4 * (w >> 1), nbase = 4 * (w & 1);
   f32x4 hs[4][4];
@@ -68,151 +74,140 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
   float zs = 0.f;
 
   const int j_lo = chunk * kChunk, j_hi = min(T, j_lo + kChunk);
-  for (int j = j_lo; j < j_hi; ++j) {
-    float kt[4][8];
-    uint4 vraw[4];
-    bool valid[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
+  auto load_kv = [&](int j, u32x4 (&kw)[4], u32x4 (&vw)[4]) {
+    static_for<4>([&](auto p) {
       const int row = kBlock * j + r0 + 16 * p;
-      valid[p] = row < N;
-      uint4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-      if (valid[p]) {
-        const size_t off = ((size_t)bh * N + row) * D + 8 * c;
-        kw = *reinterpret_cast<const uint4*>(k + off);
-        vw = *reinterpret_cast<const uint4*>(v + off);
-      }
-      vraw[p] = vw;
-      const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kt[p][2 * e] = valid[p] ? bf16_lo(ka[e]) - mu[2 * e] : 0.f;
-        kt[p][2 * e + 1] = valid[p] ? bf16_hi(ka[e]) - mu[2 * e + 1] : 0.f;
-      }
-    }
+      const bool ok = row < N;
+      const size_t off = ((size_t)bh * N + (ok ? row : 0)) * D + 8 * c;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(k + off);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(v + off);
+      kw[p] = ok ? a : u32x4{0, 0, 0, 0};
+      vw[p] = ok ? b : u32x4{0, 0, 0, 0};
+    });
+  };
+  u32x4 kw[4], vw[4];
+  load_kv(j_lo, kw, vw);
 
-    if constexpr (FP8) {
-      float amax = 0.f;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(kt[p][e]));
-      amax = wave_max(amax);
-      if (lane == 0) wmax[w] = amax;
-      __syncthreads();
-      const float bm = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-      float s = __fdiv_rn(bm, kFp8Max);
-      if (s == 0.f) s = 1.f;
-      if (tid == 0) k_scale[(size_t)bh * T + j] = s;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(kt[p][e], s));
-        uint2 codes;
-        codes.x = pack_fp8x4(y[0], y[1], y[2], y[3]);
-        codes.y = pack_fp8x4(y[4], y[5], y[6], y[7]);
-        const int row = kBlock * j + r0 + 16 * p;
-        *reinterpret_cast<uint2*>(k8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
-      }
-    }
-
-    // phi over the 128 features of each row (16 lanes of one 16-lane row hold a token)
+  for (int j = j_lo; j < j_hi; ++j) {
+    // ---- phase 1: K~, exp, row sums; V and phi (hi/lo) to LDS; z partials; block maxima
+    float kt[4][8];
+    bool valid[4];
+    float amax = 0.f, pmax = 0.f;
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
-    float phv[4][8];
-    float phmax = 0.f;
+    static_for<4>([&](auto p) {
+      valid[p] = kBlock * j + r0 + 16 * p < N;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+      for (int e = 0; e < 4; ++e) {
+        kt[p][2 * e] = valid[p] ? bf16_lo(kw[p][e]) - mu[2 * e] : 0.f;
+        kt[p][2 * e + 1] = valid[p] ? bf16_hi(kw[p][e]) - mu[2 * e + 1] : 0.f;
+      }
       float mx = kt[p][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, kt[p][e]);
       mx = row16_max(mx);
-      float ex[8], sm = 0.f;
+      float sm = 0.f, ex[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        ex[e] = exp2f((kt[p][e] - mx) * kLog2e);
+        ex[e] = __builtin_amdgcn_exp2f((kt[p][e] - mx) * kLog2e);
         sm += ex[e];
+        amax = fmaxf(amax, fabsf(kt[p][e]));
       }
       sm = row16_sum(sm);
       const float inv = valid[p] ? 1.f / sm : 0.f;
+      pmax = fmaxf(pmax, inv);                 // largest phi of this row
       uint32_t pw[4], pl[4];
-      float ph[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ph[e] = ex[e] * inv;
-        zp[e] += ph[e];
-        phv[p][e] = ph[e];
-        phmax = fmaxf(phmax, ph[e]);
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pw[e] = pack_bf16x2(ph[2 * e], ph[2 * e + 1]);
-        pl[e] = pack_bf16x2(ph[2 * e] - bf16_lo(pw[e]), ph[2 * e + 1] - bf16_hi(pw[e]));
+        const float a0 = ex[2 * e] * inv, a1 = ex[2 * e + 1] * inv;
+        zp[2 * e] += a0;
+        zp[2 * e + 1] += a1;
+        pw[e] = pack_bf16x2(a0, a1);
+        pl[e] = pack_bf16x2(a0 - bf16_lo(pw[e]), a1 - bf16_hi(pw[e]));
       }
       const int r = r0 + 16 * p;
       uint32_t* pd = phiS + r * SW + 4 * c;
-      pd[0] = pw[0]; pd[1] = pw[1]; pd[2] = pw[2]; pd[3] = pw[3];
       uint32_t* pld = phiLoS + r * SW + 4 * c;
-      pld[0] = pl[0]; pld[1] = pl[1]; pld[2] = pl[2]; pld[3] = pl[3];
       uint32_t* vd = vS + r * SW + 4 * c;
-      vd[0] = vraw[p].x; vd[1] = vraw[p].y; vd[2] = vraw[p].z; vd[3] = vraw[p].w;
-    }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pd[e] = pw[e];
+        pld[e] = pl[e];
+        vd[e] = vw[p][e];
+      }
+    });
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
-    phmax = wave_max(phmax);
-    if (lane == 0) pmax[w] = phmax;
+    amax = wave_max(amax);
+    pmax = wave_max(pmax);
+    if (lane == 0) {
+      wred[0][w] = amax;
+      wred[1][w] = pmax;
+    }
+    // next block's K and V stream in while this one finishes
+    if (j + 1 < j_hi) load_kv(j + 1, kw, vw);
     __syncthreads();
 
-    if (tid < D) {
-      float s = 0.f;
+    // ---- phase 2: codes of K~ and phi, z, h tiles, V^T
+    if constexpr (FP8) {
+      const float bm = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+      float s = __fdiv_rn(bm, kFp8Max);
+      if (s == 0.f) s = 1.f;
+      if (tid == 0) k_scale[(size_t)bh * T + j] = s;
+      static_for<4>([&](auto p) {
+        float y[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += zred[r * D + tid];
-      if (z != nullptr) z[((size_t)bh * T + j) * D + tid] = s;
-      zs += s;
+        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(kt[p][e], s));
+        u32x2 codes;
+        codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
+        codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
+        const int row = kBlock * j + r0 + 16 * p;
+        *reinterpret_cast<u32x2*>(k8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
+      });
     }
-    // e4m3 codes of phi(K~) for the fused forward kernel: one max/448 scale per block
     {
-      const float bm = fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]));
+      const float bm = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
       float sp = __fdiv_rn(bm, kFp8Max);
       if (sp == 0.f) sp = 1.f;
       if (tid == 0) phik_scale[(size_t)bh * T + j] = sp;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      // phi from its bf16 hi + lo parts in LDS (within 2^-16 of the fp32 value)
+      static_for<4>([&](auto p) {
+        const int r = r0 + 16 * p;
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(phv[p][e], sp));
-        uint2 codes;
-        codes.x = pack_fp8x4(y[0], y[1], y[2], y[3]);
-        codes.y = pack_fp8x4(y[4], y[5], y[6], y[7]);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t hw = phiS[r * SW + 4 * c + e], lw = phiLoS[r * SW + 4 * c + e];
+          y[2 * e] = clamp_fp8(__fdiv_rn(bf16_lo(hw) + bf16_lo(lw), sp));
+          y[2 * e + 1] = clamp_fp8(__fdiv_rn(bf16_hi(hw) + bf16_hi(lw), sp));
+        }
+        u32x2 codes;
+        codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
+        codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
         const int row = kBlock * j + r0 + 16 * p;
-        *reinterpret_cast<uint2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
-      }
+        *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
+      });
+    }
+    if (tid < D) {
+      float sz = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sz += zred[r * D + tid];
+      if constexpr (STORE) z[((size_t)bh * T + j) * D + tid] = sz;
+      zs += sz;
     }
 
-    // h^T tiles on the matrix cores
+    // h^T tiles on the matrix cores: D[a][c] = sum_t phi[t][a] V[t][c]
     f32x4 acc[4][4];
+    if constexpr (STORE) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int t0 = 32 * ks + 8 * g;
-      bf16x8 A[4], Alo[4], Bv[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int a = 16 * (mbase + mi) + l16;
-        uint16_t e16[8], l16v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          e16[e] = phi16[(t0 + e) * 2 * SW + a];
-          l16v[e] = philo16[(t0 + e) * 2 * SW + a];
-        }
-        A[mi] = __builtin_bit_cast(bf16x8, e16);
-        Alo[mi] = __builtin_bit_cast(bf16x8, l16v);
-      }
+      bf16x8 Bv[4];
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         const int cc = 16 * (nbase + ni) + l16;
@@ -222,35 +217,45 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
         Bv[ni] = __builtin_bit_cast(bf16x8, e16);
       }
 #pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int a = 16 * (mbase + mi) + l16;
+        uint16_t e16[8], l16v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          e16[e] = phi16[(t0 + e) * 2 * SW + a];
+          l16v[e] = philo16[(t0 + e) * 2 * SW + a];
+        }
+        const bf16x8 Ah = __builtin_bit_cast(bf16x8, e16), Al = __builtin_bit_cast(bf16x8, l16v);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          f32x4& dst = STORE ? acc[mi][ni] : hs[mi][ni];
+          dst = mfma_bf16(Al, Bv[ni], dst);
+          dst = mfma_bf16(Ah, Bv[ni], dst);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (STORE) {
+      // D[a = 16m + 4g + r][c = 16n + l16] -> h[j][c][a .. a+3]
+      uint16_t* hj = h + ((size_t)bh * T + j) * D * D;
+#pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          acc[mi][ni] = mfma_bf16(Alo[mi], Bv[ni], acc[mi][ni]);
-          acc[mi][ni] = mfma_bf16(A[mi], Bv[ni], acc[mi][ni]);
+          const int a0 = 16 * (mbase + mi) + 4 * g;
+          const int cc = 16 * (nbase + ni) + l16;
+          u32x2 st;
+          st[0] = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+          st[1] = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+          *reinterpret_cast<u32x2*>(hj + (size_t)cc * D + a0) = st;
+          hs[mi][ni] += acc[mi][ni];
         }
     }
-    // D[a = 16m + 4g + r][c = 16n + l16] -> h[j][c][a .. a+3] (if stored)
-    uint16_t* hj = h + ((size_t)bh * T + j) * D * D;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int a0 = 16 * (mbase + mi) + 4 * g;
-        const int cc = 16 * (nbase + ni) + l16;
-        if (h != nullptr) {
-          uint2 st;
-          st.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-          st.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
-          *reinterpret_cast<uint2*>(hj + (size_t)cc * D + a0) = st;
-        }
-        hs[mi][ni] += acc[mi][ni];
-      }
 
     // V of this block, transposed: vt[j][c][32s + 8gg + e] = V[key][c] with
     // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4)
     uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+    static_for<4>([&](auto pp) {
       const int qd = tid + 256 * pp;
       const int cc = qd >> 3, s = (qd >> 2) & 1, gg = qd & 3;
       uint16_t e16[8];
@@ -259,9 +264,8 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
         const int key = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
         e16[e] = v16[key * 2 * SW + cc];
       }
-      *reinterpret_cast<uint4*>(vtj + (size_t)cc * kBlock + 32 * s + 8 * gg) =
-          __builtin_bit_cast(uint4, e16);
-    }
+      *reinterpret_cast<u32x4*>(vtj + (size_t)cc * kBlock + 32 * s + 8 * gg) = __builtin_bit_cast(u32x4, e16);
+    });
     __syncthreads();
   }
 
@@ -272,8 +276,7 @@ __global__ __launch_bounds__(256) void precompute_bf16_kernel(
     for (int ni = 0; ni < 4; ++ni) {
       const int a0 = 16 * (mbase + mi) + 4 * g;
       const int cc = 16 * (nbase + ni) + l16;
-      *reinterpret_cast<float4*>(hp + (size_t)cc * D + a0) =
-          make_float4(hs[mi][ni][0], hs[mi][ni][1], hs[mi][ni][2], hs[mi][ni][3]);
+      *reinterpret_cast<f32x4*>(hp + (size_t)cc * D + a0) = hs[mi][ni];
     }
   if (tid < D) zpart[((size_t)bh * P + chunk) * D + tid] = zs;
 }
@@ -351,38 +354,58 @@ __global__ __launch_bounds__(256) void precompute_f32_kernel(
   if (tid < D) zpart[((size_t)bh * P + chunk) * D + tid] = zs;
 }
 
-// h_sum / z_sum: sum of the chunk partials in chunk order.
+// h_sum / z_sum: sum of the chunk partials.  A workgroup owns 64 consecutive entries (16
+// quads) of one head; thread (quad q, part u) adds the partials p = u, u + 16, ... of its quad
+// with 16-byte loads, then the 16 parts are combined in fixed order.
 __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restrict__ hpart,
                                                           const float* __restrict__ zpart, int P, int D,
                                                           float* __restrict__ h_sum,
                                                           float* __restrict__ z_sum) {
-  const int bh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  __shared__ f32x4 red[16][16];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int q = tid & 15, u = tid >> 4;
   const int DD = D * D;
-  if (e < DD) {
-    float s = 0.f;
-    for (int p = 0; p < P; ++p) s += hpart[((size_t)bh * P + p) * DD + e];
-    h_sum[(size_t)bh * DD + e] = s;
+  const int e0 = blockIdx.x * 64 + 4 * q;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (e0 < DD) {
+#pragma unroll 8
+    for (int p = u; p < P; p += 16) acc += *reinterpret_cast<const f32x4*>(hpart + ((size_t)bh * P + p) * DD + e0);
   }
-  if (blockIdx.x == 0 && threadIdx.x < D) {
-    float s = 0.f;
-    for (int p = 0; p < P; ++p) s += zpart[((size_t)bh * P + p) * D + threadIdx.x];
-    z_sum[(size_t)bh * D + threadIdx.x] = s;
+  red[u][q] = acc;
+  __syncthreads();
+  if (u == 0 && e0 < DD) {
+    f32x4 sm = red[0][q];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) sm += red[k][q];
+    *reinterpret_cast<f32x4*>(h_sum + (size_t)bh * DD + e0) = sm;
   }
+  if (blockIdx.x == 0 && tid < D) {
+    float sz = 0.f;
+    for (int p = 0; p < P; ++p) sz += zpart[((size_t)bh * P + p) * D + tid];
+    z_sum[(size_t)bh * D + tid] = sz;
+  }
+}
+
+template <bool FP8, bool STORE>
+static void launch_precompute_bf16(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+  hipLaunchKernelGGL((precompute_bf16_kernel<FP8, STORE>), dim3(g.P, g.BH), dim3(256), 0, s, (const uint16_t*)t.k,
+                     (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale, (uint16_t*)t.h, t.z, ws.hpart,
+                     ws.zpart, ws.vt, ws.phik8, ws.phik_scale);
 }
 
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws,
                              hipStream_t s) {
   dim3 grid(g.P, g.BH);
   if (g.bf16) {
-    if (g.fp8)
-      hipLaunchKernelGGL(precompute_bf16_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)t.k,
-                         (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale,
-                         (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt, ws.phik8, ws.phik_scale);
-    else
-      hipLaunchKernelGGL(precompute_bf16_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)t.k,
-                         (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, (uint8_t*)nullptr,
-                         (float*)nullptr, (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt, ws.phik8,
-                         ws.phik_scale);
+    // h_j and z_j are stored only when both buffers are given
+    const bool store = t.h != nullptr && t.z != nullptr;
+    if (g.fp8) {
+      if (store) launch_precompute_bf16<true, true>(g, t, ws, s);
+      else launch_precompute_bf16<true, false>(g, t, ws, s);
+    } else {
+      if (store) launch_precompute_bf16<false, true>(g, t, ws, s);
+      else launch_precompute_bf16<false, false>(g, t, ws, s);
+    }
   } else if (g.D == 128) {
     hipLaunchKernelGGL(precompute_f32_kernel<128>, grid, dim3(256), 0, s, (const float*)t.k,
                        (const float*)t.v, t.k_mean, g.N, g.T, g.P, (float*)t.h, t.z, ws.hpart,
@@ -392,7 +415,7 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
                        (const float*)t.v, t.k_mean, g.N, g.T, g.P, (float*)t.h, t.z, ws.hpart,
                        ws.zpart);
   }
-  hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 255) / 256, g.BH), dim3(256), 0, s,
+  hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 63) / 64, g.BH), dim3(256), 0, s,
                      ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum);
   return hipGetLastError();
 }

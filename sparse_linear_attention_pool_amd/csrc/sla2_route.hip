@@ -129,41 +129,43 @@ __global__ __launch_bounds__(D) void kpart_kernel(const double* __restrict__ ksu
   const int P32 = (T + 31) / 32;
   double s = 0.0;
   const int lo = 32 * p, hi = min(T, lo + 32);
+#pragma unroll 32
   for (int i = lo; i < hi; ++i) s += ksum[((size_t)bh * T + i) * D + c];
   kpart[((size_t)bh * P32 + p) * D + c] = s;
 }
 
 // ---------------------------------------------------------------------------------------
-// Project: one workgroup per (16 blocks, head); threads [0, D) handle Q, [D, 2D) handle K.
+// Project: one workgroup per (16 blocks, head, Q or K), 256 threads.
 // mu = (sum of all K) / N; q_bar = block mean of Q; k_bar = block mean of K - mu;
-// q_hat = q_bar W_q, k_hat = k_bar W_k in fp64 (W NULL = identity).
+// q_hat = q_bar W_q, k_hat = k_bar W_k in fp64 (W NULL = identity).  Thread (rg, cg) computes
+// rows 2rg, 2rg+1 and output columns 4cg..4cg+3 (D = 128) or 2cg..2cg+1 (D = 64).
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(2 * D) void project_kernel(
+__global__ __launch_bounds__(256) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum, const double* __restrict__ kpart,
     int N, int T, int smooth_k, const float* __restrict__ wq, const float* __restrict__ wk,
     float* __restrict__ q_pool, float* __restrict__ k_pool, float* __restrict__ k_mean,
     double* __restrict__ mu_out, double* __restrict__ qhat, double* __restrict__ khatT) {
   constexpr int R = 16;
+  constexpr int CPT = D / 32;                 // output columns per thread
   __shared__ double mu_s[D];
-  __shared__ double rows[2][R][D];
-  const int bh = blockIdx.y, i0 = blockIdx.x * R;
-  const int which = threadIdx.x / D, c = threadIdx.x % D;
+  __shared__ __attribute__((aligned(16))) double rows[D][R];   // [a][r]: a row pair is 16 bytes
+  const int bh = blockIdx.y, i0 = blockIdx.x * R, which = blockIdx.z, tid = threadIdx.x;
   const int P32 = (T + 31) / 32;
 
-  if (which == 0) {
-    double s = 0.0;
-    for (int p = 0; p < P32; ++p) s += kpart[((size_t)bh * P32 + p) * D + c];
-    const double m = smooth_k ? s / (double)N : 0.0;
-    mu_s[c] = m;
+  if (which == 1 && tid < D) {
+    double sm = 0.0;
+    for (int p = 0; p < P32; ++p) sm += kpart[((size_t)bh * P32 + p) * D + tid];
+    const double m = smooth_k ? sm / (double)N : 0.0;
+    mu_s[tid] = m;
     if (blockIdx.x == 0) {
-      k_mean[(size_t)bh * D + c] = (float)m;
-      mu_out[(size_t)bh * D + c] = m;
+      k_mean[(size_t)bh * D + tid] = (float)m;
+      mu_out[(size_t)bh * D + tid] = m;
     }
   }
   __syncthreads();
-  for (int r = 0; r < R; ++r) {
-    const int i = i0 + r;
+  for (int x = tid; x < R * D; x += 256) {
+    const int r = x / D, c = x % D, i = i0 + r;
     double v = 0.0;
     if (i < T) {
       const int n = min(kBlock, N - kBlock * i);
@@ -176,32 +178,53 @@ __global__ __launch_bounds__(2 * D) void project_kernel(
         k_pool[idx] = (float)v;
       }
     }
-    rows[which][r][c] = v;
+    rows[c][r] = v;
   }
   __syncthreads();
 
-  double acc[R];
+  const int rg = tid >> 5, cg = tid & 31;
+  const int r0 = 2 * rg, c0 = CPT * cg;
+  double acc[2][CPT];
   const float* W = which ? wk : wq;
   if (W != nullptr) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    for (int a = 0; a < D; ++a) {
-      const double w = (double)W[a * D + c];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = fma(rows[which][r][a], w, acc[r]);
+      for (int x = 0; x < CPT; ++x) acc[u][x] = 0.0;
+#pragma unroll 8
+    for (int a = 0; a < D; ++a) {
+      const double2 rv = *reinterpret_cast<const double2*>(&rows[a][r0]);
+      float wv[CPT];
+      if constexpr (CPT == 4) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(W + a * D + c0);
+        wv[0] = w4[0]; wv[1] = w4[1]; wv[2] = w4[2]; wv[3] = w4[3];
+      } else {
+#pragma unroll
+        for (int x = 0; x < CPT; ++x) wv[x] = W[a * D + c0 + x];
+      }
+#pragma unroll
+      for (int x = 0; x < CPT; ++x) {
+        acc[0][x] = fma(rv.x, (double)wv[x], acc[0][x]);
+        acc[1][x] = fma(rv.y, (double)wv[x], acc[1][x]);
+      }
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = rows[which][r][c];
+    for (int x = 0; x < CPT; ++x) {
+      acc[0][x] = rows[c0 + x][r0];
+      acc[1][x] = rows[c0 + x][r0 + 1];
+    }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = i0 + r;
-    if (i < T) {
+  for (int u = 0; u < 2; ++u) {
+    const int i = i0 + r0 + u;
+    if (i >= T) continue;
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) {
       if (which == 0)
-        qhat[((size_t)bh * T + i) * D + c] = acc[r];
+        qhat[((size_t)bh * T + i) * D + c0 + x] = acc[u][x];
       else
-        khatT[((size_t)bh * D + c) * T + i] = acc[r];
+        khatT[((size_t)bh * D + c0 + x) * T + i] = acc[u][x];
     }
   }
 }
@@ -215,7 +238,7 @@ __global__ __launch_bounds__(2 * D) void project_kernel(
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxSlots = 64;   // T <= 64 * 64 = 4096
 
-template <int R>
+template <int R, int MAXS>
 __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qhat,
                                                    const double* __restrict__ khatT, int T, int D,
                                                    int topk, double inv_sqrt_d,
@@ -236,6 +259,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qh
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0;
     const double* kc = khatT + (size_t)bh * D * T + j;
+#pragma unroll 8
     for (int c = 0; c < D; ++c) {
       const double kv = kc[(size_t)c * T];
 #pragma unroll
@@ -251,9 +275,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qh
   for (int r = w; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= T) break;
-    double v[kMaxSlots];
+    double v[MAXS];
 #pragma unroll
-    for (int s = 0; s < kMaxSlots; ++s) {
+    for (int s = 0; s < MAXS; ++s) {
       const int j = 64 * s + lane;
       v[s] = (s < S && j < T) ? sc[r * T + j] : -INFINITY;
     }
@@ -262,7 +286,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qh
       double bv = -INFINITY;
       int bj = 0x7fffffff;
 #pragma unroll
-      for (int s = 0; s < kMaxSlots; ++s) {
+      for (int s = 0; s < MAXS; ++s) {
         if (s < S) {
           const int j = 64 * s + lane;
           if (!((sel >> s) & 1ull) && j < T && (v[s] > bv || bj == 0x7fffffff)) {
@@ -296,12 +320,31 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qh
   }
 }
 
+constexpr size_t kTopkLdsMax = 160 * 1024;
+
+template <int R, int MAXS>
+static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+  const size_t lds = (size_t)R * (g.D + g.T) * sizeof(double);
+  static bool attr_set = false;   // the kernel may use up to 160 KB of dynamic LDS
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)kTopkLdsMax);
+    attr_set = true;
+  }
+  dim3 grid((g.T + R - 1) / R, g.BH);
+  hipLaunchKernelGGL((topk_kernel<R, MAXS>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.D, g.topk,
+                     1.0 / sqrt((double)g.D), t.lut, t.mask);
+}
+
+// candidate slots per lane: the smallest power of two >= ceil(T / 64)
 template <int R>
 static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
-  const size_t lds = (size_t)R * (g.D + g.T) * sizeof(double);
-  dim3 grid((g.T + R - 1) / R, g.BH);
-  hipLaunchKernelGGL(topk_kernel<R>, grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.D, g.topk,
-                     1.0 / sqrt((double)g.D), t.lut, t.mask);
+  const int S = (g.T + 63) / 64;
+  if (S <= 4) launch_topk_s<R, 4>(g, t, ws, s);
+  else if (S <= 8) launch_topk_s<R, 8>(g, t, ws, s);
+  else if (S <= 16) launch_topk_s<R, 16>(g, t, ws, s);
+  else if (S <= 32) launch_topk_s<R, 32>(g, t, ws, s);
+  else launch_topk_s<R, 64>(g, t, ws, s);
 }
 
 template <typename Tin, int D>
@@ -321,7 +364,7 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
   // ws.mu first holds the 32-block partials; the projection kernel reads them and writes
   // the final mean into the tail of the same region.
   double* mu_final = ws.mu + (size_t)g.BH * P32 * D;
-  hipLaunchKernelGGL(project_kernel<D>, dim3((g.T + 15) / 16, g.BH), dim3(2 * D), 0, s, ws.qsum,
+  hipLaunchKernelGGL(project_kernel<D>, dim3((g.T + 15) / 16, g.BH, 2), dim3(256), 0, s, ws.qsum,
                      ws.ksum, ws.mu, g.N, g.T, (int)g.smooth_k, t.wq, t.wk, t.q_pool, t.k_pool,
                      t.k_mean, mu_final, ws.qhat, ws.khatT);
 }
@@ -334,9 +377,9 @@ hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspac
     if (g.D == 128) launch_route_typed<float, 128>(g, t, ws, s);
     else launch_route_typed<float, 64>(g, t, ws, s);
   }
-  // rows per workgroup: the largest power of two <= 16 whose scores fit in 64 KB of LDS
+  // rows per workgroup: the largest power of two <= 16 whose scores fit in the LDS budget
   int R = 16;
-  while (R > 1 && (size_t)R * (g.D + g.T) * sizeof(double) > 65536) R >>= 1;
+  while (R > 1 && (size_t)R * (g.D + g.T) * sizeof(double) > kTopkLdsMax) R >>= 1;
   switch (R) {
     case 16: launch_topk<16>(g, t, ws, s); break;
     case 8: launch_topk<8>(g, t, ws, s); break;
