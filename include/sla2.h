@@ -142,10 +142,11 @@ int sla2_attention_bwd(const sla2_params *p, const sla2_tensors *t, const void *
  * so a test can pin the operand lane layouts the kernels assume.
  *   which = 0: v_mfma_f32_16x16x32_bf16, a/b = 64 lanes x 8 bf16 (16 bytes per lane)
  *   which = 1: v_mfma_f32_16x16x128_f8f6f4 with e4m3 operands, 64 lanes x 32 bytes
- * a, b: device arrays of the lane-major operand registers; d: device float[64*4], lane-major
- * accumulator registers of the result (C = 0).  Returns SLA2_ERR_INVALID_ARG for other
- * values of `which`. */
-int sla2_selftest_mfma(int which, const void *a, const void *b, float *d, void *stream);
+ *   which = 2: v_mfma_f64_16x16x4_f64, a/b = 64 lanes x 1 double
+ * a, b: device arrays of the lane-major operand registers; d: device array of the lane-major
+ * accumulator registers of the result (C = 0): float[64*4] for which = 0 and 1,
+ * double[64*4] for which = 2.  Returns SLA2_ERR_INVALID_ARG for other values of `which`. */
+int sla2_selftest_mfma(int which, const void *a, const void *b, void *d, void *stream);
 
 const char *sla2_status_string(int status);
 const char *sla2_last_error(void);   /* message of the last failed call on this thread */

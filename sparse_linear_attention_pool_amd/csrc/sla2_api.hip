@@ -218,8 +218,8 @@ int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* 
   return fail(SLA2_ERR_UNSUPPORTED, "sla2_attention_bwd: the backward pass is not implemented");
 }
 
-int sla2_selftest_mfma(int which, const void* a, const void* b, float* d, void* stream) {
-  if (which != 0 && which != 1) return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: which must be 0 or 1");
+int sla2_selftest_mfma(int which, const void* a, const void* b, void* d, void* stream) {
+  if (which < 0 || which > 2) return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: which must be 0, 1 or 2");
   if (a == nullptr || b == nullptr || d == nullptr)
     return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: NULL operand");
   return hip_status(launch_selftest_mfma(which, a, b, d, (hipStream_t)stream), "sla2_selftest_mfma");

@@ -15,6 +15,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 64;           // b_q = b_kv (SLA page, section 2 Q2)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -63,6 +64,12 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, SLA2_FP8_MFMA_SCALE, 0,
                                                           SLA2_FP8_MFMA_SCALE);
+}
+
+// D(16x16) += A(16x4) * B(4x16), fp64.  Lane l holds A[l%16][l/16] and B[l/16][l%16];
+// D[4r+l/16][l%16] in accumulator r (rows interleaved, unlike the fp32-output forms above).
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- cross-lane

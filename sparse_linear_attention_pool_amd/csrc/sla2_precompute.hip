@@ -354,35 +354,42 @@ __global__ __launch_bounds__(256) void precompute_f32_kernel(
   if (tid < D) zpart[((size_t)bh * P + chunk) * D + tid] = zs;
 }
 
-// h_sum / z_sum: sum of the chunk partials.  A workgroup owns 64 consecutive entries (16
-// quads) of one head; thread (quad q, part u) adds the partials p = u, u + 16, ... of its quad
-// with 16-byte loads, then the 16 parts are combined in fixed order.
+// h_sum / z_sum: sum of the chunk partials.  A workgroup owns 256 consecutive entries (64
+// quads) of one head; thread (quad q, part u) adds the partials p = u, u + 4, ... of its quad
+// with 16-byte loads, then the 4 parts are combined in fixed order.
 __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restrict__ hpart,
                                                           const float* __restrict__ zpart, int P, int D,
                                                           float* __restrict__ h_sum,
                                                           float* __restrict__ z_sum) {
-  __shared__ f32x4 red[16][16];
+  __shared__ f32x4 red[4][64];
   const int bh = blockIdx.y, tid = threadIdx.x;
-  const int q = tid & 15, u = tid >> 4;
+  const int q = tid & 63, u = tid >> 6;
   const int DD = D * D;
-  const int e0 = blockIdx.x * 64 + 4 * q;
+  const int e0 = blockIdx.x * 256 + 4 * q;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (e0 < DD) {
-#pragma unroll 8
-    for (int p = u; p < P; p += 16) acc += *reinterpret_cast<const f32x4*>(hpart + ((size_t)bh * P + p) * DD + e0);
+#pragma unroll 16
+    for (int p = u; p < P; p += 4) acc += *reinterpret_cast<const f32x4*>(hpart + ((size_t)bh * P + p) * DD + e0);
   }
   red[u][q] = acc;
   __syncthreads();
   if (u == 0 && e0 < DD) {
-    f32x4 sm = red[0][q];
-#pragma unroll
-    for (int k = 1; k < 16; ++k) sm += red[k][q];
+    const f32x4 sm = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
     *reinterpret_cast<f32x4*>(h_sum + (size_t)bh * DD + e0) = sm;
   }
-  if (blockIdx.x == 0 && tid < D) {
+  if (blockIdx.x == 0) {
+    // z_sum: thread (c, part v) adds partials p = v, v + 256/D, ...; parts combined in order
+    __shared__ float zred[256];
+    const int parts = 256 / D, c = tid % D, v = tid / D;
     float sz = 0.f;
-    for (int p = 0; p < P; ++p) sz += zpart[((size_t)bh * P + p) * D + tid];
-    z_sum[(size_t)bh * D + tid] = sz;
+#pragma unroll 8
+    for (int p = v; p < P; p += parts) sz += zpart[((size_t)bh * P + p) * D + c];
+    zred[tid] = sz;
+    __syncthreads();
+    if (v == 0) {
+      for (int k = 1; k < parts; ++k) sz += zred[k * D + c];
+      z_sum[(size_t)bh * D + c] = sz;
+    }
   }
 }
 
@@ -415,7 +422,7 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
                        (const float*)t.v, t.k_mean, g.N, g.T, g.P, (float*)t.h, t.z, ws.hpart,
                        ws.zpart);
   }
-  hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 63) / 64, g.BH), dim3(256), 0, s,
+  hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 255) / 256, g.BH), dim3(256), 0, s,
                      ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum);
   return hipGetLastError();
 }

@@ -137,19 +137,23 @@ __global__ __launch_bounds__(D) void kpart_kernel(const double* __restrict__ ksu
 // ---------------------------------------------------------------------------------------
 // Project: one workgroup per (16 blocks, head, Q or K), 256 threads.
 // mu = (sum of all K) / N; q_bar = block mean of Q; k_bar = block mean of K - mu;
-// q_hat = q_bar W_q, k_hat = k_bar W_k in fp64 (W NULL = identity).  Thread (rg, cg) computes
-// rows 2rg, 2rg+1 and output columns 4cg..4cg+3 (D = 128) or 2cg..2cg+1 (D = 64).
+// q_hat = q_bar W_q, k_hat = k_bar W_k in fp64 (W NULL = identity) on the fp64 matrix cores.
+// Wave w computes the 16 x 16 output tiles of columns 16 ct .. 16 ct + 15, ct = w, w + 4, ...
+// For K the transposed tile k_hat^T = W_k^T k_bar^T is formed (the same two operands in
+// swapped roles), so both outputs are stored in 128-byte rows.
 // ---------------------------------------------------------------------------------------
+constexpr int kProjRows = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum, const double* __restrict__ kpart,
     int N, int T, int smooth_k, const float* __restrict__ wq, const float* __restrict__ wk,
     float* __restrict__ q_pool, float* __restrict__ k_pool, float* __restrict__ k_mean,
     double* __restrict__ mu_out, double* __restrict__ qhat, double* __restrict__ khatT) {
-  constexpr int R = 16;
-  constexpr int CPT = D / 32;                 // output columns per thread
+  constexpr int R = kProjRows;
+  constexpr int KS = D / 4;   // matrix-core steps over the input channel
   __shared__ double mu_s[D];
-  __shared__ __attribute__((aligned(16))) double rows[D][R];   // [a][r]: a row pair is 16 bytes
+  __shared__ double rows[R][D + 1];
   const int bh = blockIdx.y, i0 = blockIdx.x * R, which = blockIdx.z, tid = threadIdx.x;
   const int P32 = (T + 31) / 32;
 
@@ -178,173 +182,253 @@ __global__ __launch_bounds__(256) void project_kernel(
         k_pool[idx] = (float)v;
       }
     }
-    rows[c][r] = v;
+    rows[r][c] = v;
   }
   __syncthreads();
 
-  const int rg = tid >> 5, cg = tid & 31;
-  const int r0 = 2 * rg, c0 = CPT * cg;
-  double acc[2][CPT];
   const float* W = which ? wk : wq;
-  if (W != nullptr) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) acc[u][x] = 0.0;
-#pragma unroll 8
-    for (int a = 0; a < D; ++a) {
-      const double2 rv = *reinterpret_cast<const double2*>(&rows[a][r0]);
-      float wv[CPT];
-      if constexpr (CPT == 4) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(W + a * D + c0);
-        wv[0] = w4[0]; wv[1] = w4[1]; wv[2] = w4[2]; wv[3] = w4[3];
+  const int w = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+  if (W == nullptr) {
+    for (int x = tid; x < R * D; x += 256) {
+      if (which == 0) {
+        const int r = x / D, c = x % D;
+        if (i0 + r < T) qhat[((size_t)bh * T + i0 + r) * D + c] = rows[r][c];
       } else {
-#pragma unroll
-        for (int x = 0; x < CPT; ++x) wv[x] = W[a * D + c0 + x];
-      }
-#pragma unroll
-      for (int x = 0; x < CPT; ++x) {
-        acc[0][x] = fma(rv.x, (double)wv[x], acc[0][x]);
-        acc[1][x] = fma(rv.y, (double)wv[x], acc[1][x]);
+        const int c = x / R, r = x % R;
+        if (i0 + r < T) khatT[((size_t)bh * D + c) * T + i0 + r] = rows[r][c];
       }
     }
-  } else {
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      acc[0][x] = rows[c0 + x][r0];
-      acc[1][x] = rows[c0 + x][r0 + 1];
-    }
+    return;
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = i0 + r0 + u;
-    if (i >= T) continue;
-#pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      if (which == 0)
-        qhat[((size_t)bh * T + i) * D + c0 + x] = acc[u][x];
-      else
-        khatT[((size_t)bh * D + c0 + x) * T + i] = acc[u][x];
+  double xa[KS];   // pooled row li, input channels 4s + lk
+  static_for<KS>([&](auto s) { xa[s] = rows[li][4 * s + lk]; });
+  for (int ct = w; ct < D / 16; ct += 4) {
+    double wb[KS];   // W[4s + lk][16 ct + li]
+    static_for<KS>([&](auto s) { wb[s] = (double)W[(4 * s + lk) * D + 16 * ct + li]; });
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+    if (which == 0) {
+      static_for<KS>([&](auto s) { acc = mfma_f64(xa[s], wb[s], acc); });
+      // acc[r] = q_hat[i0 + 4 r + lk][16 ct + li]
+      static_for<4>([&](auto r) {
+        const int i = i0 + 4 * r + lk;
+        if (i < T) qhat[((size_t)bh * T + i) * D + 16 * ct + li] = acc[int(r)];
+      });
+    } else {
+      static_for<KS>([&](auto s) { acc = mfma_f64(wb[s], xa[s], acc); });
+      // acc[r] = k_hat[i0 + li][16 ct + 4 r + lk]
+      if (i0 + li < T) {
+        static_for<4>([&](auto r) { khatT[((size_t)bh * D + 16 * ct + 4 * r + lk) * T + i0 + li] = acc[int(r)]; });
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// Scores + Top-k: one workgroup per (R query blocks, head).  Phase 1: every thread scores
-// key blocks j = tid, tid+256, ... against the R query rows (fp64; k_hat read once per
-// workgroup) into LDS.  Phase 2: one wave per row picks the topk largest scores by
-// repeated wave arg-max (ties -> lower j), then writes the mask row and the ascending LUT
-// row by ballot compaction.
+// Scores + Top-k: one workgroup per (R query blocks, head), 256 threads.
+//
+// Phase 1: scores q_hat k_hat^T / sqrt(d) in fp64 on the matrix cores.  The A operand is the
+// 16 x D tile of q_hat rows (rows past R repeat earlier rows and are discarded); wave w takes
+// the 16-key tiles tt = w, w + 4, ..., loading the k_hat operand one half tile (D/2 channels)
+// ahead of the multiplies.  The scores are stored in LDS as order-preserving 64-bit keys.
+//
+// Phase 2: one wave per row.  The topk-th largest key is found by a bitwise binary search:
+// bit by bit from the top, a candidate threshold is kept when at least topk keys reach it
+// (counted with ballots); the search stops as soon as exactly topk keys reach the threshold.
+// The high 32 bits are searched first; the low 32 bits only when the high halves tie.
+// Keys equal to the final threshold are taken in increasing j until topk are chosen, which
+// gives the lower block index on ties.  The mask row and the ascending LUT row follow by
+// ballot compaction.
 // ---------------------------------------------------------------------------------------
-constexpr int kMaxSlots = 64;   // T <= 64 * 64 = 4096
 
-template <int R, int MAXS>
-__global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ qhat,
-                                                   const double* __restrict__ khatT, int T, int D,
-                                                   int topk, double inv_sqrt_d,
-                                                   int32_t* __restrict__ lut, uint8_t* __restrict__ mask) {
-  extern __shared__ double smem_d[];
-  double* qs = smem_d;            // [R][D]
-  double* sc = smem_d + R * D;    // [R][T]
-  const int bh = blockIdx.y, i0 = blockIdx.x * R, tid = threadIdx.x;
+// Order-preserving map of a double to an unsigned key (-0.0 is taken as +0.0).
+__device__ __forceinline__ uint64_t score_key(double v) {
+  uint64_t u = __double_as_longlong(v);
+  if (u == 0x8000000000000000ull) u = 0;
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
 
-  for (int x = tid; x < R * D; x += 256) {
-    const int r = x / D, c = x % D;
-    const int i = i0 + r;
-    qs[x] = (i < T) ? qhat[((size_t)bh * T + i) * D + c] : 0.0;
-  }
-  __syncthreads();
-  for (int j = tid; j < T; j += 256) {
-    double acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    const double* kc = khatT + (size_t)bh * D * T + j;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) {
-      const double kv = kc[(size_t)c * T];
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * D + c], kv, acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) sc[r * T + j] = acc[r] * inv_sqrt_d;
-  }
-  __syncthreads();
+__device__ __forceinline__ int ballot_count(bool p) {
+  return __popcll(__builtin_amdgcn_ballot_w64(p));
+}
 
+template <int R, int MAXS, int D>
+__global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__ qhat,
+                                                      const double* __restrict__ khatT, int T, int topk,
+                                                      double inv_sqrt_d, int32_t* __restrict__ lut,
+                                                      uint8_t* __restrict__ mask) {
+  constexpr int KS = D / 4;    // matrix-core steps over the channels
+  constexpr int HS = KS / 2;   // steps per half tile
+  extern __shared__ uint64_t keys_s[];   // [R][T]
+  // consecutive row blocks of a head run on one XCD, which then holds that head's k_hat in L2
+  const int nrb = gridDim.x;
+  const int lid = xcd_remap(blockIdx.x + nrb * blockIdx.y, nrb * gridDim.y);
+  const int bh = lid / nrb, i0 = (lid % nrb) * R, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const int S = (T + 63) >> 6;
-  for (int r = w; r < R; r += 4) {
-    const int i = i0 + r;
-    if (i >= T) break;
-    double v[MAXS];
-#pragma unroll
-    for (int s = 0; s < MAXS; ++s) {
+  {
+    const int li = lane & 15, lk = lane >> 4;
+    const int arow = min(i0 + li % R, T - 1);
+    const double* qrow = qhat + ((size_t)bh * T + arow) * D + lk;
+    double qa[KS];
+    static_for<KS>([&](auto s) { qa[s] = qrow[4 * s]; });
+    const double* kb = khatT + ((size_t)bh * D + lk) * T;
+    const int ntiles = (T + 15) >> 4;
+    // half tiles: the k_hat operand of steps half*HS .. half*HS + HS - 1 of key tile tt
+    double kv[2][HS];
+    auto load_half = [&](double(&dst)[HS], int tt, int half) {
+      const int j = min(16 * tt + li, T - 1);
+      static_for<HS>([&](auto s) { dst[s] = kb[(size_t)(4 * (half * HS + s)) * T + j]; });
+    };
+    if (w < ntiles) load_half(kv[0], w, 0);
+    for (int tt = w; tt < ntiles; tt += 4) {
+      load_half(kv[1], tt, 1);
+      // two accumulators (even / odd steps) keep two independent chains in flight
+      f64x4 acc0 = f64x4{0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+      static_for<HS / 2>([&](auto s) {
+        acc0 = mfma_f64(qa[2 * s], kv[0][2 * s], acc0);
+        acc1 = mfma_f64(qa[2 * s + 1], kv[0][2 * s + 1], acc1);
+      });
+      if (tt + 4 < ntiles) load_half(kv[0], tt + 4, 0);
+      static_for<HS / 2>([&](auto s) {
+        acc0 = mfma_f64(qa[HS + 2 * s], kv[1][2 * s], acc0);
+        acc1 = mfma_f64(qa[HS + 2 * s + 1], kv[1][2 * s + 1], acc1);
+      });
+      const f64x4 acc = acc0 + acc1;
+      const int j = 16 * tt + li;
+      static_for<4>([&](auto r) {
+        const int row = 4 * r + lk;   // accumulator r holds tile row 4r + lane/16
+        if (row < R && j < T) keys_s[row * T + j] = score_key(acc[int(r)] * inv_sqrt_d);
+      });
+    }
+  }
+  __syncthreads();
+
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  // Finish row r from the threshold found on the high halves: search the low halves when the
+  // high halves tie at the boundary, then emit the LUT and mask rows.
+  auto finish_row = [&](int r, uint32_t thr_hi, bool exact) {
+    uint64_t key[MAXS];
+    static_for<MAXS>([&](auto s) {
       const int j = 64 * s + lane;
-      v[s] = (s < S && j < T) ? sc[r * T + j] : -INFINITY;
-    }
-    uint64_t sel = 0;
-    for (int it = 0; it < topk; ++it) {
-      double bv = -INFINITY;
-      int bj = 0x7fffffff;
-#pragma unroll
-      for (int s = 0; s < MAXS; ++s) {
-        if (s < S) {
-          const int j = 64 * s + lane;
-          if (!((sel >> s) & 1ull) && j < T && (v[s] > bv || bj == 0x7fffffff)) {
-            bv = v[s];
-            bj = j;
-          }
+      key[s] = j < T ? keys_s[r * T + j] : 0ull;   // 0 is below every score key
+    });
+    uint64_t thr = (uint64_t)thr_hi << 32;
+    if (!exact) {
+      // low 32 bits among the keys whose high half equals thr_hi; keys above it count as base
+      int base_cnt = 0;
+      uint32_t lo[MAXS];
+      static_for<MAXS>([&](auto s) {
+        const uint32_t hs = (uint32_t)(key[s] >> 32);
+        base_cnt += ballot_count(hs > thr_hi);
+        lo[s] = hs == thr_hi ? (uint32_t)key[s] : 0u;   // 0 never reaches a candidate
+      });
+      uint32_t thr_lo = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr_lo | (1u << bit);
+        uint64_t bl[MAXS];
+        static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(lo[s] >= cand); });
+        int cnt = base_cnt;
+        static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
+        if (cnt >= topk) {
+          thr_lo = cand;
+          if (cnt == topk) break;
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (oj != 0x7fffffff && (bj == 0x7fffffff || ov > bv || (ov == bv && oj < bj))) {
-          bv = ov;
-          bj = oj;
-        }
-      }
-      if (bj == 0x7fffffff) break;
-      if ((bj & 63) == lane) sel |= 1ull << (bj >> 6);
+      thr |= thr_lo;
     }
-    const size_t row = (size_t)bh * T + i;
+    // keys above thr are all taken; keys equal to thr fill the rest in increasing j
+    int need = topk;
+    static_for<MAXS>([&](auto s) { need -= ballot_count(key[s] > thr); });
+    const size_t row = (size_t)bh * T + i0 + r;
     int base = 0;
-    for (int s = 0; s < S; ++s) {
+    static_for<MAXS>([&](auto s) {
       const int j = 64 * s + lane;
-      const bool on = (sel >> s) & 1ull;
-      const uint64_t b = __ballot(on);
-      if (on) lut[row * topk + base + __popcll(b & ((1ull << lane) - 1ull))] = j;
-      base += __popcll(b);
+      const uint64_t eq = __builtin_amdgcn_ballot_w64(key[s] == thr);
+      const int n_eq = __popcll(eq);
+      const int take = n_eq < need ? n_eq : need;
+      const bool on = key[s] > thr || (key[s] == thr && __popcll(eq & lt_mask) < take);
+      need -= take;
+      const uint64_t bmask = __builtin_amdgcn_ballot_w64(on);
+      if (on) lut[row * topk + base + __popcll(bmask & lt_mask)] = j;
+      base += __popcll(bmask);
       if (j < T) mask[row * T + j] = on ? 1 : 0;
+    });
+  };
+
+  // J rows of a wave are searched together, so that their independent steps overlap.
+  constexpr int J = (MAXS <= 8) ? R / 4 : 1;
+  for (int r0 = w * J; r0 < R; r0 += 4 * J) {
+    uint32_t hi[J][MAXS];
+    uint32_t thr[J];
+    bool done[J];
+    static_for<J>([&](auto jj) {
+      const int r = r0 + jj;
+      static_for<MAXS>([&](auto s) {
+        const int j = 64 * s + lane;
+        hi[jj][s] = (j < T && i0 + r < T) ? (uint32_t)(keys_s[r * T + j] >> 32) : 0u;
+      });
+      thr[jj] = 0;
+      done[jj] = i0 + r >= T;   // rows past T are skipped
+    });
+    // Largest high-half threshold reached by at least topk keys; a row is done once exactly
+    // topk keys reach its threshold (all ballots of a step are formed before they are counted).
+    for (int bit = 31; bit >= 0; --bit) {
+      bool all = true;
+      static_for<J>([&](auto jj) {
+        const uint32_t cand = thr[jj] | (1u << bit);
+        uint64_t bl[MAXS];
+        static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(hi[jj][s] >= cand); });
+        int cnt = 0;
+        static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
+        const bool take = !done[jj] && cnt >= topk;
+        thr[jj] = take ? cand : thr[jj];
+        done[jj] = done[jj] || (take && cnt == topk);
+        all = all && done[jj];
+      });
+      if (all) break;
     }
+    static_for<J>([&](auto jj) {
+      const int r = r0 + jj;
+      if (i0 + r < T) {
+        // a row left undone after bit 0 ties in its high halves at the boundary
+        finish_row(r, thr[jj], done[jj]);
+      }
+    });
   }
 }
 
-constexpr size_t kTopkLdsMax = 160 * 1024;
+// LDS for the score keys of one workgroup: R rows of T keys.
+constexpr size_t kTopkLdsBudget = 160 * 1024;
 
-template <int R, int MAXS>
+template <int R, int MAXS, int D>
 static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
-  const size_t lds = (size_t)R * (g.D + g.T) * sizeof(double);
-  static bool attr_set = false;   // the kernel may use up to 160 KB of dynamic LDS
+  const size_t lds = (size_t)R * g.T * sizeof(uint64_t);
+  static bool attr_set = false;   // dynamic LDS above the 64 KB default
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)kTopkLdsMax);
+    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)kTopkLdsBudget);
     attr_set = true;
   }
   dim3 grid((g.T + R - 1) / R, g.BH);
-  hipLaunchKernelGGL((topk_kernel<R, MAXS>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.D, g.topk,
+  hipLaunchKernelGGL((topk_kernel<R, MAXS, D>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
                      1.0 / sqrt((double)g.D), t.lut, t.mask);
 }
 
-// candidate slots per lane: the smallest power of two >= ceil(T / 64)
-template <int R>
+// Rows per workgroup R: 16 (one matrix-core tile) when the keys fit in the LDS budget, else
+// 8 or 4.  Candidate slots per lane MAXS: the smallest power of two >= ceil(T / 64).  T <= 4096
+// leaves the pairs below.
+template <int D>
 static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+  int R = 16;
+  while (R > 4 && (size_t)R * g.T * sizeof(uint64_t) > kTopkLdsBudget) R >>= 1;
   const int S = (g.T + 63) / 64;
-  if (S <= 4) launch_topk_s<R, 4>(g, t, ws, s);
-  else if (S <= 8) launch_topk_s<R, 8>(g, t, ws, s);
-  else if (S <= 16) launch_topk_s<R, 16>(g, t, ws, s);
-  else if (S <= 32) launch_topk_s<R, 32>(g, t, ws, s);
-  else launch_topk_s<R, 64>(g, t, ws, s);
+  if (R == 16 && S <= 4) launch_topk_s<16, 4, D>(g, t, ws, s);
+  else if (R == 16 && S <= 8) launch_topk_s<16, 8, D>(g, t, ws, s);
+  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D>(g, t, ws, s);
+  else if (R == 16) launch_topk_s<16, 32, D>(g, t, ws, s);
+  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D>(g, t, ws, s);
+  else if (R == 8) launch_topk_s<8, 64, D>(g, t, ws, s);
+  else launch_topk_s<4, 64, D>(g, t, ws, s);
 }
 
 template <typename Tin, int D>
@@ -364,7 +448,7 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
   // ws.mu first holds the 32-block partials; the projection kernel reads them and writes
   // the final mean into the tail of the same region.
   double* mu_final = ws.mu + (size_t)g.BH * P32 * D;
-  hipLaunchKernelGGL(project_kernel<D>, dim3((g.T + 15) / 16, g.BH, 2), dim3(256), 0, s, ws.qsum,
+  hipLaunchKernelGGL(project_kernel<D>, dim3((g.T + kProjRows - 1) / kProjRows, g.BH, 2), dim3(256), 0, s, ws.qsum,
                      ws.ksum, ws.mu, g.N, g.T, (int)g.smooth_k, t.wq, t.wk, t.q_pool, t.k_pool,
                      t.k_mean, mu_final, ws.qhat, ws.khatT);
 }
@@ -377,16 +461,8 @@ hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspac
     if (g.D == 128) launch_route_typed<float, 128>(g, t, ws, s);
     else launch_route_typed<float, 64>(g, t, ws, s);
   }
-  // rows per workgroup: the largest power of two <= 16 whose scores fit in the LDS budget
-  int R = 16;
-  while (R > 1 && (size_t)R * (g.D + g.T) * sizeof(double) > kTopkLdsMax) R >>= 1;
-  switch (R) {
-    case 16: launch_topk<16>(g, t, ws, s); break;
-    case 8: launch_topk<8>(g, t, ws, s); break;
-    case 4: launch_topk<4>(g, t, ws, s); break;
-    case 2: launch_topk<2>(g, t, ws, s); break;
-    default: launch_topk<1>(g, t, ws, s); break;
-  }
+  if (g.D == 128) launch_topk<128>(g, t, ws, s);
+  else launch_topk<64>(g, t, ws, s);
   return hipGetLastError();
 }
 

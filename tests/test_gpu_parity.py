@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import sla2_inputs as I
+from oracle import sla2_oracle as O
 from tests.gpu_util import (TOL_F32, TOL_LOWP, check_head, compare, oracle_head, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
@@ -86,6 +87,25 @@ def test_mfma_fp8_operand_layout_and_scale():
     assert rel <= 2.0 ** -12
 
 
+def test_mfma_f64_operand_layout():
+    import torch
+    from sparse_linear_attention_pool_amd import binding as Bn
+    rng = np.random.default_rng(2)
+    # small integers: every product and sum is exact in fp64, so the result is bit-exact
+    A = rng.integers(-64, 64, (16, 4)).astype(np.float64)
+    Bm = rng.integers(-64, 64, (4, 16)).astype(np.float64)
+    a = np.array([A[l % 16, l // 16] for l in range(64)])
+    b = np.array([Bm[l // 16, l % 16] for l in range(64)])
+    dd = torch.zeros((64, 4), dtype=torch.float64, device="cuda")
+    Bn.sla2_selftest_mfma(2, torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), dd)
+    d = dd.cpu().numpy()
+    got = np.zeros((16, 16))
+    for l in range(64):
+        for r in range(4):
+            got[4 * r + l // 16, l % 16] = d[l, r]   # fp64 output rows are interleaved
+    assert np.array_equal(got, A @ Bm)
+
+
 # ----------------------------------------------------------------------------- whole path
 SMALL = [
     # (base, overrides)
@@ -133,6 +153,36 @@ def test_smoothing_off_and_topk_one():
     check_head(w, inp, out, 0, 0, topk=1, smooth_k=False)
     out = run_gpu(w, inp, topk=1, smooth_k=True)
     check_head(w, inp, out, 0, 5, topk=1, smooth_k=True)
+
+
+def test_topk_exact_and_near_ties():
+    """Router Top-k where the k-th and (k+1)-th scores tie exactly (repeated key blocks) or
+    differ only far below the top 32 bits of their fp64 keys (one element 1 ulp apart)."""
+    T = 24
+    w = I.make_workload("C0", N=64 * T, H=2, seed=44, name="router ties")
+    inp = I.generate(w)
+    k = inp["k"]
+    for j in range(6):
+        k[:, :, (12 + j) * 64:(13 + j) * 64] = k[:, :, j * 64:(j + 1) * 64]
+        blk = k[:, :, (6 + j) * 64:(7 + j) * 64].copy()
+        blk[:, :, 5, 3] = np.nextafter(blk[:, :, 5, 3], np.float32(np.inf))
+        k[:, :, (18 + j) * 64:(19 + j) * 64] = blk
+    exact_hits = near_hits = 0
+    for topk in range(1, T):
+        out = run_gpu(w, inp, topk=topk, with_lse=False)
+        for h in range(w.H):
+            route = O.route_head(inp["q"][0, h], inp["k"][0, h], inp["wq"], inp["wk"], topk, True)
+            sc, lut = route["scores"], out["lut"][0, h]
+            for i in range(T):
+                srt = np.sort(sc[i])[::-1]
+                gap = srt[topk - 1] - srt[topk]
+                exact_hits += gap == 0
+                near_hits += 0 < gap < 1e-6 * abs(srt[topk - 1])
+                # exact ties go to the lower index; every other gap here is far above fp64
+                # rounding, so the choice must be the oracle's
+                assert np.array_equal(lut[i], route["lut"][i]), (topk, h, i, lut[i], route["lut"][i])
+    say(f"    boundary at an exact tie in {exact_hits} rows, at a near tie in {near_hits} rows")
+    assert exact_hits > 0 and near_hits > 0
 
 
 def test_runs_are_deterministic():
