@@ -21,6 +21,9 @@ constexpr int kBlock = 64;           // b_q = b_kv (SLA page, section 2 Q2)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kFp8Max = 448.0f;    // largest finite OCP e4m3 magnitude
+// phi values lie in (0, 1]: their e4m3 codes use the fixed scale 1/448, so a product of two
+// codes carries the factor 448^2.
+constexpr float kPhiCodeScale = 448.0f;
 
 // E8M0 exponent passed to the scaled fp8 matrix-core instruction for "no extra scaling".
 #ifndef SLA2_FP8_MFMA_SCALE

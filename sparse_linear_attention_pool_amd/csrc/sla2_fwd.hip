@@ -28,10 +28,9 @@ struct FwdArgs {
   const float* q_scale;   // [BH, T]
   const float* k_scale;
   const uint16_t* vt;     // [BH, T, D, 64]
-  const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of phi(K~)
-  const float* phik_scale;  // [BH, T]
+  const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of 448 phi(K~), features permuted
   const int32_t* lut;     // [BH, T, topk]
-  const float* h_sum;     // [BH, D, D]
+  const uint16_t* hbf;    // [BH, D, D] bf16 LDS image of H^T = h_sum (see Workspace::hbf)
   const float* z_sum;     // [BH, D]
   const float* alpha;     // [H, D]
   const float* k_mean;    // [BH, D] (lse of the native mode is shifted to the smoothed keys)
@@ -41,11 +40,11 @@ struct FwdArgs {
   float eps;
 };
 
-// LDS geometry of one staged key block (bytes).  Rows are stored unpadded with the 16-byte
-// chunks of each row permuted (physical chunk = logical chunk XOR (row mod 8), mod 16 for
-// 256-byte rows), so that the 16-byte operand reads of 8 consecutive lanes (8 consecutive
-// rows, same logical chunk) hit distinct banks.
-template <bool FP8>
+// LDS geometry of one staged key block (bytes) for a workgroup of NT threads.  Rows are stored
+// unpadded with the 16-byte chunks of each row permuted (physical chunk = logical chunk XOR
+// (row mod 8), mod 16 for 256-byte rows), so that the 16-byte operand reads of consecutive
+// lanes (consecutive rows, same logical chunk) hit distinct banks.
+template <bool FP8, int NT>
 struct FwdLds {
   static constexpr int KROW = FP8 ? 128 : 256;    // one key row: 128 e4m3 codes or 128 bf16
   static constexpr int KTILE = 64 * KROW;
@@ -54,10 +53,10 @@ struct FwdLds {
   static constexpr int POFF = KTILE, VOFF = KTILE + PTILE;
   static constexpr int STAGE = KTILE + PTILE + VTILE;
   static constexpr int BYTES = 2 * STAGE;         // the tile being read, the tile being written
-  static constexpr int KLOADS = KTILE / 4096;     // 16-byte loads per thread per tile part
-  static constexpr int PLOADS = PTILE / 4096;
-  static constexpr int VLOADS = VTILE / 4096;
-  static_assert(128 * 256 + 512 <= BYTES, "epilogue H^T tile must fit in the staging buffers");
+  static constexpr int KLOADS = KTILE / (16 * NT);   // 16-byte loads per thread per tile part
+  static constexpr int PLOADS = PTILE / (16 * NT);
+  static constexpr int VLOADS = VTILE / (16 * NT);
+  static_assert(128 * 256 <= BYTES, "epilogue H^T tile must fit in the staging buffers");
 };
 
 // Barrier for LDS hand-offs inside the routed-block loop: this wave's LDS writes are retired,
@@ -72,24 +71,28 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // This thread's share of one key block's tiles, in registers.
-template <bool FP8>
+template <bool FP8, int NT>
 struct TileRegs {
-  u32x4 kk[FwdLds<FP8>::KLOADS];
-  u32x4 pp[FwdLds<FP8>::PLOADS];
-  u32x4 vv[FwdLds<FP8>::VLOADS];
+  u32x4 kk[FwdLds<FP8, NT>::KLOADS];
+  u32x4 pp[FwdLds<FP8, NT>::PLOADS];
+  u32x4 vv[FwdLds<FP8, NT>::VLOADS];
 };
 
-// Thread tid moves the 16-byte chunks q = tid + 256p: K row q / (chunks per row), logical
+// Thread tid moves the 16-byte chunks q = tid + NT p: K row q / (chunks per row), logical
 // chunk q % (chunks per row); phi(K~) codes row q / 8, chunk q % 8; V^T row q / 8, chunk q % 8.
-template <bool FP8>
-__device__ __forceinline__ void load_tile(const FwdArgs& A, int bh, int j, int tid, TileRegs<FP8>& t) {
-  using L = FwdLds<FP8>;
+template <bool FP8, int NT>
+__device__ __forceinline__ void load_tile(const FwdArgs& A, int bh, int j, int tid, TileRegs<FP8, NT>& t) {
+  using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
+  // j is wave-uniform: one scalar base per tile part plus a fixed 32-bit offset per lane
+  const size_t blk = (size_t)bh * A.T + j;
+  const uint8_t* kbase = FP8 ? A.k8 + blk * (kBlock * D) : nullptr;
+  const uint8_t* pbase = A.phik8 + blk * (kBlock * D);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(A.vt + blk * (D * kBlock));
   static_for<L::KLOADS>([&](auto P) {
-    const int qd = tid + 256 * P;
+    const int qd = tid + NT * P;
     if constexpr (FP8) {
-      const int row = qd >> 3, lc = qd & 7;
-      t.kk[P] = *reinterpret_cast<const u32x4*>(A.k8 + (((size_t)bh * A.T + j) * kBlock + row) * D + 16 * lc);
+      t.kk[P] = *reinterpret_cast<const u32x4*>(kbase + (uint32_t)(16 * qd));
     } else {
       const int row = qd >> 4, lc = qd & 15;
       const int tok = min(kBlock * j + row, A.N - 1);   // rows past N: any finite row, masked later
@@ -97,20 +100,18 @@ __device__ __forceinline__ void load_tile(const FwdArgs& A, int bh, int j, int t
     }
   });
   static_for<L::PLOADS>([&](auto P) {
-    const int qd = tid + 256 * P, row = qd >> 3, lc = qd & 7;
-    t.pp[P] = *reinterpret_cast<const u32x4*>(A.phik8 + (((size_t)bh * A.T + j) * kBlock + row) * D + 16 * lc);
+    t.pp[P] = *reinterpret_cast<const u32x4*>(pbase + (uint32_t)(16 * (tid + NT * P)));
   });
   static_for<L::VLOADS>([&](auto P) {
-    const int qd = tid + 256 * P, row = qd >> 3, lc = qd & 7;
-    t.vv[P] = *reinterpret_cast<const u32x4*>(A.vt + (((size_t)bh * A.T + j) * D + row) * kBlock + 8 * lc);
+    t.vv[P] = *reinterpret_cast<const u32x4*>(vbase + (uint32_t)(16 * (tid + NT * P)));
   });
 }
 
-template <bool FP8>
-__device__ __forceinline__ void store_tile(uint8_t* stage, int tid, const TileRegs<FP8>& t) {
-  using L = FwdLds<FP8>;
+template <bool FP8, int NT>
+__device__ __forceinline__ void store_tile(uint8_t* stage, int tid, const TileRegs<FP8, NT>& t) {
+  using L = FwdLds<FP8, NT>;
   static_for<L::KLOADS>([&](auto P) {
-    const int qd = tid + 256 * P;
+    const int qd = tid + NT * P;
     if constexpr (FP8) {
       const int row = qd >> 3, lc = qd & 7;
       *reinterpret_cast<u32x4*>(stage + row * L::KROW + 16 * (lc ^ (row & 7))) = t.kk[P];
@@ -120,12 +121,40 @@ __device__ __forceinline__ void store_tile(uint8_t* stage, int tid, const TileRe
     }
   });
   static_for<L::PLOADS>([&](auto P) {
-    const int qd = tid + 256 * P, row = qd >> 3, lc = qd & 7;
+    const int qd = tid + NT * P, row = qd >> 3, lc = qd & 7;
     *reinterpret_cast<u32x4*>(stage + L::POFF + row * 128 + 16 * (lc ^ (row & 7))) = t.pp[P];
   });
   static_for<L::VLOADS>([&](auto P) {
-    const int qd = tid + 256 * P, row = qd >> 3, lc = qd & 7;
+    const int qd = tid + NT * P, row = qd >> 3, lc = qd & 7;
     *reinterpret_cast<u32x4*>(stage + L::VOFF + row * 128 + 16 * (lc ^ (row & 7))) = t.vv[P];
+  });
+}
+
+// The 32 KB bf16 image of H^T (already in its LDS layout) through the tile registers: thread
+// tid moves the 16-byte chunks q = tid + NT p, in order over kk, pp, vv.
+template <bool FP8, int NT>
+__device__ __forceinline__ void load_himage(const FwdArgs& A, int bh, int tid, TileRegs<FP8, NT>& t) {
+  using L = FwdLds<FP8, NT>;
+  constexpr int NCH = 2048 / NT;
+  static_assert(NCH <= L::KLOADS + L::PLOADS + L::VLOADS, "tile registers too small for the H^T image");
+  const u32x4* src = reinterpret_cast<const u32x4*>(A.hbf + (size_t)bh * 128 * 128);
+  static_for<NCH>([&](auto P) {
+    const u32x4 v = src[tid + NT * P];
+    if constexpr (P < L::KLOADS) t.kk[P] = v;
+    else if constexpr (P < L::KLOADS + L::PLOADS) t.pp[P - L::KLOADS] = v;
+    else t.vv[P - L::KLOADS - L::PLOADS] = v;
+  });
+}
+
+template <bool FP8, int NT>
+__device__ __forceinline__ void store_himage(uint8_t* dst, int tid, const TileRegs<FP8, NT>& t) {
+  using L = FwdLds<FP8, NT>;
+  constexpr int NCH = 2048 / NT;
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  static_for<NCH>([&](auto P) {
+    if constexpr (P < L::KLOADS) d[tid + NT * P] = t.kk[P];
+    else if constexpr (P < L::KLOADS + L::PLOADS) d[tid + NT * P] = t.pp[P - L::KLOADS];
+    else d[tid + NT * P] = t.vv[P - L::KLOADS - L::PLOADS];
   });
 }
 
@@ -140,25 +169,37 @@ __device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g
 
 constexpr int kLutCache = 512;   // routed blocks whose index and scales are cached in LDS
 
-// Per-lane state of the routed-block loop (one query per lane, see the kernel comment).
+// Per-lane state of the routed-block loop: QT queries per lane (one per 16-query tile).
+template <int QT>
 struct FwdState {
-  f32x4 acc[8];          // O_s^T: sum_s p_s V_s, features 16dt + 4g + rr
-  f32x4 accl[8];         // sum over routed keys of (phi(q).phi(k_s)) V_s, same layout
-  float m_run, l_run;    // running max (log2 units) and this lane's partial sum of p
-  float a_run;           // this lane's partial sum of phi(q).phi(k_s) over routed keys
+  f32x4 acc[QT][8];      // O_s^T: sum_s p_s V_s, features 16dt + 4g + rr
+  f32x4 accl[QT][8];     // sum over routed keys of (phi(q).phi(k_s)) V_s, same layout
+  float m_run[QT];       // running max (log2 units)
+  float l_run[QT];       // this lane's partial sum of p
+  float a_run[QT];       // this lane's partial sum of phi(q).phi(k_s) over routed keys
+};
+
+// Operands of this lane's queries that stay in registers for the whole loop.
+template <int QT>
+struct QueryOps {
+  i32x8 q8[QT];          // FP8: e4m3 codes of features 32g..32g+31 (B of S^T = K Q^T)
+  bf16x8 qb[QT][4];      // native: bf16 features 32s + 8g + e
+  i32x8 phq8[QT];        // e4m3 codes of 448 phi(q), features 32s + 8g + e in (s, e) order
+  bf16x8 phb[QT][4];     // phi(q) in bf16, features 32s + 8g + e (B of O_l^T = H^T phi(Q)^T)
+  float dz[QT];          // phi(q).Z_tot over all 128 features (bf16 phi(q))
 };
 
 // One routed block, the r-th LUT entry, whose tile is in LDS stage r % 2.  t holds the tile
 // of block r+1 (loaded one iteration earlier); at the end it goes to the other stage and t is
 // refilled with the tile of block r+2.  mask: the block may be partial (only the last LUT
 // entry can be: LUT rows are ascending and only block T-1 is partial).
-template <bool FP8, bool LUT_LDS>
-__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState& st, uint8_t* smem, const int* lutS,
-                                              const float* kscS, const float* pscS, const int32_t* lutG, int r,
-                                              int topk, int bh, int l16, int g, int tid, const i32x8& q8op,
-                                              const bf16x8 (&qop)[4], const i32x8& phq8op, float cq, float cphq,
-                                              bool mask, TileRegs<FP8>& t) {
-  using L = FwdLds<FP8>;
+template <bool FP8, bool LUT_LDS, int QT>
+__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, const int* lutS,
+                                              const float* kscS, const int32_t* lutG, int r,
+                                              int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
+                                              float cq, bool mask, TileRegs<FP8, 256 / QT>& t) {
+  constexpr int NT = 256 / QT;
+  using L = FwdLds<FP8, NT>;
   // the LUT row comes from the LDS cache, or from global memory when it is longer than the
   // cache (a separate instantiation, so no load ever has to serve both address spaces)
   auto lut_at = [&](int x) {
@@ -168,11 +209,11 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState& st, ui
   const int j = lut_at(r);
   const uint8_t* stage = smem + (r & 1) * L::STAGE;
 
-  // ---- S^T = K_j Q^T and Ph^T = phi(K_j) phi(Q)^T: keys 16mt + 4g + rr x queries l16.
-  // Operand reads run one key tile ahead of the matrix-core products (read tile mt+1, then
-  // multiply tile mt); the scheduling fences keep the compiler from hoisting every read,
-  // which would hold all operands of the block in registers at once.
-  f32x4 S[4], Ph[4];
+  // ---- S^T = K_j Q^T and Ph^T = phi(K_j) phi(Q)^T: keys 16mt + 4g + rr x queries l16 of each
+  // query tile.  Operand reads run one key tile ahead of the matrix-core products; the
+  // scheduling fences keep the compiler from hoisting every read, which would hold all
+  // operands of the block in registers at once.
+  f32x4 S[QT][4], Ph[QT][4];
   if constexpr (FP8) {
     i32x8 ka = lds_fp8_row(stage, l16, g), pa = lds_fp8_row(stage + L::POFF, l16, g);
 #pragma unroll
@@ -182,8 +223,11 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState& st, ui
         kb = lds_fp8_row(stage, 16 * (mt + 1) + l16, g);
         pb = lds_fp8_row(stage + L::POFF, 16 * (mt + 1) + l16, g);
       }
-      S[mt] = mfma_fp8(ka, q8op, f32x4{0.f, 0.f, 0.f, 0.f});
-      Ph[mt] = mfma_fp8(pa, phq8op, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        S[qt][mt] = mfma_fp8(ka, qo.q8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+        Ph[qt][mt] = mfma_fp8(pa, qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
       __builtin_amdgcn_sched_barrier(0);
       ka = kb;
       pa = pb;
@@ -193,62 +237,74 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState& st, ui
     for (int mt = 0; mt < 4; ++mt) {
       const int row = 16 * mt + l16;
       const uint8_t* krow = stage + row * L::KROW;
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) S[qt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * s + g) ^ (row & 15)));
-        sacc = mfma_bf16(__builtin_bit_cast(bf16x8, a), qop[s], sacc);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[qt][mt] = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.qb[qt][s], S[qt][mt]);
       }
-      S[mt] = sacc;
-      Ph[mt] = mfma_fp8(lds_fp8_row(stage + L::POFF, row, g), phq8op, f32x4{0.f, 0.f, 0.f, 0.f});
+      const i32x8 pa = lds_fp8_row(stage + L::POFF, row, g);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) Ph[qt][mt] = mfma_fp8(pa, qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float cj = cq, pj;
-  if constexpr (LUT_LDS) {
-    if constexpr (FP8) cj = cq * kscS[r];
-    pj = cphq * pscS[r];
-  } else {
-    if constexpr (FP8) cj = cq * A.k_scale[(size_t)bh * A.T + j];
-    pj = cphq * A.phik_scale[(size_t)bh * A.T + j];
+  float cj = cq;
+  if constexpr (FP8) {
+    if constexpr (LUT_LDS) cj = cq * kscS[r];
+    else cj = cq * A.k_scale[(size_t)bh * A.T + j];
   }
   if (mask) {   // phi codes of keys past N are zero already; only the scores need it
     const int nvalid = min(kBlock, A.N - kBlock * j);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (16 * mt + 4 * g + rr >= nvalid) S[mt][rr] = -INFINITY;
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (16 * mt + 4 * g + rr >= nvalid) S[qt][mt][rr] = -INFINITY;
   }
 
-  // ---- online softmax for this lane's query.  The running max is only raised when the
-  // block max exceeds it by more than 8 (log2 units), so p <= 256; the rescale is skipped
+  // ---- online softmax, one query per lane and tile.  The running max is only raised when
+  // the block max exceeds it by more than 8 (log2 units), so p <= 256; the rescale is skipped
   // by the whole wave when no lane needs it.
-  float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(S[2][0], S[2][1]), fmaxf(S[2][2], S[2][3])),
-                       fmaxf(fmaxf(S[3][0], S[3][1]), fmaxf(S[3][2], S[3][3]))));
-  mx = rows4_max(mx) * cj;
-  const bool raise = mx > st.m_run + 8.f;
-  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-    const float mnew = raise ? mx : st.m_run;
-    const float f = __builtin_amdgcn_exp2f(st.m_run - mnew);
-    st.l_run *= f;
+  float mx[QT];
+  bool raise_any = false;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= f;
-    st.m_run = mnew;
+  for (int qt = 0; qt < QT; ++qt) {
+    float m = fmaxf(S[qt][0][0], S[qt][0][1]);
+    static_for<7>([&](auto u) {   // chained three-input maxima over the remaining 14 scores
+      constexpr int a = 2 + 2 * u, b = 3 + 2 * u;
+      m = fmaxf(fmaxf(m, S[qt][a / 4][a % 4]), S[qt][b / 4][b % 4]);
+    });
+    mx[qt] = rows4_max(m) * cj;
+    raise_any = raise_any || (mx[qt] > st.m_run[qt] + 8.f);
   }
-  float psum = 0.f, asum = 0.f;
-  bf16x8 pop[2], aop[2];
+  if (__builtin_amdgcn_ballot_w64(raise_any) != 0) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float pv[8], av[8];
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mnew = mx[qt] > st.m_run[qt] + 8.f ? mx[qt] : st.m_run[qt];
+      const float f = __builtin_amdgcn_exp2f(st.m_run[qt] - mnew);
+      st.l_run[qt] *= f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.acc[qt][dt] *= f;
+      st.m_run[qt] = mnew;
+    }
+  }
+
+  // P (probabilities) and A (448^2 phi(q).phi(k), the raw product of the codes) of key half s,
+  // keys 32s + 16h + 4g + rr, as the bf16 B operands of the products below
+  bf16x8 pop[QT][2], aop[QT][2];
+  auto make_ops = [&](int qt, int s) {
+    float pv[8], av[8], psum = 0.f, asum = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[2 * s + h][rr], cj, -st.m_run));
-        av[4 * h + rr] = Ph[2 * s + h][rr] * pj;
+        pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][2 * s + h][rr], cj, -st.m_run[qt]));
+        av[4 * h + rr] = Ph[qt][2 * s + h][rr];
         psum += pv[4 * h + rr];
         asum += av[4 * h + rr];
       }
@@ -256,79 +312,152 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState& st, ui
                             pack_bf16x2(pv[6], pv[7])};
     const uint32_t aw[4] = {pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]), pack_bf16x2(av[4], av[5]),
                             pack_bf16x2(av[6], av[7])};
-    pop[s] = __builtin_bit_cast(bf16x8, pw);
-    aop[s] = __builtin_bit_cast(bf16x8, aw);
-  }
-  st.l_run += psum;
-  st.a_run += asum;
+    pop[qt][s] = __builtin_bit_cast(bf16x8, pw);
+    aop[qt][s] = __builtin_bit_cast(bf16x8, aw);
+    st.l_run[qt] += psum;
+    st.a_run[qt] += asum;
+  };
 
-  // ---- O_s^T += V^T P^T and O_corr^T += V^T Ph^T, sharing each V^T operand read; reads run
-  // one feature tile ahead of the products
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    make_ops(qt, 0);
+    make_ops(qt, 1);
+  }
+
+  // ---- O_s^T += V^T P^T and O_corr^T += V^T Ph^T, sharing each V^T operand read between the
+  // query tiles and the two products; reads run one feature tile ahead of the products
   auto vread = [&](int dt, int s) {
     const int row = 16 * dt + l16;
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
                                                                      16 * ((4 * s + g) ^ (row & 7))));
   };
-  bf16x8 v0 = vread(0, 0), v1 = vread(0, 1);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    bf16x8 n0 = v0, n1 = v1;
-    if (dt < 7) {
-      n0 = vread(dt + 1, 0);
-      n1 = vread(dt + 1, 1);
+  bf16x8 vq[2][2];
+  vq[0][0] = vread(0, 0);
+  vq[0][1] = vread(0, 1);
+  static_for<8>([&](auto dt) {
+    if constexpr (dt + 1 < 8) {
+      vq[(dt + 1) & 1][0] = vread(dt + 1, 0);
+      vq[(dt + 1) & 1][1] = vread(dt + 1, 1);
     }
-    st.acc[dt] = mfma_bf16(v0, pop[0], st.acc[dt]);
-    st.accl[dt] = mfma_bf16(v0, aop[0], st.accl[dt]);
-    st.acc[dt] = mfma_bf16(v1, pop[1], st.acc[dt]);
-    st.accl[dt] = mfma_bf16(v1, aop[1], st.accl[dt]);
+    const bf16x8 v0 = vq[dt & 1][0], v1 = vq[dt & 1][1];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      st.acc[qt][dt] = mfma_bf16(v0, pop[qt][0], st.acc[qt][dt]);
+      st.accl[qt][dt] = mfma_bf16(v0, aop[qt][0], st.accl[qt][dt]);
+      st.acc[qt][dt] = mfma_bf16(v1, pop[qt][1], st.acc[qt][dt]);
+      st.accl[qt][dt] = mfma_bf16(v1, aop[qt][1], st.accl[qt][dt]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    v0 = n0;
-    v1 = n1;
-  }
+  });
 
   // ---- the tile of block r+1 goes to the other stage (its previous tile, block r-1, was
   // consumed before the last barrier); t is refilled with the tile of block r+2
-  if (r + 1 < topk) store_tile<FP8>(smem + ((r + 1) & 1) * L::STAGE, tid, t);
-  if (r + 2 < topk) load_tile<FP8>(A, bh, lut_at(r + 2), tid, t);
+  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, tid, t);
+  if (r + 2 < topk) load_tile<FP8, NT>(A, bh, __builtin_amdgcn_readfirstlane(lut_at(r + 2)), tid, t);
+  else if (r + 2 == topk) load_himage<FP8, NT>(A, bh, tid, t);   // the epilogue's H^T, in flight early
   lds_barrier();
 }
 
-// One workgroup (4 waves) per (head, query block).  Wave w owns queries 16w..16w+15 and
-// computes S^T = K_j Q_w^T so that each lane holds one query (l % 16) and 16 of the block's
-// keys (16mt + 4(l/16) + rr): the softmax state is per lane, and P feeds the P.V product as
-// the B operand of O^T = V^T P^T without a transpose.
+// phi(q) = softmax over the 128 features of query row q (bf16 input).  This lane holds the
+// features 32s + 8g + e (s < 4, e < 8), in two operand forms:
+//  * e4m3 codes of 448 phi, in (s, e) order: the B operand of Ph^T = phi(K) phi(q)^T, whose
+//    phi(K) codes are stored with the same feature permutation;
+//  * bf16 values (B of O_l^T = H^T phi(q)^T), and their dot product with Z_tot.
+__device__ __forceinline__ void phi_q_ops(const uint16_t* qrow, const float* zsum, bool qok, int g, i32x8& codes,
+                                          bf16x8 (&phb)[4], float& dz) {
+  float y[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 u = qok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[s][2 * e] = bf16_lo(uw[e]);
+      y[s][2 * e + 1] = bf16_hi(uw[e]);
+    }
+  }
+  float mx = y[0][0];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, y[s][e]);
+  mx = rows4_max(mx);
+  float sm = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[s][e] = __builtin_amdgcn_exp2f((y[s][e] - mx) * kLog2e);
+      sm += y[s][e];
+    }
+  const float rs = 1.f / rows4_sum(sm);
+  uint32_t wds[8];
+  float d = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = y[s][e] * rs;
+    wds[2 * s] = pack_fp8x4(clamp_fp8(f[0] * kPhiCodeScale), clamp_fp8(f[1] * kPhiCodeScale),
+                            clamp_fp8(f[2] * kPhiCodeScale), clamp_fp8(f[3] * kPhiCodeScale));
+    wds[2 * s + 1] = pack_fp8x4(clamp_fp8(f[4] * kPhiCodeScale), clamp_fp8(f[5] * kPhiCodeScale),
+                                clamp_fp8(f[6] * kPhiCodeScale), clamp_fp8(f[7] * kPhiCodeScale));
+    uint32_t bw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+      d = fmaf(bf16_lo(bw[e]), zsum[32 * s + 8 * g + 2 * e], d);
+      d = fmaf(bf16_hi(bw[e]), zsum[32 * s + 8 * g + 2 * e + 1], d);
+    }
+    phb[s] = __builtin_bit_cast(bf16x8, bw);
+  }
+  codes = i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3], (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
+  dz = rows4_sum(d);
+}
+
+// One workgroup of 4/QT waves per (head, query block).  Wave w owns queries
+// 16 QT w + 16 qt + (0..15), qt < QT, and computes S^T = K_j Q^T so that each lane holds one
+// query (l % 16) of each tile and 16 of the block's keys (16mt + 4(l/16) + rr): the softmax
+// state is per lane, and P feeds the P.V product as the B operand of O^T = V^T P^T without a
+// transpose.  With QT = 2 every key-tile and V^T operand read from LDS serves two query tiles.
 // The linear branch needs, for the unrouted blocks, phi(q) H_i and phi(q).Z_i with
 // H_i = h_sum - sum over routed j of h_j.  The routed part phi(q) h_j = (phi(q) phi(K_j)^T) V_j
 // is evaluated by re-association over the same routed keys and V^T tiles as the sparse
 // branch, with phi(K~) and phi(q) as e4m3 codes (phi(q) scaled per query).
 // Pipeline per routed block r: compute on the LDS tile of block r, write the tile of block
 // r+1 (loaded one iteration earlier) to the other LDS stage, load the tile of block r+2.
-template <bool FP8, bool LUT_LDS>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs A) {
-  using L = FwdLds<FP8>;
+template <bool FP8, bool LUT_LDS, int QT>
+__global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
+  constexpr int NT = 256 / QT;
+  using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
   __shared__ int lutS[kLutCache];
   __shared__ float kscS[kLutCache];
-  __shared__ float pscS[kLutCache];
+  __shared__ float alphaS[D];
 
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
   const int bh = lid / A.T, i = lid % A.T;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int hidx = bh % A.H;
-  const int qrow = kBlock * i + 16 * w + l16;  // this lane's query token
-  const bool qok = qrow < A.N;
+  int qrow[QT];   // this lane's query tokens
+  bool qok[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    qrow[qt] = kBlock * i + 16 * QT * w + 16 * qt + l16;
+    qok[qt] = qrow[qt] < A.N;
+  }
   const int32_t* lutG = A.lut + ((size_t)bh * A.T + i) * A.topk;
   const int topk = A.topk;
 
   if constexpr (LUT_LDS) {
-    for (int x = tid; x < topk; x += 256) {
+    for (int x = tid; x < topk; x += NT) {
       const int j = lutG[x];
       lutS[x] = j;
       if constexpr (FP8) kscS[x] = A.k_scale[(size_t)bh * A.T + j];
-      pscS[x] = A.phik_scale[(size_t)bh * A.T + j];
     }
   }
+  for (int c = tid; c < D; c += NT) alphaS[c] = A.alpha[(size_t)hidx * D + c];
   __syncthreads();
   auto lut0 = [&](int x) {
     if constexpr (LUT_LDS) return lutS[x];
@@ -338,204 +467,110 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdArgs A) {
   const bool last_partial = (lut0(topk - 1) == A.T - 1) && (A.N % kBlock != 0);
 
   // prologue: tile of block 0 -> registers (-> LDS stage 0 below), then tile of block 1
-  TileRegs<FP8> t;
-  load_tile<FP8>(A, bh, lut0(0), tid, t);
+  TileRegs<FP8, NT> t;
+  load_tile<FP8, NT>(A, bh, lut0(0), tid, t);
 
-  // Q operands (B of S^T = K Q^T): FP8 codes of features 32g..32g+31, or bf16 features 32s+8g+e
-  i32x8 q8op = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-  bf16x8 qop[4];
+  QueryOps<QT> qo;
   float cq = kLog2e / sqrtf((float)D);
-  if constexpr (FP8) {
-    const uint8_t* src = A.q8 + (((size_t)bh * A.T * kBlock) + qrow) * D + 32 * g;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(src);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(src + 16);
-    q8op = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-    cq *= A.q_scale[(size_t)bh * A.T + i];
-  } else {
+  if constexpr (FP8) cq *= A.q_scale[(size_t)bh * A.T + i];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 a = qok ? *reinterpret_cast<const u32x4*>(A.q + ((size_t)bh * A.N + qrow) * D + 32 * s + 8 * g)
-                          : u32x4{0, 0, 0, 0};
-      qop[s] = __builtin_bit_cast(bf16x8, a);
-    }
-  }
-  // phi(q) as e4m3 codes of features 32g..32g+31 with one max/448 scale for this query
-  i32x8 phq8op;
-  float cphq;
-  {
-    float x[32];
-    const uint16_t* qsrc = A.q + ((size_t)bh * A.N + qrow) * D + 32 * g;
+  for (int qt = 0; qt < QT; ++qt) {
+    if constexpr (FP8) {
+      const uint8_t* src = A.q8 + (((size_t)bh * A.T * kBlock) + qrow[qt]) * D + 32 * g;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(src + 16);
+      qo.q8[qt] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = qok ? *reinterpret_cast<const u32x4*>(qsrc + 8 * c) : u32x4{0, 0, 0, 0};
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * c + 2 * e] = bf16_lo(vw[e]);
-        x[8 * c + 2 * e + 1] = bf16_hi(vw[e]);
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = qok[qt] ? *reinterpret_cast<const u32x4*>(A.q + ((size_t)bh * A.N + qrow[qt]) * D + 32 * s + 8 * g)
+                                : u32x4{0, 0, 0, 0};
+        qo.qb[qt][s] = __builtin_bit_cast(bf16x8, a);
       }
     }
-    float mx = x[0];
+    phi_q_ops(A.q + ((size_t)bh * A.N + qrow[qt]) * D, A.z_sum + (size_t)bh * D, qok[qt], g, qo.phq8[qt],
+              qo.phb[qt], qo.dz[qt]);
+  }
+
+  FwdState<QT> st;
 #pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    mx = rows4_max(mx);
-    float sm = 0.f, pmx = 0.f;
+  for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = __builtin_amdgcn_exp2f((x[e] - mx) * kLog2e);
-      sm += x[e];
-      pmx = fmaxf(pmx, x[e]);
+    for (int dt = 0; dt < 8; ++dt) {
+      st.acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.accl[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    sm = rows4_sum(sm);
-    pmx = rows4_max(pmx) / sm;                 // max of phi(q)
-    float sp = __fdiv_rn(pmx, kFp8Max);
-    if (!(sp > 0.f)) sp = 1.f;
-    const float inv = 1.f / (sm * sp);          // code = phi / sp = e / (sum * sp)
-    uint32_t wds[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      wds[c] = pack_fp8x4(clamp_fp8(x[4 * c] * inv), clamp_fp8(x[4 * c + 1] * inv), clamp_fp8(x[4 * c + 2] * inv),
-                          clamp_fp8(x[4 * c + 3] * inv));
-    phq8op = i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3], (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
-    cphq = sp;
+    st.m_run[qt] = -INFINITY;
+    st.l_run[qt] = 0.f;
+    st.a_run[qt] = 0.f;
   }
 
-  FwdState st;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.accl[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
-  st.a_run = 0.f;
-
-  store_tile<FP8>(smem, tid, t);
-  if (topk > 1) load_tile<FP8>(A, bh, lut0(1), tid, t);
+  store_tile<FP8, NT>(smem, tid, t);
+  if (topk > 1) load_tile<FP8, NT>(A, bh, lut0(1), tid, t);
+  else load_himage<FP8, NT>(A, bh, tid, t);
   lds_barrier();
 
   for (int r = 0; r < topk; ++r)
-    fwd_iteration<FP8, LUT_LDS>(A, st, smem, lutS, kscS, pscS, lutG, r, topk, bh, l16, g, tid, q8op, qop, phq8op, cq,
-                                cphq, last_partial && r == topk - 1, t);
+    fwd_iteration<FP8, LUT_LDS, QT>(A, st, smem, lutS, kscS, lutG, r, topk, bh, l16, g, tid, qo, cq,
+                                    last_partial && r == topk - 1, t);
 
   // ---------------- epilogue ----------------
-  const float l_tot = rows4_sum(st.l_run);
-  const float a_tot = rows4_sum(st.a_run);
-  const float inv_l = 1.f / l_tot;
-
-  // H^T = h_sum (bf16, rows c, columns a; 256-byte rows, chunk k stored at k ^ (row % 16)) and
-  // Z = z_sum into LDS; every wave needs all of them.
+  // H^T (bf16 image loaded during the last iterations) into the free staging buffers; every
+  // wave needs all of it.
   uint8_t* Hs = smem;
-  float* Zs = reinterpret_cast<float*>(smem + 128 * 256);
-  {
-    const float* hsum = A.h_sum + (size_t)bh * D * D;
+  store_himage<FP8, NT>(Hs, tid, t);
+  lds_barrier();
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int qd = tid + 256 * p;          // 8 features of row qd / 16, chunk qd % 16
-      const int cr = qd >> 4, ch = qd & 15;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(hsum + cr * D + 8 * ch);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(hsum + cr * D + 8 * ch + 4);
-      u32x4 hv;
-      hv.x = pack_bf16x2(x0.x, x0.y);
-      hv.y = pack_bf16x2(x0.z, x0.w);
-      hv.z = pack_bf16x2(x1.x, x1.y);
-      hv.w = pack_bf16x2(x1.z, x1.w);
-      *reinterpret_cast<u32x4*>(Hs + cr * 256 + 16 * (ch ^ (cr & 15))) = hv;
-    }
-    if (tid < D) Zs[tid] = A.z_sum[(size_t)bh * D + tid];
-  }
-  // phi(q) in bf16 as the B operand of O_l^T = H^T phi(Q)^T: features a = 32s + 8g + e
-  float qf[4][8];
-  {
-    float qmax = -INFINITY;
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = rows4_sum(st.l_run[qt]);
+    constexpr float kCodes2 = 1.f / (kPhiCodeScale * kPhiCodeScale);   // undo the code scales
+    const float a_tot = rows4_sum(st.a_run[qt]) * kCodes2;
+    const float inv_l = 1.f / l_tot;
+    // denominator over the unrouted keys: phi(q).Z_tot - sum over routed keys of phi(q).phi(k)
+    const float inv_den = 1.f / (qo.dz[qt] - a_tot + A.eps);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 v = qok ? *reinterpret_cast<const u32x4*>(A.q + ((size_t)bh * A.N + qrow) * D + 32 * s + 8 * g)
-                          : u32x4{0, 0, 0, 0};
-      const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[s][2 * e] = bf16_lo(ww[e]);
-        qf[s][2 * e + 1] = bf16_hi(ww[e]);
-        qmax = fmaxf(qmax, fmaxf(qf[s][2 * e], qf[s][2 * e + 1]));
-      }
-    }
-    qmax = rows4_max(qmax);
-    float qsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qf[s][e] = __builtin_amdgcn_exp2f((qf[s][e] - qmax) * kLog2e);
-        qsum += qf[s][e];
-      }
-    qsum = rows4_sum(qsum);
-    const float qinv = 1.f / qsum;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] *= qinv;
-  }
-  __syncthreads();   // H^T and Z in LDS
-  bf16x8 phop[4];
-  float den = 0.f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint32_t wds[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wds[e] = pack_bf16x2(qf[s][2 * e], qf[s][2 * e + 1]);
-      den = fmaf(bf16_lo(wds[e]), Zs[32 * s + 8 * g + 2 * e], den);
-      den = fmaf(bf16_hi(wds[e]), Zs[32 * s + 8 * g + 2 * e + 1], den);
-    }
-    phop[s] = __builtin_bit_cast(bf16x8, wds);
-  }
-  // denominator over the unrouted keys: phi(q).Z_tot - sum over routed keys of phi(q).phi(k)
-  den = rows4_sum(den) - a_tot + A.eps;
-  const float inv_den = 1.f / den;
-
-  const float* al = A.alpha + (size_t)hidx * D;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int hr = 16 * dt + l16;
-    const uint8_t* hrow = Hs + hr * 256;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
-      ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), phop[s], ol);
-    }
-    const f32x4 a4 = *reinterpret_cast<const f32x4*>(al + 16 * dt + 4 * g);
-    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-    float ov[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      ov[rr] = av[rr] * (st.acc[dt][rr] * inv_l) + (1.f - av[rr]) * ((ol[rr] - st.accl[dt][rr]) * inv_den);
-    if (qok) {
-      u32x2 sv;
-      sv.x = pack_bf16x2(ov[0], ov[1]);
-      sv.y = pack_bf16x2(ov[2], ov[3]);
-      *reinterpret_cast<u32x2*>(A.o + ((size_t)bh * A.N + qrow) * D + 16 * dt + 4 * g) = sv;
-    }
-  }
-  if (A.lse != nullptr) {
-    // native mode scored the raw keys: log-sum-exp over K~ = K - mu is lower by q.mu/sqrt(d)
-    float shift = 0.f;
-    if constexpr (!FP8) {
+    for (int dt = 0; dt < 8; ++dt) {
+      f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int hr = 16 * dt + l16;
+      const uint8_t* hrow = Hs + hr * 256;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 wv = __builtin_bit_cast(u32x4, qop[s]);
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-        const float* mu = A.k_mean + (size_t)bh * D + 32 * s + 8 * g;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          shift = fmaf(bf16_lo(ww[e]), mu[2 * e], shift);
-          shift = fmaf(bf16_hi(ww[e]), mu[2 * e + 1], shift);
-        }
+        const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
+        ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.phb[qt][s], ol);
       }
-      shift = rows4_sum(shift) * (1.f / sqrtf((float)D));
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(alphaS + 16 * dt + 4 * g);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      float ov[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        ov[rr] = av[rr] * (st.acc[qt][dt][rr] * inv_l) +
+                 (1.f - av[rr]) * (fmaf(-kCodes2, st.accl[qt][dt][rr], ol[rr]) * inv_den);
+      if (qok[qt]) {
+        u32x2 sv;
+        sv.x = pack_bf16x2(ov[0], ov[1]);
+        sv.y = pack_bf16x2(ov[2], ov[3]);
+        *reinterpret_cast<u32x2*>(A.o + ((size_t)bh * A.N + qrow[qt]) * D + 16 * dt + 4 * g) = sv;
+      }
     }
-    if (g == 0 && qok) A.lse[(size_t)bh * A.N + qrow] = (st.m_run + log2f(l_tot)) * kLn2 - shift;
+    if (A.lse != nullptr) {
+      // native mode scored the raw keys: log-sum-exp over K~ = K - mu is lower by q.mu/sqrt(d)
+      float shift = 0.f;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 wv = __builtin_bit_cast(u32x4, qo.qb[qt][s]);
+          const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+          const float* mu = A.k_mean + (size_t)bh * D + 32 * s + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            shift = fmaf(bf16_lo(ww[e]), mu[2 * e], shift);
+            shift = fmaf(bf16_hi(ww[e]), mu[2 * e + 1], shift);
+          }
+        }
+        shift = rows4_sum(shift) * (1.f / sqrtf((float)D));
+      }
+      if (g == 0 && qok[qt]) A.lse[(size_t)bh * A.N + qrow[qt]] = (st.m_run[qt] + log2f(l_tot)) * kLn2 - shift;
+    }
   }
 }
 
@@ -682,9 +717,8 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.k_scale = t.k_scale;
     A.vt = ws.vt;
     A.phik8 = ws.phik8;
-    A.phik_scale = ws.phik_scale;
     A.lut = t.lut;
-    A.h_sum = t.h_sum;
+    A.hbf = ws.hbf;
     A.z_sum = t.z_sum;
     A.alpha = t.alpha;
     A.k_mean = t.k_mean;
@@ -697,12 +731,14 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.nblocks = g.BH * g.T;
     A.eps = g.eps;
     const bool lds_lut = g.topk <= kLutCache;
+    // FP8: two query tiles per wave, two waves per workgroup; native bf16 Q.K: one tile per
+    // wave, four waves (its 16 KB key tiles leave no LDS for a second tile set).
     if (g.fp8) {
-      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<true, true>), dim3(A.nblocks), dim3(256), 0, s, A);
-      else hipLaunchKernelGGL((fwd_mfma_kernel<true, false>), dim3(A.nblocks), dim3(256), 0, s, A);
+      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
+      else hipLaunchKernelGGL((fwd_mfma_kernel<true, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
     } else {
-      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<false, true>), dim3(A.nblocks), dim3(256), 0, s, A);
-      else hipLaunchKernelGGL((fwd_mfma_kernel<false, false>), dim3(A.nblocks), dim3(256), 0, s, A);
+      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<false, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
+      else hipLaunchKernelGGL((fwd_mfma_kernel<false, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
     }
   } else {
     dim3 grid(g.T, g.BH);

@@ -28,8 +28,10 @@ struct Workspace {
   float* hpart;    // [BH, P, D, D] chunk partials of h_sum (transposed like h)
   float* zpart;    // [BH, P, D]
   uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted
-  uint8_t* phik8;  // bf16 modes: [BH, T*64, D] e4m3 codes of phi(K~) / phik_scale (pad rows 0)
-  float* phik_scale;  // bf16 modes: [BH, T] max of phi(K~) over the block / 448 (1 if 0)
+  uint8_t* phik8;  // bf16 modes: [BH, T*64, D] e4m3 codes of 448 phi(K~) (pad rows 0); in each
+                   // row, byte 32g + 8s + e holds feature 32s + 8g + e (g, s < 4, e < 8)
+  uint16_t* hbf;   // bf16 modes: [BH, D, D] h_sum (rows c, columns a) in bf16, 16-byte chunk k of
+                   // row c stored at chunk k ^ (c % 16): the LDS image the forward epilogue uses
 };
 
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);

@@ -5,8 +5,9 @@
 // plus h_sum = sum_j h_j and z_sum = sum_j z_j (chunk partials, then a fixed-order sum).
 // In FP8 mode the same pass quantises K~ per 64-token block (absmax/448 scale, e4m3 codes).
 // The bf16 pass also writes, for the fused forward kernel, each block's V transposed (with
-// the key order of its matrix-core operands) and the e4m3 codes of phi(K~) with one
-// max/448 scale per block; h_j and z_j themselves are stored only if asked for.
+// the key order of its matrix-core operands) and the e4m3 codes of 448 phi(K~) (phi <= 1, so
+// one fixed scale serves every block; features permuted to the forward kernel's operand
+// order); h_j and z_j themselves are stored only if asked for.
 //
 // Pages: "SLA: Beyond Sparsity in Diffusion Transformers...", section 2 Q2 step 3 and the
 // section 3 figure (h_j = phi(K_j)^T V_j, z_j = rowsum(phi(K_j)^T), phi = softmax), section 4
@@ -30,23 +31,20 @@ namespace sla2 {
 // D[a][c] = sum_t phi[t][a] V[t][c] with v_mfma_f32_16x16x32_bf16 over 64 tokens.  phi is
 // split into bf16 hi + lo parts (phi - hi rounded again), so the product carries phi to about
 // 2^-16 relative although the matrix cores take bf16; V is bf16 already.
-// The largest phi of a block is max over its rows of 1 / (sum of exp), since the row maximum
-// has exp(0) = 1; it is reduced together with |K~| before the codes are written.
 // ---------------------------------------------------------------------------------------
 template <bool FP8, bool STORE>
 __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
     int N, int T, int P, uint8_t* __restrict__ k8, float* __restrict__ k_scale,
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
-    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8,
-    float* __restrict__ phik_scale) {
+    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8) {
   constexpr int D = 128;
   constexpr int SW = 65;  // LDS row stride in 32-bit words
   __shared__ uint32_t phiS[64 * SW];
   __shared__ uint32_t phiLoS[64 * SW];
   __shared__ uint32_t vS[64 * SW];
   __shared__ float zred[16 * D];
-  __shared__ float wred[2][4];
+  __shared__ float wred[4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -92,7 +90,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     // ---- phase 1: K~, exp, row sums; V and phi (hi/lo) to LDS; z partials; block maxima
     float kt[4][8];
     bool valid[4];
-    float amax = 0.f, pmax = 0.f;
+    float amax = 0.f;
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
@@ -116,7 +114,6 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       }
       sm = row16_sum(sm);
       const float inv = valid[p] ? 1.f / sm : 0.f;
-      pmax = fmaxf(pmax, inv);                 // largest phi of this row
       uint32_t pw[4], pl[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -140,18 +137,14 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
     amax = wave_max(amax);
-    pmax = wave_max(pmax);
-    if (lane == 0) {
-      wred[0][w] = amax;
-      wred[1][w] = pmax;
-    }
+    if (lane == 0) wred[w] = amax;
     // next block's K and V stream in while this one finishes
     if (j + 1 < j_hi) load_kv(j + 1, kw, vw);
     __syncthreads();
 
     // ---- phase 2: codes of K~ and phi, z, h tiles, V^T
     if constexpr (FP8) {
-      const float bm = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+      const float bm = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
       float s = __fdiv_rn(bm, kFp8Max);
       if (s == 0.f) s = 1.f;
       if (tid == 0) k_scale[(size_t)bh * T + j] = s;
@@ -167,25 +160,22 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       });
     }
     {
-      const float bm = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
-      float sp = __fdiv_rn(bm, kFp8Max);
-      if (sp == 0.f) sp = 1.f;
-      if (tid == 0) phik_scale[(size_t)bh * T + j] = sp;
-      // phi from its bf16 hi + lo parts in LDS (within 2^-16 of the fp32 value)
+      // phi from its bf16 hi + lo parts in LDS (within 2^-16 of the fp32 value); features
+      // 8c..8c+7 = 32s + 8g' + e with s = c / 4, g' = c % 4 go to bytes 32g' + 8s + e
       static_for<4>([&](auto p) {
         const int r = r0 + 16 * p;
         float y[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t hw = phiS[r * SW + 4 * c + e], lw = phiLoS[r * SW + 4 * c + e];
-          y[2 * e] = clamp_fp8(__fdiv_rn(bf16_lo(hw) + bf16_lo(lw), sp));
-          y[2 * e + 1] = clamp_fp8(__fdiv_rn(bf16_hi(hw) + bf16_hi(lw), sp));
+          y[2 * e] = clamp_fp8((bf16_lo(hw) + bf16_lo(lw)) * kPhiCodeScale);
+          y[2 * e + 1] = clamp_fp8((bf16_hi(hw) + bf16_hi(lw)) * kPhiCodeScale);
         }
         u32x2 codes;
         codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
         codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
         const int row = kBlock * j + r0 + 16 * p;
-        *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
+        *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 32 * (c & 3) + 8 * (c >> 2)) = codes;
       });
     }
     if (tid < D) {
@@ -360,7 +350,8 @@ __global__ __launch_bounds__(256) void precompute_f32_kernel(
 __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restrict__ hpart,
                                                           const float* __restrict__ zpart, int P, int D,
                                                           float* __restrict__ h_sum,
-                                                          float* __restrict__ z_sum) {
+                                                          float* __restrict__ z_sum,
+                                                          uint16_t* __restrict__ hbf) {
   __shared__ f32x4 red[4][64];
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int q = tid & 63, u = tid >> 6;
@@ -376,6 +367,13 @@ __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restric
   if (u == 0 && e0 < DD) {
     const f32x4 sm = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
     *reinterpret_cast<f32x4*>(h_sum + (size_t)bh * DD + e0) = sm;
+    if (hbf != nullptr) {   // D = 128: 8 bf16 per 16-byte chunk, chunk k of row c at k ^ (c % 16)
+      const int c = e0 / D, a = e0 % D;
+      u32x2 w2;
+      w2.x = pack_bf16x2(sm.x, sm.y);
+      w2.y = pack_bf16x2(sm.z, sm.w);
+      *reinterpret_cast<u32x2*>(hbf + (size_t)bh * DD + c * D + 8 * ((a >> 3) ^ (c & 15)) + (a & 7)) = w2;
+    }
   }
   if (blockIdx.x == 0) {
     // z_sum: thread (c, part v) adds partials p = v, v + 256/D, ...; parts combined in order
@@ -397,7 +395,7 @@ template <bool FP8, bool STORE>
 static void launch_precompute_bf16(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
   hipLaunchKernelGGL((precompute_bf16_kernel<FP8, STORE>), dim3(g.P, g.BH), dim3(256), 0, s, (const uint16_t*)t.k,
                      (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale, (uint16_t*)t.h, t.z, ws.hpart,
-                     ws.zpart, ws.vt, ws.phik8, ws.phik_scale);
+                     ws.zpart, ws.vt, ws.phik8);
 }
 
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws,
@@ -423,7 +421,7 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
                        ws.zpart);
   }
   hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 255) / 256, g.BH), dim3(256), 0, s,
-                     ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum);
+                     ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
