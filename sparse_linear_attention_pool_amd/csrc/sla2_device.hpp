@@ -56,6 +56,12 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 __device__ __forceinline__ float clamp_fp8(float y) { return fminf(fmaxf(y, -kFp8Max), kFp8Max); }
 
+// fl32(x / s) for the block quantisers, given inv_s = fl64(1 / s): fl32(fl64(x * inv_s)).  The
+// fp64 product is within 2^-52 (relative) of x / s, while a quotient of two fp32 values is
+// never an fp32 rounding midpoint and lies more than 2^-49 (relative) from every one, so
+// rounding the product to fp32 gives the correctly rounded quotient.
+__device__ __forceinline__ float div_by_scale(float x, double inv_s) { return (float)((double)x * inv_s); }
+
 // ---------------------------------------------------------------- matrix cores
 // D(16x16) += A(16x32) * B(32x16), bf16 in, fp32 accumulate.  Lane l holds A[l%16][8(l/16)+e]
 // and B[8(l/16)+e][l%16] (e = 0..7); D[4(l/16)+r][l%16] in accumulator r.

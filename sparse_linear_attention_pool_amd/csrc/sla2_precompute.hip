@@ -148,10 +148,11 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       float s = __fdiv_rn(bm, kFp8Max);
       if (s == 0.f) s = 1.f;
       if (tid == 0) k_scale[(size_t)bh * T + j] = s;
+      const double inv_s = 1.0 / (double)s;
       static_for<4>([&](auto p) {
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(kt[p][e], s));
+        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(div_by_scale(kt[p][e], inv_s));
         u32x2 codes;
         codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
         codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
   constexpr int RPP = 256 / CPR;         // rows per pass
   constexpr int PASSES = kBlock / RPP;
   static_assert(!FP8 || VEC == 8, "FP8 quantisation needs bf16 input");
-  __shared__ double red[RPP * D];
+  __shared__ double red[2][RPP * CPR * (VEC + 1)];
   __shared__ float wmax[4];
 
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -79,24 +79,23 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // column sums: per-thread partials -> LDS -> one thread per column
+  // column sums: per-thread partials -> LDS (row stride padded to VEC + 1 per chunk, so the
+  // 8-byte writes of a 16-lane row hit distinct banks) -> one thread per column, fixed order
+  constexpr int RS = CPR * (VEC + 1);
   const size_t out = ((size_t)bh * T + i) * D;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[r0 * D + c * VEC + e] = qs[e];
-  __syncthreads();
-  if (tid < D) {
-    double s = 0.0;
-    for (int r = 0; r < RPP; ++r) s += red[r * D + tid];
-    qsum[out + tid] = s;
+  for (int e = 0; e < VEC; ++e) {
+    red[0][r0 * RS + c * (VEC + 1) + e] = qs[e];
+    red[1][r0 * RS + c * (VEC + 1) + e] = ks[e];
   }
   __syncthreads();
+  if (tid < 2 * D) {
+    const int which = tid / D, col = tid % D;
+    const double* rd = red[which] + (col / VEC) * (VEC + 1) + col % VEC;
+    double sm = 0.0;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[r0 * D + c * VEC + e] = ks[e];
-  __syncthreads();
-  if (tid < D) {
-    double s = 0.0;
-    for (int r = 0; r < RPP; ++r) s += red[r * D + tid];
-    ksum[out + tid] = s;
+    for (int r = 0; r < RPP; ++r) sm += rd[r * RS];
+    (which ? ksum : qsum)[out + col] = sm;
   }
 
   if constexpr (FP8) {
@@ -107,12 +106,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
     float s = __fdiv_rn(bm, kFp8Max);
     if (s == 0.f) s = 1.f;
     if (tid == 0) q_scale[(size_t)bh * T + i] = s;
+    const double inv_s = 1.0 / (double)s;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = kBlock * i + r0 + p * RPP;
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(__fdiv_rn(qv[p][e], s));
+      for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(div_by_scale(qv[p][e], inv_s));
       uint2 codes;
       codes.x = pack_fp8x4(y[0], y[1], y[2], y[3]);
       codes.y = pack_fp8x4(y[4], y[5], y[6], y[7]);
@@ -455,8 +455,7 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
 
 hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
   if (g.bf16) {
-    if (g.D == 128) launch_route_typed<uint16_t, 128>(g, t, ws, s);
-    else launch_route_typed<uint16_t, 64>(g, t, ws, s);
+    launch_route_typed<uint16_t, 128>(g, t, ws, s);   // bf16 inputs have d = 128
   } else {
     if (g.D == 128) launch_route_typed<float, 128>(g, t, ws, s);
     else launch_route_typed<float, 64>(g, t, ws, s);
