@@ -81,6 +81,8 @@ size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
   w.zpart = (float*)take(BH * P * D * sizeof(float));
   w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * sizeof(uint16_t) : 0);
   w.phik8 = (uint8_t*)take(g.bf16 ? BH * T * 64 * D : 0);
+  w.zblk = (float*)take(g.bf16 ? BH * T * D * sizeof(float) : 0);
+  w.zrout = (float*)take(g.bf16 ? BH * T * D * sizeof(float) : 0);
   w.hbf = (uint16_t*)take(g.bf16 ? BH * D * D * sizeof(uint16_t) : 0);
   if (ws) *ws = w;
   return off;

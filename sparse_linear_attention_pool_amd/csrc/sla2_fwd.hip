@@ -31,6 +31,7 @@ struct FwdArgs {
   const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of 448 phi(K~), features permuted
   const int32_t* lut;     // [BH, T, topk]
   const uint16_t* hbf;    // [BH, D, D] bf16 LDS image of H^T = h_sum (see Workspace::hbf)
+  const float* zrout;     // [BH, T, D] Z_R(i): sum of z_j over the routed blocks of row i
   const float* z_sum;     // [BH, D]
   const float* alpha;     // [H, D]
   const float* k_mean;    // [BH, D] (lse of the native mode is shifted to the smoothed keys)
@@ -80,19 +81,32 @@ struct TileRegs {
 
 // Thread tid moves the 16-byte chunks q = tid + NT p: K row q / (chunks per row), logical
 // chunk q % (chunks per row); phi(K~) codes row q / 8, chunk q % 8; V^T row q / 8, chunk q % 8.
+// Buffer resources over one head's K8, phi(K~) code and V^T tiles: a tile load is then a fixed
+// per-lane offset plus the wave-uniform tile offset, with no per-load address arithmetic.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t k8, phik8, vt;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
+  constexpr int D = 128;
+  const size_t head = (size_t)bh * A.T * kBlock * D;   // elements of one head's tiles
+  const int bytes8 = A.T * kBlock * D;                 // <= 4096 * 8 KB
+  TileSrc s;
+  s.k8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.k8 != nullptr ? A.k8 + head : A.phik8), 0, bytes8, 0x00020000);
+  s.phik8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.phik8 + head), 0, bytes8, 0x00020000);
+  s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
+  return s;
+}
+
 template <bool FP8, int NT>
-__device__ __forceinline__ void load_tile(const FwdArgs& A, int bh, int j, int tid, TileRegs<FP8, NT>& t) {
+__device__ __forceinline__ void load_tile(const FwdArgs& A, const TileSrc& src, int bh, int j, int tid,
+                                          TileRegs<FP8, NT>& t) {
   using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
-  // j is wave-uniform: one scalar base per tile part plus a fixed 32-bit offset per lane
-  const size_t blk = (size_t)bh * A.T + j;
-  const uint8_t* kbase = FP8 ? A.k8 + blk * (kBlock * D) : nullptr;
-  const uint8_t* pbase = A.phik8 + blk * (kBlock * D);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(A.vt + blk * (D * kBlock));
   static_for<L::KLOADS>([&](auto P) {
     const int qd = tid + NT * P;
     if constexpr (FP8) {
-      t.kk[P] = *reinterpret_cast<const u32x4*>(kbase + (uint32_t)(16 * qd));
+      t.kk[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.k8, 16 * qd, j * (kBlock * D), 0));
     } else {
       const int row = qd >> 4, lc = qd & 15;
       const int tok = min(kBlock * j + row, A.N - 1);   // rows past N: any finite row, masked later
@@ -100,10 +114,12 @@ __device__ __forceinline__ void load_tile(const FwdArgs& A, int bh, int j, int t
     }
   });
   static_for<L::PLOADS>([&](auto P) {
-    t.pp[P] = *reinterpret_cast<const u32x4*>(pbase + (uint32_t)(16 * (tid + NT * P)));
+    t.pp[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.phik8, 16 * (tid + NT * P),
+                                                                               j * (kBlock * D), 0));
   });
   static_for<L::VLOADS>([&](auto P) {
-    t.vv[P] = *reinterpret_cast<const u32x4*>(vbase + (uint32_t)(16 * (tid + NT * P)));
+    t.vv[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.vt, 16 * (tid + NT * P),
+                                                                               j * (2 * kBlock * D), 0));
   });
 }
 
@@ -176,7 +192,6 @@ struct FwdState {
   f32x4 accl[QT][8];     // sum over routed keys of (phi(q).phi(k_s)) V_s, same layout
   float m_run[QT];       // running max (log2 units)
   float l_run[QT];       // this lane's partial sum of p
-  float a_run[QT];       // this lane's partial sum of phi(q).phi(k_s) over routed keys
 };
 
 // Operands of this lane's queries that stay in registers for the whole loop.
@@ -185,9 +200,22 @@ struct QueryOps {
   i32x8 q8[QT];          // FP8: e4m3 codes of features 32g..32g+31 (B of S^T = K Q^T)
   bf16x8 qb[QT][4];      // native: bf16 features 32s + 8g + e
   i32x8 phq8[QT];        // e4m3 codes of 448 phi(q), features 32s + 8g + e in (s, e) order
-  bf16x8 phb[QT][4];     // phi(q) in bf16, features 32s + 8g + e (B of O_l^T = H^T phi(Q)^T)
-  float dz[QT];          // phi(q).Z_tot over all 128 features (bf16 phi(q))
+  bf16x8 phb[QT][4];     // phi(q) in bf16, same features (B of O_l^T = H^T phi(q)^T)
 };
+
+// The tile of LUT entry k (k < topk), or the epilogue's H^T image for k = topk, into t.
+template <bool FP8, bool LUT_LDS, int NT>
+__device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, const int* lutS, const int32_t* lutG,
+                                          int k, int topk, int bh, int tid, TileRegs<FP8, NT>& t) {
+  if (k < topk) {
+    int j;
+    if constexpr (LUT_LDS) j = lutS[k];
+    else j = lutG[k];
+    load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(j), tid, t);
+  } else if (k == topk) {
+    load_himage<FP8, NT>(A, bh, tid, t);
+  }
+}
 
 // One routed block, the r-th LUT entry, whose tile is in LDS stage r % 2.  t holds the tile
 // of block r+1 (loaded one iteration earlier); at the end it goes to the other stage and t is
@@ -197,7 +225,7 @@ template <bool FP8, bool LUT_LDS, int QT>
 __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, const int* lutS,
                                               const float* kscS, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
-                                              float cq, bool mask, TileRegs<FP8, 256 / QT>& t) {
+                                              float cq, bool mask, const TileSrc& src, TileRegs<FP8, 256 / QT>& t) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT>;
   // the LUT row comes from the LDS cache, or from global memory when it is longer than the
@@ -298,7 +326,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   // keys 32s + 16h + 4g + rr, as the bf16 B operands of the products below
   bf16x8 pop[QT][2], aop[QT][2];
   auto make_ops = [&](int qt, int s) {
-    float pv[8], av[8], psum = 0.f, asum = 0.f;
+    float pv[8], av[8], psum = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -306,7 +334,6 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
         pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][2 * s + h][rr], cj, -st.m_run[qt]));
         av[4 * h + rr] = Ph[qt][2 * s + h][rr];
         psum += pv[4 * h + rr];
-        asum += av[4 * h + rr];
       }
     const uint32_t pw[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                             pack_bf16x2(pv[6], pv[7])};
@@ -315,7 +342,6 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     pop[qt][s] = __builtin_bit_cast(bf16x8, pw);
     aop[qt][s] = __builtin_bit_cast(bf16x8, aw);
     st.l_run[qt] += psum;
-    st.a_run[qt] += asum;
   };
 
 #pragma unroll
@@ -351,68 +377,59 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   });
 
   // ---- the tile of block r+1 goes to the other stage (its previous tile, block r-1, was
-  // consumed before the last barrier); t is refilled with the tile of block r+2
+  // consumed before the last barrier); t is refilled with the tile of block r+2 (or, once the
+  // LUT is exhausted, the epilogue's H^T image)
   if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, tid, t);
-  if (r + 2 < topk) load_tile<FP8, NT>(A, bh, __builtin_amdgcn_readfirstlane(lut_at(r + 2)), tid, t);
-  else if (r + 2 == topk) load_himage<FP8, NT>(A, bh, tid, t);   // the epilogue's H^T, in flight early
+  load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, r + 2, topk, bh, tid, t);
   lds_barrier();
 }
 
-// phi(q) = softmax over the 128 features of query row q (bf16 input).  This lane holds the
-// features 32s + 8g + e (s < 4, e < 8), in two operand forms:
-//  * e4m3 codes of 448 phi, in (s, e) order: the B operand of Ph^T = phi(K) phi(q)^T, whose
-//    phi(K) codes are stored with the same feature permutation;
-//  * bf16 values (B of O_l^T = H^T phi(q)^T), and their dot product with Z_tot.
-__device__ __forceinline__ void phi_q_ops(const uint16_t* qrow, const float* zsum, bool qok, int g, i32x8& codes,
-                                          bf16x8 (&phb)[4], float& dz) {
-  float y[4][8];
+// phi(q) = softmax over the 128 features of query row q (bf16 input): this lane's features
+// 32s + 8g + e (s < 4, e < 8), f[s][e].
+__device__ __forceinline__ void phi_q_values(const uint16_t* qrow, bool qok, int g, float (&f)[4][8]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const u32x4 u = qok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      y[s][2 * e] = bf16_lo(uw[e]);
-      y[s][2 * e + 1] = bf16_hi(uw[e]);
+      f[s][2 * e] = bf16_lo(uw[e]);
+      f[s][2 * e + 1] = bf16_hi(uw[e]);
     }
   }
-  float mx = y[0][0];
+  float mx = f[0][0];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, y[s][e]);
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, f[s][e]);
   mx = rows4_max(mx);
   float sm = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      y[s][e] = __builtin_amdgcn_exp2f((y[s][e] - mx) * kLog2e);
-      sm += y[s][e];
+      f[s][e] = __builtin_amdgcn_exp2f((f[s][e] - mx) * kLog2e);
+      sm += f[s][e];
     }
   const float rs = 1.f / rows4_sum(sm);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[s][e] *= rs;
+}
+
+// e4m3 codes of 448 phi(q) in (s, e) order: the B operand of Ph^T = phi(K) phi(q)^T, whose
+// phi(K) codes are stored with the same feature permutation.
+__device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
   uint32_t wds[8];
-  float d = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = y[s][e] * rs;
-    wds[2 * s] = pack_fp8x4(clamp_fp8(f[0] * kPhiCodeScale), clamp_fp8(f[1] * kPhiCodeScale),
-                            clamp_fp8(f[2] * kPhiCodeScale), clamp_fp8(f[3] * kPhiCodeScale));
-    wds[2 * s + 1] = pack_fp8x4(clamp_fp8(f[4] * kPhiCodeScale), clamp_fp8(f[5] * kPhiCodeScale),
-                                clamp_fp8(f[6] * kPhiCodeScale), clamp_fp8(f[7] * kPhiCodeScale));
-    uint32_t bw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-      d = fmaf(bf16_lo(bw[e]), zsum[32 * s + 8 * g + 2 * e], d);
-      d = fmaf(bf16_hi(bw[e]), zsum[32 * s + 8 * g + 2 * e + 1], d);
-    }
-    phb[s] = __builtin_bit_cast(bf16x8, bw);
+    wds[2 * s] = pack_fp8x4(clamp_fp8(f[s][0] * kPhiCodeScale), clamp_fp8(f[s][1] * kPhiCodeScale),
+                            clamp_fp8(f[s][2] * kPhiCodeScale), clamp_fp8(f[s][3] * kPhiCodeScale));
+    wds[2 * s + 1] = pack_fp8x4(clamp_fp8(f[s][4] * kPhiCodeScale), clamp_fp8(f[s][5] * kPhiCodeScale),
+                                clamp_fp8(f[s][6] * kPhiCodeScale), clamp_fp8(f[s][7] * kPhiCodeScale));
   }
-  codes = i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3], (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
-  dz = rows4_sum(d);
+  return i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3], (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
 }
 
 // One workgroup of 4/QT waves per (head, query block).  Wave w owns queries
@@ -450,6 +467,12 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   const int32_t* lutG = A.lut + ((size_t)bh * A.T + i) * A.topk;
   const int topk = A.topk;
 
+  // the first routed block straight from the LUT in memory, so its tile load starts at once
+  TileRegs<FP8, NT> t;
+  const TileSrc src = tile_src(A, bh);
+  load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(lutG[0]), tid, t);
+  const float zr = tid < D ? A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
+
   if constexpr (LUT_LDS) {
     for (int x = tid; x < topk; x += NT) {
       const int j = lutG[x];
@@ -465,10 +488,6 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   };
   // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
   const bool last_partial = (lut0(topk - 1) == A.T - 1) && (A.N % kBlock != 0);
-
-  // prologue: tile of block 0 -> registers (-> LDS stage 0 below), then tile of block 1
-  TileRegs<FP8, NT> t;
-  load_tile<FP8, NT>(A, bh, lut0(0), tid, t);
 
   QueryOps<QT> qo;
   float cq = kLog2e / sqrtf((float)D);
@@ -488,8 +507,16 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
         qo.qb[qt][s] = __builtin_bit_cast(bf16x8, a);
       }
     }
-    phi_q_ops(A.q + ((size_t)bh * A.N + qrow[qt]) * D, A.z_sum + (size_t)bh * D, qok[qt], g, qo.phq8[qt],
-              qo.phb[qt], qo.dz[qt]);
+    float f[4][8];
+    phi_q_values(A.q + ((size_t)bh * A.N + qrow[qt]) * D, qok[qt], g, f);
+    qo.phq8[qt] = phi_q_codes(f);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t bw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bw[e] = pack_bf16x2(f[s][2 * e], f[s][2 * e + 1]);
+      qo.phb[qt][s] = __builtin_bit_cast(bf16x8, bw);
+    }
   }
 
   FwdState<QT> st;
@@ -502,32 +529,46 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     }
     st.m_run[qt] = -INFINITY;
     st.l_run[qt] = 0.f;
-    st.a_run[qt] = 0.f;
   }
 
   store_tile<FP8, NT>(smem, tid, t);
-  if (topk > 1) load_tile<FP8, NT>(A, bh, lut0(1), tid, t);
-  else load_himage<FP8, NT>(A, bh, tid, t);
+  load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, 1, topk, bh, tid, t);
   lds_barrier();
 
   for (int r = 0; r < topk; ++r)
     fwd_iteration<FP8, LUT_LDS, QT>(A, st, smem, lutS, kscS, lutG, r, topk, bh, l16, g, tid, qo, cq,
-                                    last_partial && r == topk - 1, t);
+                                    last_partial && r == topk - 1, src, t);
 
   // ---------------- epilogue ----------------
   // H^T (bf16 image loaded during the last iterations) into the free staging buffers; every
   // wave needs all of it.
   uint8_t* Hs = smem;
+  __shared__ float zrS[D];
   store_himage<FP8, NT>(Hs, tid, t);
+  if (tid < D) zrS[tid] = zr;
   lds_barrier();
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l_tot = rows4_sum(st.l_run[qt]);
     constexpr float kCodes2 = 1.f / (kPhiCodeScale * kPhiCodeScale);   // undo the code scales
-    const float a_tot = rows4_sum(st.a_run[qt]) * kCodes2;
     const float inv_l = 1.f / l_tot;
-    // denominator over the unrouted keys: phi(q).Z_tot - sum over routed keys of phi(q).phi(k)
-    const float inv_den = 1.f / (qo.dz[qt] - a_tot + A.eps);
+    // denominator over the unrouted blocks: phi(q).(Z_tot - Z_R), with the bf16 phi(q)
+    float den = 0.f;
+    {
+      const float* zt = A.z_sum + (size_t)bh * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 bw = __builtin_bit_cast(u32x4, qo.phb[qt][s]);
+        const uint32_t ww[4] = {bw.x, bw.y, bw.z, bw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int a = 32 * s + 8 * g + 2 * e;
+          den = fmaf(bf16_lo(ww[e]), zt[a] - zrS[a], den);
+          den = fmaf(bf16_hi(ww[e]), zt[a + 1] - zrS[a + 1], den);
+        }
+      }
+    }
+    const float inv_den = 1.f / (rows4_sum(den) + A.eps);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -717,6 +758,7 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.k_scale = t.k_scale;
     A.vt = ws.vt;
     A.phik8 = ws.phik8;
+    A.zrout = ws.zrout;
     A.lut = t.lut;
     A.hbf = ws.hbf;
     A.z_sum = t.z_sum;

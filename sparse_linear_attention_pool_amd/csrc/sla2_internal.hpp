@@ -30,6 +30,8 @@ struct Workspace {
   uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted
   uint8_t* phik8;  // bf16 modes: [BH, T*64, D] e4m3 codes of 448 phi(K~) (pad rows 0); in each
                    // row, byte 32g + 8s + e holds feature 32s + 8g + e (g, s < 4, e < 8)
+  float* zblk;     // bf16 modes: [BH, T, D] z_j of every key block
+  float* zrout;    // bf16 modes: [BH, T, D] Z_R(i) = sum of z_j over the routed blocks of row i
   uint16_t* hbf;   // bf16 modes: [BH, D, D] h_sum (rows c, columns a) in bf16, 16-byte chunk k of
                    // row c stored at chunk k ^ (c % 16): the LDS image the forward epilogue uses
 };

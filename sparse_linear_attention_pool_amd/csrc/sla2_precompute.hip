@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
     int N, int T, int P, uint8_t* __restrict__ k8, float* __restrict__ k_scale,
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
-    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8) {
+    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8, float* __restrict__ zblk) {
   constexpr int D = 128;
   constexpr int SW = 65;  // LDS row stride in 32-bit words
   __shared__ uint32_t phiS[64 * SW];
@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sz += zred[r * D + tid];
       if constexpr (STORE) z[((size_t)bh * T + j) * D + tid] = sz;
+      zblk[((size_t)bh * T + j) * D + tid] = sz;
       zs += sz;
     }
 
@@ -392,11 +393,24 @@ __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restric
   }
 }
 
+// Z_R(i) = sum of z_j over the routed blocks j of query-block row i, in LUT order: one
+// workgroup per (row, head), thread c owns feature c.  The forward pass needs it for the
+// denominator of the linear branch over the unrouted blocks, phi(q).(Z_tot - Z_R).
+__global__ __launch_bounds__(128) void zroute_kernel(const float* __restrict__ zblk, const int32_t* __restrict__ lut,
+                                                     int T, int topk, float* __restrict__ zrout) {
+  const int i = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+  const int32_t* row = lut + ((size_t)bh * T + i) * topk;
+  float s = 0.f;
+#pragma unroll 8
+  for (int x = 0; x < topk; ++x) s += zblk[((size_t)bh * T + row[x]) * 128 + c];
+  zrout[((size_t)bh * T + i) * 128 + c] = s;
+}
+
 template <bool FP8, bool STORE>
 static void launch_precompute_bf16(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
   hipLaunchKernelGGL((precompute_bf16_kernel<FP8, STORE>), dim3(g.P, g.BH), dim3(256), 0, s, (const uint16_t*)t.k,
                      (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale, (uint16_t*)t.h, t.z, ws.hpart,
-                     ws.zpart, ws.vt, ws.phik8);
+                     ws.zpart, ws.vt, ws.phik8, ws.zblk);
 }
 
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws,
@@ -423,6 +437,7 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
   }
   hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 255) / 256, g.BH), dim3(256), 0, s,
                      ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr);
+  if (g.bf16) hipLaunchKernelGGL(zroute_kernel, dim3(g.T, g.BH), dim3(128), 0, s, ws.zblk, t.lut, g.T, g.topk, ws.zrout);
   return hipGetLastError();
 }
 
