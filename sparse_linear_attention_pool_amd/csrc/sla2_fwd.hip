@@ -77,6 +77,7 @@ struct TileRegs {
   u32x4 kk[FwdLds<FP8, NT>::KLOADS];
   u32x4 pp[FwdLds<FP8, NT>::PLOADS];
   u32x4 vv[FwdLds<FP8, NT>::VLOADS];
+  float ksc;   // FP8: the block's K scale
 };
 
 // Thread tid moves the 16-byte chunks q = tid + NT p: K row q / (chunks per row), logical
@@ -84,7 +85,7 @@ struct TileRegs {
 // Buffer resources over one head's K8, phi(K~) code and V^T tiles: a tile load is then a fixed
 // per-lane offset plus the wave-uniform tile offset, with no per-load address arithmetic.
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t k8, phik8, vt;
+  __amdgpu_buffer_rsrc_t k8, phik8, vt, hbf;
 };
 
 __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
@@ -95,6 +96,7 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   s.k8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.k8 != nullptr ? A.k8 + head : A.phik8), 0, bytes8, 0x00020000);
   s.phik8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.phik8 + head), 0, bytes8, 0x00020000);
   s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
+  s.hbf = __builtin_amdgcn_make_buffer_rsrc((void*)(A.hbf + (size_t)bh * D * D), 0, 2 * D * D, 0x00020000);
   return s;
 }
 
@@ -103,6 +105,8 @@ __device__ __forceinline__ void load_tile(const FwdArgs& A, const TileSrc& src, 
                                           TileRegs<FP8, NT>& t) {
   using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
+  // the scale first: loads complete in issue order, so its wait does not hold up the tile's
+  if constexpr (FP8) t.ksc = A.k_scale[(size_t)bh * A.T + j];
   static_for<L::KLOADS>([&](auto P) {
     const int qd = tid + NT * P;
     if constexpr (FP8) {
@@ -124,8 +128,11 @@ __device__ __forceinline__ void load_tile(const FwdArgs& A, const TileSrc& src, 
 }
 
 template <bool FP8, int NT>
-__device__ __forceinline__ void store_tile(uint8_t* stage, int tid, const TileRegs<FP8, NT>& t) {
+__device__ __forceinline__ void store_tile(uint8_t* stage, float* ksc_slot, int tid, const TileRegs<FP8, NT>& t) {
   using L = FwdLds<FP8, NT>;
+  if constexpr (FP8) {
+    if (tid == 0) *ksc_slot = t.ksc;
+  }
   static_for<L::KLOADS>([&](auto P) {
     const int qd = tid + NT * P;
     if constexpr (FP8) {
@@ -149,13 +156,12 @@ __device__ __forceinline__ void store_tile(uint8_t* stage, int tid, const TileRe
 // The 32 KB bf16 image of H^T (already in its LDS layout) through the tile registers: thread
 // tid moves the 16-byte chunks q = tid + NT p, in order over kk, pp, vv.
 template <bool FP8, int NT>
-__device__ __forceinline__ void load_himage(const FwdArgs& A, int bh, int tid, TileRegs<FP8, NT>& t) {
+__device__ __forceinline__ void load_himage(const TileSrc& src, int tid, TileRegs<FP8, NT>& t) {
   using L = FwdLds<FP8, NT>;
   constexpr int NCH = 2048 / NT;
   static_assert(NCH <= L::KLOADS + L::PLOADS + L::VLOADS, "tile registers too small for the H^T image");
-  const u32x4* src = reinterpret_cast<const u32x4*>(A.hbf + (size_t)bh * 128 * 128);
   static_for<NCH>([&](auto P) {
-    const u32x4 v = src[tid + NT * P];
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.hbf, 16 * tid, 16 * NT * P, 0));
     if constexpr (P < L::KLOADS) t.kk[P] = v;
     else if constexpr (P < L::KLOADS + L::PLOADS) t.pp[P - L::KLOADS] = v;
     else t.vv[P - L::KLOADS - L::PLOADS] = v;
@@ -213,7 +219,7 @@ __device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, 
     else j = lutG[k];
     load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(j), tid, t);
   } else if (k == topk) {
-    load_himage<FP8, NT>(A, bh, tid, t);
+    load_himage<FP8, NT>(src, tid, t);
   }
 }
 
@@ -223,7 +229,7 @@ __device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, 
 // entry can be: LUT rows are ascending and only block T-1 is partial).
 template <bool FP8, bool LUT_LDS, int QT>
 __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, const int* lutS,
-                                              const float* kscS, const int32_t* lutG, int r,
+                                              float* kscS, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
                                               float cq, bool mask, const TileSrc& src, TileRegs<FP8, 256 / QT>& t) {
   constexpr int NT = 256 / QT;
@@ -280,10 +286,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     }
   }
   float cj = cq;
-  if constexpr (FP8) {
-    if constexpr (LUT_LDS) cj = cq * kscS[r];
-    else cj = cq * A.k_scale[(size_t)bh * A.T + j];
-  }
+  if constexpr (FP8) cj = cq * kscS[r & 1];   // stored with the tile
   if (mask) {   // phi codes of keys past N are zero already; only the scores need it
     const int nvalid = min(kBlock, A.N - kBlock * j);
 #pragma unroll
@@ -379,17 +382,20 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   // ---- the tile of block r+1 goes to the other stage (its previous tile, block r-1, was
   // consumed before the last barrier); t is refilled with the tile of block r+2 (or, once the
   // LUT is exhausted, the epilogue's H^T image)
-  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, tid, t);
+  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, kscS + ((r + 1) & 1), tid, t);
   load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, r + 2, topk, bh, tid, t);
   lds_barrier();
 }
 
 // phi(q) = softmax over the 128 features of query row q (bf16 input): this lane's features
 // 32s + 8g + e (s < 4, e < 8), f[s][e].
-__device__ __forceinline__ void phi_q_values(const uint16_t* qrow, bool qok, int g, float (&f)[4][8]) {
+__device__ __forceinline__ void phi_q_values(const uint16_t* qrow, int g, float (&f)[4][8]) {
+  u32x4 uu[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) uu[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const u32x4 u = qok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g) : u32x4{0, 0, 0, 0};
+    const u32x4 u = uu[s];
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -450,44 +456,36 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
   __shared__ int lutS[kLutCache];
-  __shared__ float kscS[kLutCache];
+  __shared__ float kscS[2];   // K scale of the tile in each stage
   __shared__ float alphaS[D];
 
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
-  const int bh = lid / A.T, i = lid % A.T;
+  // uniform indices in scalar registers, so per-block scalars load through the scalar cache
+  const int bh = __builtin_amdgcn_readfirstlane(lid / A.T), i = __builtin_amdgcn_readfirstlane(lid % A.T);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int hidx = bh % A.H;
   int qrow[QT];   // this lane's query tokens
+  int qsrc[QT];   // the token its operands load from: rows past N read row N-1 (never stored)
   bool qok[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     qrow[qt] = kBlock * i + 16 * QT * w + 16 * qt + l16;
     qok[qt] = qrow[qt] < A.N;
+    qsrc[qt] = min(qrow[qt], A.N - 1);
   }
   const int32_t* lutG = A.lut + ((size_t)bh * A.T + i) * A.topk;
   const int topk = A.topk;
 
-  // the first routed block straight from the LUT in memory, so its tile load starts at once
+  // The LUT row for the LDS cache and, straight from memory, its first entry, so that the first
+  // tile load starts at once; the query operands load meanwhile.
+  int lutv[kLutCache / NT];
+#pragma unroll
+  for (int u = 0; u < kLutCache / NT; ++u) lutv[u] = (LUT_LDS && tid + NT * u < topk) ? lutG[tid + NT * u] : 0;
+  static_assert(NT >= D, "one thread per feature for alpha and Z_R");
+  const float alv = tid < D ? A.alpha[(size_t)hidx * D + tid] : 0.f;
   TileRegs<FP8, NT> t;
   const TileSrc src = tile_src(A, bh);
   load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(lutG[0]), tid, t);
-  const float zr = tid < D ? A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
-
-  if constexpr (LUT_LDS) {
-    for (int x = tid; x < topk; x += NT) {
-      const int j = lutG[x];
-      lutS[x] = j;
-      if constexpr (FP8) kscS[x] = A.k_scale[(size_t)bh * A.T + j];
-    }
-  }
-  for (int c = tid; c < D; c += NT) alphaS[c] = A.alpha[(size_t)hidx * D + c];
-  __syncthreads();
-  auto lut0 = [&](int x) {
-    if constexpr (LUT_LDS) return lutS[x];
-    else return lutG[x];
-  };
-  // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
-  const bool last_partial = (lut0(topk - 1) == A.T - 1) && (A.N % kBlock != 0);
 
   QueryOps<QT> qo;
   float cq = kLog2e / sqrtf((float)D);
@@ -495,20 +493,19 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     if constexpr (FP8) {
-      const uint8_t* src = A.q8 + (((size_t)bh * A.T * kBlock) + qrow[qt]) * D + 32 * g;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(src);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(src + 16);
+      const uint8_t* src8 = A.q8 + (((size_t)bh * A.T * kBlock) + qrow[qt]) * D + 32 * g;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(src8);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(src8 + 16);
       qo.q8[qt] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = qok[qt] ? *reinterpret_cast<const u32x4*>(A.q + ((size_t)bh * A.N + qrow[qt]) * D + 32 * s + 8 * g)
-                                : u32x4{0, 0, 0, 0};
+        const u32x4 a = *reinterpret_cast<const u32x4*>(A.q + ((size_t)bh * A.N + qsrc[qt]) * D + 32 * s + 8 * g);
         qo.qb[qt][s] = __builtin_bit_cast(bf16x8, a);
       }
     }
     float f[4][8];
-    phi_q_values(A.q + ((size_t)bh * A.N + qrow[qt]) * D, qok[qt], g, f);
+    phi_q_values(A.q + ((size_t)bh * A.N + qsrc[qt]) * D, g, f);
     qo.phq8[qt] = phi_q_codes(f);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -518,6 +515,21 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
       qo.phb[qt][s] = __builtin_bit_cast(bf16x8, bw);
     }
   }
+  const float zr = tid < D ? A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
+
+  if constexpr (LUT_LDS) {
+#pragma unroll
+    for (int u = 0; u < kLutCache / NT; ++u)
+      if (tid + NT * u < topk) lutS[tid + NT * u] = lutv[u];
+  }
+  if (tid < D) alphaS[tid] = alv;
+  lds_barrier();
+  auto lut0 = [&](int x) {
+    if constexpr (LUT_LDS) return lutS[x];
+    else return lutG[x];
+  };
+  // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
+  const bool last_partial = (lut0(topk - 1) == A.T - 1) && (A.N % kBlock != 0);
 
   FwdState<QT> st;
 #pragma unroll
@@ -531,7 +543,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     st.l_run[qt] = 0.f;
   }
 
-  store_tile<FP8, NT>(smem, tid, t);
+  store_tile<FP8, NT>(smem, kscS, tid, t);
   load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, 1, topk, bh, tid, t);
   lds_barrier();
 
