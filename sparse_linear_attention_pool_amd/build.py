@@ -54,6 +54,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host pass failed leaves its launch stub undefined; catch it here, not at load
+    nm = shutil.which("nm")
+    if nm is not None:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        missing = [ln.split()[-1] for ln in und.splitlines() if "sla2" in ln]
+        if missing:
+            raise RuntimeError(f"link left library symbols undefined: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -189,7 +189,15 @@ __device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g
   return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-constexpr int kLutCache = 512;   // routed blocks whose index and scales are cached in LDS
+constexpr int kLutReg = 64;   // LUT rows up to this long live in one register (lane x holds entry x)
+
+// Entry x of this query block's LUT row: read across lanes from the register copy, or from
+// memory when the row is longer than a wave.
+template <bool LUT_REG>
+__device__ __forceinline__ int lut_entry(int lutv, const int32_t* lutG, int x) {
+  if constexpr (LUT_REG) return __builtin_amdgcn_readlane(lutv, x);
+  else return __builtin_amdgcn_readfirstlane(lutG[x]);
+}
 
 // Per-lane state of the routed-block loop: QT queries per lane (one per 16-query tile).
 template <int QT>
@@ -210,14 +218,11 @@ struct QueryOps {
 };
 
 // The tile of LUT entry k (k < topk), or the epilogue's H^T image for k = topk, into t.
-template <bool FP8, bool LUT_LDS, int NT>
-__device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, const int* lutS, const int32_t* lutG,
+template <bool FP8, bool LUT_REG, int NT>
+__device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, int lutv, const int32_t* lutG,
                                           int k, int topk, int bh, int tid, TileRegs<FP8, NT>& t) {
   if (k < topk) {
-    int j;
-    if constexpr (LUT_LDS) j = lutS[k];
-    else j = lutG[k];
-    load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(j), tid, t);
+    load_tile<FP8, NT>(A, src, bh, lut_entry<LUT_REG>(lutv, lutG, k), tid, t);
   } else if (k == topk) {
     load_himage<FP8, NT>(src, tid, t);
   }
@@ -227,21 +232,22 @@ __device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, 
 // of block r+1 (loaded one iteration earlier); at the end it goes to the other stage and t is
 // refilled with the tile of block r+2.  mask: the block may be partial (only the last LUT
 // entry can be: LUT rows are ascending and only block T-1 is partial).
-template <bool FP8, bool LUT_LDS, int QT>
-__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, const int* lutS,
+template <bool FP8, bool LUT_REG, int QT>
+__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, int lutv,
                                               float* kscS, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
                                               float cq, bool mask, const TileSrc& src, TileRegs<FP8, 256 / QT>& t) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT>;
-  // the LUT row comes from the LDS cache, or from global memory when it is longer than the
-  // cache (a separate instantiation, so no load ever has to serve both address spaces)
-  auto lut_at = [&](int x) {
-    if constexpr (LUT_LDS) return lutS[x];
-    else return lutG[x];
-  };
-  const int j = lut_at(r);
   const uint8_t* stage = smem + (r & 1) * L::STAGE;
+
+  // ---- first, the tile of block r+1 (loaded during the previous iteration) goes to the other
+  // stage, whose previous tile (block r-1) was consumed before the last barrier; t is refilled
+  // with the tile of block r+2 (or, once the LUT is exhausted, the epilogue's H^T image).  The
+  // writes and loads then complete while this block is processed.
+  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, kscS + ((r + 1) & 1), tid, t);
+  load_next<FP8, LUT_REG, NT>(A, src, lutv, lutG, r + 2, topk, bh, tid, t);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- S^T = K_j Q^T and Ph^T = phi(K_j) phi(Q)^T: keys 16mt + 4g + rr x queries l16 of each
   // query tile.  Operand reads run one key tile ahead of the matrix-core products; the
@@ -288,7 +294,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   float cj = cq;
   if constexpr (FP8) cj = cq * kscS[r & 1];   // stored with the tile
   if (mask) {   // phi codes of keys past N are zero already; only the scores need it
-    const int nvalid = min(kBlock, A.N - kBlock * j);
+    const int nvalid = A.N - kBlock * (A.T - 1);   // only block T-1 can be partial
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -379,11 +385,6 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     __builtin_amdgcn_sched_barrier(0);
   });
 
-  // ---- the tile of block r+1 goes to the other stage (its previous tile, block r-1, was
-  // consumed before the last barrier); t is refilled with the tile of block r+2 (or, once the
-  // LUT is exhausted, the epilogue's H^T image)
-  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, kscS + ((r + 1) & 1), tid, t);
-  load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, r + 2, topk, bh, tid, t);
   lds_barrier();
 }
 
@@ -447,15 +448,14 @@ __device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
 // H_i = h_sum - sum over routed j of h_j.  The routed part phi(q) h_j = (phi(q) phi(K_j)^T) V_j
 // is evaluated by re-association over the same routed keys and V^T tiles as the sparse
 // branch, with phi(K~) and phi(q) as e4m3 codes (phi(q) scaled per query).
-// Pipeline per routed block r: compute on the LDS tile of block r, write the tile of block
-// r+1 (loaded one iteration earlier) to the other LDS stage, load the tile of block r+2.
-template <bool FP8, bool LUT_LDS, int QT>
+// Pipeline per routed block r: write the tile of block r+1 (loaded one iteration earlier) to
+// the other LDS stage, load the tile of block r+2, compute on the LDS tile of block r.
+template <bool FP8, bool LUT_REG, int QT>
 __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
-  __shared__ int lutS[kLutCache];
   __shared__ float kscS[2];   // K scale of the tile in each stage
   __shared__ float alphaS[D];
 
@@ -476,11 +476,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   const int32_t* lutG = A.lut + ((size_t)bh * A.T + i) * A.topk;
   const int topk = A.topk;
 
-  // The LUT row for the LDS cache and, straight from memory, its first entry, so that the first
-  // tile load starts at once; the query operands load meanwhile.
-  int lutv[kLutCache / NT];
-#pragma unroll
-  for (int u = 0; u < kLutCache / NT; ++u) lutv[u] = (LUT_LDS && tid + NT * u < topk) ? lutG[tid + NT * u] : 0;
+  // The LUT row into a register (lane x holds entry x) and, straight from memory, its first
+  // entry, so that the first tile load starts at once; the query operands load meanwhile.
+  const int lutv = (LUT_REG && lane < topk) ? lutG[lane] : 0;
   static_assert(NT >= D, "one thread per feature for alpha and Z_R");
   const float alv = tid < D ? A.alpha[(size_t)hidx * D + tid] : 0.f;
   TileRegs<FP8, NT> t;
@@ -517,19 +515,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   }
   const float zr = tid < D ? A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
 
-  if constexpr (LUT_LDS) {
-#pragma unroll
-    for (int u = 0; u < kLutCache / NT; ++u)
-      if (tid + NT * u < topk) lutS[tid + NT * u] = lutv[u];
-  }
-  if (tid < D) alphaS[tid] = alv;
-  lds_barrier();
-  auto lut0 = [&](int x) {
-    if constexpr (LUT_LDS) return lutS[x];
-    else return lutG[x];
-  };
+  if (tid < D) alphaS[tid] = alv;   // read in the epilogue, after several barriers
   // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
-  const bool last_partial = (lut0(topk - 1) == A.T - 1) && (A.N % kBlock != 0);
+  const bool last_partial = (lut_entry<LUT_REG>(lutv, lutG, topk - 1) == A.T - 1) && (A.N % kBlock != 0);
 
   FwdState<QT> st;
 #pragma unroll
@@ -544,11 +532,15 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   }
 
   store_tile<FP8, NT>(smem, kscS, tid, t);
-  load_next<FP8, LUT_LDS, NT>(A, src, lutS, lutG, 1, topk, bh, tid, t);
+  // Complete the query-operand loads here, before the next tile's loads are issued: the wait
+  // for their first use would otherwise sit inside the loop, where the counter cannot tell
+  // them from the prefetches in flight, and would drain every load on each iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only (expcnt and lgkmcnt fields at their maxima)
+  load_next<FP8, LUT_REG, NT>(A, src, lutv, lutG, 1, topk, bh, tid, t);
   lds_barrier();
 
   for (int r = 0; r < topk; ++r)
-    fwd_iteration<FP8, LUT_LDS, QT>(A, st, smem, lutS, kscS, lutG, r, topk, bh, l16, g, tid, qo, cq,
+    fwd_iteration<FP8, LUT_REG, QT>(A, st, smem, lutv, kscS, lutG, r, topk, bh, l16, g, tid, qo, cq,
                                     last_partial && r == topk - 1, src, t);
 
   // ---------------- epilogue ----------------
@@ -784,14 +776,14 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.topk = g.topk;
     A.nblocks = g.BH * g.T;
     A.eps = g.eps;
-    const bool lds_lut = g.topk <= kLutCache;
+    const bool lut_reg = g.topk <= kLutReg;
     // FP8: two query tiles per wave, two waves per workgroup; native bf16 Q.K: one tile per
     // wave, four waves (its 16 KB key tiles leave no LDS for a second tile set).
     if (g.fp8) {
-      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
+      if (lut_reg) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
       else hipLaunchKernelGGL((fwd_mfma_kernel<true, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
     } else {
-      if (lds_lut) hipLaunchKernelGGL((fwd_mfma_kernel<false, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
+      if (lut_reg) hipLaunchKernelGGL((fwd_mfma_kernel<false, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
       else hipLaunchKernelGGL((fwd_mfma_kernel<false, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
     }
   } else {
