@@ -72,20 +72,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // This thread's share of one key block's tiles, in registers.
-template <bool FP8, int NT>
-struct TileRegs {
-  u32x4 kk[FwdLds<FP8, NT>::KLOADS];
-  u32x4 pp[FwdLds<FP8, NT>::PLOADS];
-  u32x4 vv[FwdLds<FP8, NT>::VLOADS];
-  float ksc;   // FP8: the block's K scale
-};
-
-// Thread tid moves the 16-byte chunks q = tid + NT p: K row q / (chunks per row), logical
-// chunk q % (chunks per row); phi(K~) codes row q / 8, chunk q % 8; V^T row q / 8, chunk q % 8.
-// Buffer resources over one head's K8, phi(K~) code and V^T tiles: a tile load is then a fixed
-// per-lane offset plus the wave-uniform tile offset, with no per-load address arithmetic.
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t k8, phik8, vt, hbf;
+  __amdgpu_buffer_rsrc_t k, phik8, vt, hbf;   // k: e4m3 codes of K~ (FP8) or bf16 K (native)
 };
 
 __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
@@ -93,92 +81,59 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   const size_t head = (size_t)bh * A.T * kBlock * D;   // elements of one head's tiles
   const int bytes8 = A.T * kBlock * D;                 // <= 4096 * 8 KB
   TileSrc s;
-  s.k8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.k8 != nullptr ? A.k8 + head : A.phik8), 0, bytes8, 0x00020000);
+  s.k = A.k8 != nullptr ? __builtin_amdgcn_make_buffer_rsrc((void*)(A.k8 + head), 0, bytes8, 0x00020000)
+                        : __builtin_amdgcn_make_buffer_rsrc((void*)(A.k + (size_t)bh * A.N * D), 0, A.N * D * 2, 0x00020000);
   s.phik8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.phik8 + head), 0, bytes8, 0x00020000);
   s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
   s.hbf = __builtin_amdgcn_make_buffer_rsrc((void*)(A.hbf + (size_t)bh * D * D), 0, 2 * D * D, 0x00020000);
   return s;
 }
 
+// Tiles move from memory straight into LDS (buffer loads with the LDS destination): lane l
+// of a wave writes the 16 bytes at its wave's LDS pointer + 16 l, so each thread loads the
+// chunk that belongs at its LDS slot.  The swizzle (chunk c of row r at position c ^ (r & 7),
+// or c ^ (r & 15) for 256-byte rows) is applied to the memory address instead.
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// The tile of key block j (K, phi(K~) codes, V^T) into the LDS stage at `stage`.
 template <bool FP8, int NT>
-__device__ __forceinline__ void load_tile(const FwdArgs& A, const TileSrc& src, int bh, int j, int tid,
-                                          TileRegs<FP8, NT>& t) {
+__device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, int j, int tid, uint8_t* stage) {
   using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
-  // the scale first: loads complete in issue order, so its wait does not hold up the tile's
-  if constexpr (FP8) t.ksc = A.k_scale[(size_t)bh * A.T + j];
+  const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 1 KB of each group
   static_for<L::KLOADS>([&](auto P) {
     const int qd = tid + NT * P;
+    uint8_t* dst = stage + 16 * NT * P + wofs;
     if constexpr (FP8) {
-      t.kk[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.k8, 16 * qd, j * (kBlock * D), 0));
+      const int row = qd >> 3, pc = qd & 7;
+      lds_dma(src.k, dst, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
     } else {
-      const int row = qd >> 4, lc = qd & 15;
+      const int row = qd >> 4, pc = qd & 15;
       const int tok = min(kBlock * j + row, A.N - 1);   // rows past N: any finite row, masked later
-      t.kk[P] = *reinterpret_cast<const u32x4*>(A.k + ((size_t)bh * A.N + tok) * D + 8 * lc);
+      lds_dma(src.k, dst, tok * (2 * D) + 16 * (pc ^ (row & 15)), 0);
     }
   });
   static_for<L::PLOADS>([&](auto P) {
-    t.pp[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.phik8, 16 * (tid + NT * P),
-                                                                               j * (kBlock * D), 0));
+    const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
+    lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
   });
   static_for<L::VLOADS>([&](auto P) {
-    t.vv[P] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.vt, 16 * (tid + NT * P),
-                                                                               j * (2 * kBlock * D), 0));
+    const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
+    lds_dma(src.vt, stage + L::VOFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (2 * kBlock * D));
   });
 }
 
-template <bool FP8, int NT>
-__device__ __forceinline__ void store_tile(uint8_t* stage, float* ksc_slot, int tid, const TileRegs<FP8, NT>& t) {
-  using L = FwdLds<FP8, NT>;
-  if constexpr (FP8) {
-    if (tid == 0) *ksc_slot = t.ksc;
-  }
-  static_for<L::KLOADS>([&](auto P) {
-    const int qd = tid + NT * P;
-    if constexpr (FP8) {
-      const int row = qd >> 3, lc = qd & 7;
-      *reinterpret_cast<u32x4*>(stage + row * L::KROW + 16 * (lc ^ (row & 7))) = t.kk[P];
-    } else {
-      const int row = qd >> 4, lc = qd & 15;
-      *reinterpret_cast<u32x4*>(stage + row * L::KROW + 16 * (lc ^ (row & 15))) = t.kk[P];
-    }
-  });
-  static_for<L::PLOADS>([&](auto P) {
-    const int qd = tid + NT * P, row = qd >> 3, lc = qd & 7;
-    *reinterpret_cast<u32x4*>(stage + L::POFF + row * 128 + 16 * (lc ^ (row & 7))) = t.pp[P];
-  });
-  static_for<L::VLOADS>([&](auto P) {
-    const int qd = tid + NT * P, row = qd >> 3, lc = qd & 7;
-    *reinterpret_cast<u32x4*>(stage + L::VOFF + row * 128 + 16 * (lc ^ (row & 7))) = t.vv[P];
-  });
+// The 32 KB bf16 image of H^T, stored in memory already in its LDS layout, into `dst`.
+template <int NT>
+__device__ __forceinline__ void dma_himage(const TileSrc& src, int tid, uint8_t* dst) {
+  const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_for<2048 / NT>([&](auto P) { lds_dma(src.hbf, dst + 16 * NT * P + wofs, 16 * (tid + NT * P), 0); });
 }
 
-// The 32 KB bf16 image of H^T (already in its LDS layout) through the tile registers: thread
-// tid moves the 16-byte chunks q = tid + NT p, in order over kk, pp, vv.
-template <bool FP8, int NT>
-__device__ __forceinline__ void load_himage(const TileSrc& src, int tid, TileRegs<FP8, NT>& t) {
-  using L = FwdLds<FP8, NT>;
-  constexpr int NCH = 2048 / NT;
-  static_assert(NCH <= L::KLOADS + L::PLOADS + L::VLOADS, "tile registers too small for the H^T image");
-  static_for<NCH>([&](auto P) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.hbf, 16 * tid, 16 * NT * P, 0));
-    if constexpr (P < L::KLOADS) t.kk[P] = v;
-    else if constexpr (P < L::KLOADS + L::PLOADS) t.pp[P - L::KLOADS] = v;
-    else t.vv[P - L::KLOADS - L::PLOADS] = v;
-  });
-}
-
-template <bool FP8, int NT>
-__device__ __forceinline__ void store_himage(uint8_t* dst, int tid, const TileRegs<FP8, NT>& t) {
-  using L = FwdLds<FP8, NT>;
-  constexpr int NCH = 2048 / NT;
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
-  static_for<NCH>([&](auto P) {
-    if constexpr (P < L::KLOADS) d[tid + NT * P] = t.kk[P];
-    else if constexpr (P < L::KLOADS + L::PLOADS) d[tid + NT * P] = t.pp[P - L::KLOADS];
-    else d[tid + NT * P] = t.vv[P - L::KLOADS - L::PLOADS];
-  });
-}
+// All of this wave's tile copies have landed in LDS (they count as vector-memory loads).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
 
 // 32 e4m3 codes of one 128-byte LDS row (logical chunks 2g and 2g+1): the A operand of a
 // 16x16x128 matrix-core product for row `row`.
@@ -217,36 +172,32 @@ struct QueryOps {
   bf16x8 phb[QT][4];     // phi(q) in bf16, same features (B of O_l^T = H^T phi(q)^T)
 };
 
-// The tile of LUT entry k (k < topk), or the epilogue's H^T image for k = topk, into t.
-template <bool FP8, bool LUT_REG, int NT>
-__device__ __forceinline__ void load_next(const FwdArgs& A, const TileSrc& src, int lutv, const int32_t* lutG,
-                                          int k, int topk, int bh, int tid, TileRegs<FP8, NT>& t) {
-  if (k < topk) {
-    load_tile<FP8, NT>(A, src, bh, lut_entry<LUT_REG>(lutv, lutG, k), tid, t);
-  } else if (k == topk) {
-    load_himage<FP8, NT>(src, tid, t);
-  }
-}
-
-// One routed block, the r-th LUT entry, whose tile is in LDS stage r % 2.  t holds the tile
-// of block r+1 (loaded one iteration earlier); at the end it goes to the other stage and t is
-// refilled with the tile of block r+2.  mask: the block may be partial (only the last LUT
-// entry can be: LUT rows are ascending and only block T-1 is partial).
-template <bool FP8, bool LUT_REG, int QT>
-__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem, int lutv,
-                                              float* kscS, const int32_t* lutG, int r,
+// One routed block, the r-th LUT entry, whose tile is in LDS stage r % 2 and whose K scale is
+// ksc.  The copy of the next tile (or, after the last, of the epilogue's H^T image) into the
+// other stage runs meanwhile.  mask: the block may be partial (only the last LUT entry can
+// be: LUT rows are ascending and only block T-1 is partial).
+template <bool FP8, bool LUT_REG, int QT, int STG>
+__device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem0, uint8_t* smem1, int lutv,
+                                              float& ksc, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
-                                              float cq, bool mask, const TileSrc& src, TileRegs<FP8, 256 / QT>& t) {
+                                              float cq, bool mask, const TileSrc& src) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT>;
-  const uint8_t* stage = smem + (r & 1) * L::STAGE;
+  // the two stages are separate LDS objects and the stage roles are fixed per instantiation,
+  // so the compiler can see that this block's reads never touch the copy in flight
+  const uint8_t* stage = STG == 0 ? smem0 : smem1;
 
-  // ---- first, the tile of block r+1 (loaded during the previous iteration) goes to the other
-  // stage, whose previous tile (block r-1) was consumed before the last barrier; t is refilled
-  // with the tile of block r+2 (or, once the LUT is exhausted, the epilogue's H^T image).  The
-  // writes and loads then complete while this block is processed.
-  if (r + 1 < topk) store_tile<FP8, NT>(smem + ((r + 1) & 1) * L::STAGE, kscS + ((r + 1) & 1), tid, t);
-  load_next<FP8, LUT_REG, NT>(A, src, lutv, lutG, r + 2, topk, bh, tid, t);
+  // ---- first, start the copy of the next tile into the other stage, whose previous tile
+  // (block r-1) was consumed before the last barrier; it lands while this block is processed
+  uint8_t* next = STG == 0 ? smem1 : smem0;
+  float ksc_next = 1.f;
+  if (r + 1 < topk) {
+    const int jn = lut_entry<LUT_REG>(lutv, lutG, r + 1);
+    if constexpr (FP8) ksc_next = A.k_scale[(size_t)bh * A.T + jn];
+    dma_tile<FP8, NT>(A, src, jn, tid, next);
+  } else {
+    dma_himage<NT>(src, tid, next);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- S^T = K_j Q^T and Ph^T = phi(K_j) phi(Q)^T: keys 16mt + 4g + rr x queries l16 of each
@@ -292,7 +243,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     }
   }
   float cj = cq;
-  if constexpr (FP8) cj = cq * kscS[r & 1];   // stored with the tile
+  if constexpr (FP8) cj = cq * ksc;
   if (mask) {   // phi codes of keys past N are zero already; only the scores need it
     const int nvalid = A.N - kBlock * (A.T - 1);   // only block T-1 can be partial
 #pragma unroll
@@ -385,7 +336,9 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     __builtin_amdgcn_sched_barrier(0);
   });
 
+  wait_dma();
   lds_barrier();
+  ksc = ksc_next;
 }
 
 // phi(q) = softmax over the 128 features of query row q (bf16 input): this lane's features
@@ -448,15 +401,15 @@ __device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
 // H_i = h_sum - sum over routed j of h_j.  The routed part phi(q) h_j = (phi(q) phi(K_j)^T) V_j
 // is evaluated by re-association over the same routed keys and V^T tiles as the sparse
 // branch, with phi(K~) and phi(q) as e4m3 codes (phi(q) scaled per query).
-// Pipeline per routed block r: write the tile of block r+1 (loaded one iteration earlier) to
-// the other LDS stage, load the tile of block r+2, compute on the LDS tile of block r.
+// Pipeline per routed block r: start copying the tile of block r+1 into the other LDS stage,
+// compute on the LDS tile of block r, wait for the copy, barrier.
 template <bool FP8, bool LUT_REG, int QT>
 __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT>;
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
-  __shared__ float kscS[2];   // K scale of the tile in each stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[L::STAGE];   // stage of even LUT entries
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[L::STAGE];   // stage of odd LUT entries
   __shared__ float alphaS[D];
 
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
@@ -481,9 +434,10 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   const int lutv = (LUT_REG && lane < topk) ? lutG[lane] : 0;
   static_assert(NT >= D, "one thread per feature for alpha and Z_R");
   const float alv = tid < D ? A.alpha[(size_t)hidx * D + tid] : 0.f;
-  TileRegs<FP8, NT> t;
   const TileSrc src = tile_src(A, bh);
-  load_tile<FP8, NT>(A, src, bh, __builtin_amdgcn_readfirstlane(lutG[0]), tid, t);
+  const int j0 = __builtin_amdgcn_readfirstlane(lutG[0]);
+  float ksc = FP8 ? A.k_scale[(size_t)bh * A.T + j0] : 1.f;
+  dma_tile<FP8, NT>(A, src, j0, tid, smem0);
 
   QueryOps<QT> qo;
   float cq = kLog2e / sqrtf((float)D);
@@ -531,26 +485,24 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     st.l_run[qt] = 0.f;
   }
 
-  store_tile<FP8, NT>(smem, kscS, tid, t);
-  // Complete the query-operand loads here, before the next tile's loads are issued: the wait
-  // for their first use would otherwise sit inside the loop, where the counter cannot tell
-  // them from the prefetches in flight, and would drain every load on each iteration.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only (expcnt and lgkmcnt fields at their maxima)
-  load_next<FP8, LUT_REG, NT>(A, src, lutv, lutG, 1, topk, bh, tid, t);
-  lds_barrier();
-
-  for (int r = 0; r < topk; ++r)
-    fwd_iteration<FP8, LUT_REG, QT>(A, st, smem, lutv, kscS, lutG, r, topk, bh, l16, g, tid, qo, cq,
-                                    last_partial && r == topk - 1, src, t);
-
-  // ---------------- epilogue ----------------
-  // H^T (bf16 image loaded during the last iterations) into the free staging buffers; every
-  // wave needs all of it.
-  uint8_t* Hs = smem;
+  // The first tile and every query-operand load complete here, before the loop: a wait for a
+  // first use inside the loop could not tell them from the copies in flight there.
+  wait_dma();
   __shared__ float zrS[D];
-  store_himage<FP8, NT>(Hs, tid, t);
   if (tid < D) zrS[tid] = zr;
   lds_barrier();
+
+  for (int r = 0; r < topk; r += 2) {
+    fwd_iteration<FP8, LUT_REG, QT, 0>(A, st, smem0, smem1, lutv, ksc, lutG, r, topk, bh, l16, g, tid, qo, cq,
+                                       last_partial && r == topk - 1, src);
+    if (r + 1 < topk)
+      fwd_iteration<FP8, LUT_REG, QT, 1>(A, st, smem0, smem1, lutv, ksc, lutG, r + 1, topk, bh, l16, g, tid, qo,
+                                         cq, last_partial && r + 1 == topk - 1, src);
+  }
+
+  // ---------------- epilogue ----------------
+  // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
+  const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l_tot = rows4_sum(st.l_run[qt]);
