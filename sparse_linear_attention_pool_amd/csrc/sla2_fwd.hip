@@ -145,6 +145,9 @@ __device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g
 }
 
 constexpr int kLutReg = 64;   // LUT rows up to this long live in one register (lane x holds entry x)
+// LDS operand reads are issued this many matrix-core steps ahead of their use
+constexpr int kSReadAhead = 1;   // key-tile rows (S and phi products)
+constexpr int kVReadAhead = 3;   // V^T rows (P.V products)
 
 // Entry x of this query block's LUT row: read across lanes from the register copy, or from
 // memory when the row is longer than a wave.
@@ -206,23 +209,23 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   // operands of the block in registers at once.
   f32x4 S[QT][4], Ph[QT][4];
   if constexpr (FP8) {
-    i32x8 ka = lds_fp8_row(stage, l16, g), pa = lds_fp8_row(stage + L::POFF, l16, g);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      i32x8 kb = ka, pb = pa;
-      if (mt < 3) {
-        kb = lds_fp8_row(stage, 16 * (mt + 1) + l16, g);
-        pb = lds_fp8_row(stage + L::POFF, 16 * (mt + 1) + l16, g);
+    i32x8 kr[4], pr[4];
+    static_for<kSReadAhead>([&](auto mt) {
+      kr[mt] = lds_fp8_row(stage, 16 * mt + l16, g);
+      pr[mt] = lds_fp8_row(stage + L::POFF, 16 * mt + l16, g);
+    });
+    static_for<4>([&](auto mt) {
+      if constexpr (mt + kSReadAhead < 4) {
+        kr[mt + kSReadAhead] = lds_fp8_row(stage, 16 * (mt + kSReadAhead) + l16, g);
+        pr[mt + kSReadAhead] = lds_fp8_row(stage + L::POFF, 16 * (mt + kSReadAhead) + l16, g);
       }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        S[qt][mt] = mfma_fp8(ka, qo.q8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
-        Ph[qt][mt] = mfma_fp8(pa, qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+        S[qt][mt] = mfma_fp8(kr[mt], qo.q8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+        Ph[qt][mt] = mfma_fp8(pr[mt], qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
       }
       __builtin_amdgcn_sched_barrier(0);
-      ka = kb;
-      pa = pb;
-    }
+    });
   } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -317,21 +320,17 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
                                                                      16 * ((4 * s + g) ^ (row & 7))));
   };
-  bf16x8 vq[2][2];
-  vq[0][0] = vread(0, 0);
-  vq[0][1] = vread(0, 1);
-  static_for<8>([&](auto dt) {
-    if constexpr (dt + 1 < 8) {
-      vq[(dt + 1) & 1][0] = vread(dt + 1, 0);
-      vq[(dt + 1) & 1][1] = vread(dt + 1, 1);
-    }
-    const bf16x8 v0 = vq[dt & 1][0], v1 = vq[dt & 1][1];
+  // Steps k = 0..15 take key half s = k / 8 of feature tile dt = k % 8, so the two products
+  // that accumulate into the same registers are eight steps apart.
+  bf16x8 vq[16];
+  static_for<kVReadAhead>([&](auto k) { vq[k] = vread(k % 8, k / 8); });
+  static_for<16>([&](auto k) {
+    if constexpr (k + kVReadAhead < 16) vq[k + kVReadAhead] = vread((k + kVReadAhead) % 8, (k + kVReadAhead) / 8);
+    constexpr int dt = k % 8, sh = k / 8;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      st.acc[qt][dt] = mfma_bf16(v0, pop[qt][0], st.acc[qt][dt]);
-      st.accl[qt][dt] = mfma_bf16(v0, aop[qt][0], st.accl[qt][dt]);
-      st.acc[qt][dt] = mfma_bf16(v1, pop[qt][1], st.acc[qt][dt]);
-      st.accl[qt][dt] = mfma_bf16(v1, aop[qt][1], st.accl[qt][dt]);
+      st.acc[qt][dt] = mfma_bf16(vq[k], pop[qt][sh], st.acc[qt][dt]);
+      st.accl[qt][dt] = mfma_bf16(vq[k], aop[qt][sh], st.accl[qt][dt]);
     }
     __builtin_amdgcn_sched_barrier(0);
   });
