@@ -33,6 +33,8 @@
  *   - Calls must be made in the order sla2_route -> sla2_linear_precompute ->
  *     sla2_attention_fwd with the same params and tensors; each reads what the previous
  *     wrote (k_mean, lut, q8/k8, h, z, h_sum, z_sum and the workspace).
+ *   - Pointers a call does not use may be NULL; a NULL pointer it needs is rejected with
+ *     SLA2_ERR_INVALID_ARG and a message naming the tensor.
  *   - Results are deterministic: every reduction has a fixed order.
  *   - Inputs must be finite.
  */
@@ -97,8 +99,10 @@ typedef struct sla2_tensors {
   uint8_t *k8;             /* FP8 mode: [B,H,T*64,d] e4m3 codes of K~ / k_scale              */
   float *k_scale;          /* FP8 mode: [B,H,T]                                              */
   void *h;                 /* [B,H,T,d,d] dtype, TRANSPOSED: h[j][c][a] = sum over the valid
-                              tokens t of block j of phi(K~_t)[a] * V_t[c]                   */
-  float *z;                /* [B,H,T,d] z[j][a] = sum_t phi(K~_t)[a]                          */
+                              tokens t of block j of phi(K~_t)[a] * V_t[c].  Required for
+                              SLA2_F32; optional (NULL = not written) for SLA2_BF16, whose
+                              forward never reads it                                           */
+  float *z;                /* [B,H,T,d] z[j][a] = sum_t phi(K~_t)[a]; same rule as h          */
   float *h_sum;            /* [B,H,d,d] sum of h over all blocks (same transposed layout)    */
   float *z_sum;            /* [B,H,d]                                                        */
   /* ---- written by sla2_attention_fwd ---- */
@@ -122,16 +126,23 @@ int sla2_buffer_sizes(const sla2_params *p, sla2_sizes *out);
 int sla2_route(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Linear-branch precompute (SLA page, sections 2-3: h_j = phi(K_j)^T V_j, z_j =
- * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v, k_mean; writes h, z,
- * h_sum, z_sum, and in FP8 mode k8, k_scale; fills the workspace's staged V tiles. */
+ * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v, k_mean and, for
+ * SLA2_BF16, lut; writes h_sum, z_sum, h and z (when given), and in FP8 mode k8, k_scale.
+ * For SLA2_BF16 it also stages into the workspace what the fused forward reads: V^T tiles,
+ * e4m3 codes of 448 phi(K~), a bf16 image of h_sum^T and, per query block, the sum of z_j
+ * over its routed blocks (hence the lut). */
 int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Fused sparse + linear + mix forward (SLA2 page, sections 3 and 6: sparse attention over
  * the M = 1 blocks, linear-attention statistics over the M = 0 blocks, O = alpha * O_s +
- * (1 - alpha) * O_l).  Reads q, k (native mode), v, alpha, lut, q8/q_scale, k8/k_scale, h, z,
- * h_sum, z_sum and the workspace; writes o and, if non-NULL, lse.  The linear statistics of
- * query block i are formed as H_i = h_sum - sum over its routed j of h_j (and likewise Z_i),
- * which equals the sum over its unrouted blocks. */
+ * (1 - alpha) * O_l).  Reads q, k (native mode), v, alpha, lut, q8/q_scale, k8/k_scale,
+ * h_sum, z_sum, k_mean, the workspace and, for SLA2_F32, h and z; writes o and, if non-NULL,
+ * lse.  The linear statistics of query block i are those of its unrouted blocks, formed as
+ * the totals minus the routed part: H_i = h_sum - sum over routed j of h_j, Z_i likewise.
+ * SLA2_F32 gathers the routed h_j, z_j; SLA2_BF16 evaluates phi(q) times the routed part of
+ * H by re-association, as the sum over the routed keys s of (phi(q).phi(K~_s)) V_s (SLA page,
+ * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and takes
+ * the routed part of Z from the precompute. */
 int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Backward pass (SLA2 page, appendix A).  Not implemented: returns SLA2_ERR_UNSUPPORTED. */

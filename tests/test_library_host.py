@@ -76,6 +76,17 @@ def test_missing_tensors_are_rejected(B):
     assert b"'q'" in B.lib.sla2_last_error()
 
 
+def test_bf16_precompute_needs_the_lut(B):
+    # bf16 modes sum phi(K~) over each query block's routed key blocks in the precompute
+    p = B.make_params(1, 2, 1024, 128, 4, "bf16", "fp8")
+    t = B.Tensors()
+    fake = 256 * 1024          # aligned, never dereferenced: the call fails before any launch
+    for name in ("workspace", "k", "v", "k_mean", "h_sum", "z_sum", "k8", "k_scale"):
+        setattr(t, name, fake)
+    assert B.lib.sla2_linear_precompute(ctypes.byref(p), ctypes.byref(t), None) == B.SLA2_ERR_INVALID_ARG
+    assert b"'lut'" in B.lib.sla2_last_error()
+
+
 def test_backward_reports_unsupported(B):
     p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
     with pytest.raises(B.SLA2Error) as e:
