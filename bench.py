@@ -1,6 +1,7 @@
 """Benchmark of the SLA2 forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2]
+    python bench.py --copy-calibration MiB    # plain device copy, for HBM counter scaling
 
 One step is the whole forward over one batch whose inputs are already in HBM:
 sla2_route (pooling, FP8 quantisation of Q, projections, Top-k) ->
@@ -56,6 +57,48 @@ def kernel_bytes(w: I.Workload):
     return {"route": route, "precompute": pre}
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "fwd_mfma_kernel_c2_hbm_traffic.md")
+KERNEL_SOURCES = ("sparse_linear_attention_pool_amd/csrc/sla2_fwd.hip",
+                  "sparse_linear_attention_pool_amd/csrc/sla2_device.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the same counter's reading for a plain copy of known size), or
+    None if there is none for this workload or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    for line in open(TRAFFIC_RECORD):
+        if line.startswith("traffic-record: "):
+            rec = json.loads(line[len("traffic-record: "):])
+            if rec.get("workload") == workload and rec.get("source_sha256") == kernel_source_hash():
+                return rec["bytes_per_launch"]
+    return None
+
+
+def copy_calibration(mib: int):
+    """A plain device-to-device copy of `mib` MiB, three times: the known-size reference that
+    FETCH_SIZE / WRITE_SIZE readings are scaled by."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+
+
 def cpu_baseline(w: I.Workload, inp: dict, heads: int):
     """The oracle as it stands, timed on the host on `heads` heads of the workload."""
     from oracle import sla2_oracle as O
@@ -85,8 +128,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=sorted(I.CONFIGS))
-    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (HBM counter scaling) and exit")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path (heads would shard across GPUs with no communication).",
@@ -187,7 +235,7 @@ def main():
                    "linear_GFLOP": round(f_lin / 1e9, 3)},
         "roofline": {"kernel": "fwd_mfma_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "passes": passes,
     }
     if args.cpu_heads > 0:
