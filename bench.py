@@ -63,11 +63,17 @@ KERNEL_SOURCES = ("sparse_linear_attention_pool_amd/csrc/sla2_fwd.hip",
 
 
 def kernel_source_hash() -> str:
+    """sha256 of the fused kernel's sources with comments and blank space removed, so that a
+    documentation edit keeps a counter record valid and any code change invalidates it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

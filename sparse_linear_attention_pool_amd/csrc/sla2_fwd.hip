@@ -1,9 +1,13 @@
 // SLA2 fused forward: for each query block i, over the routed key blocks j in LUT order,
 //   S = Q_i K_j^T / sqrt(d) (FP8 e4m3 codes times the two block scales, or bf16),
 //   online softmax (running max and sum, exp2 with log2(e) folded into the scale),
-//   acc += P V_j (bf16 matrix cores), and C += h_j, c += z_j for the linear complement;
-// then O_s = acc / l, H_i = h_sum - C, Z_i = z_sum - c (the sum over the unrouted blocks),
-// O_l = phi(Q_i) H_i / (phi(Q_i) Z_i + eps) and O = alpha * O_s + (1 - alpha) * O_l.
+//   acc += P V_j (bf16 matrix cores);
+// then O_s = acc / l and the linear branch over the unrouted blocks,
+//   O_l = phi(Q_i) H_i / (phi(Q_i) Z_i + eps), H_i = h_sum - sum_{j routed} h_j, Z_i likewise,
+// and O = alpha * O_s + (1 - alpha) * O_l.  The fp32 kernel gathers the routed h_j, z_j.  The
+// matrix-core kernel never reads h_j: it adds phi(Q_i) times the routed part of H by
+// re-association, sum_{j routed} (phi(Q_i) phi(K~_j)^T) V_j, over the same key and V^T tiles as
+// the sparse branch, and takes Z_R(i) = sum_{j routed} z_j from the precompute.
 //
 // Pages: "SLA2: Sparse-Linear Attention with Learnable Routing and QAT", section 3 (sparse
 // attention only where M = 1 on FlashAttention-style computation; linear branch from the
