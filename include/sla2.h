@@ -125,6 +125,21 @@ int sla2_buffer_sizes(const sla2_params *p, sla2_sizes *out);
  * the lower block index.  Needs T <= 4096. */
 int sla2_route(const sla2_params *p, const sla2_tensors *t, void *stream);
 
+/* SoftTop-k router for training (SLA2 page, section 4: training replaces the hard Top-k by
+ * SoftTop-k, which keeps the row sum; section 6: a sigmoid with temperature tau and a per-row
+ * offset lambda_i found by binary search so that each row sums to k_sel).  Runs everything
+ * sla2_route does (same reads and writes, including the hard lut and mask the kernels use),
+ * then, from the same fp64 scores:
+ *   P_ij = softmax_j(s_ij) (the compressed attention of SLA page, section 2 Q2 step 1),
+ *   soft_mask[b,h,i,j] = sigmoid((P_ij - lambda_i) / tau),  lambda[b,h,i] = lambda_i,
+ * with lambda_i from 60 halvings of [min_j P_ij - tau (ln T + 2), max_j P_ij + tau (ln T + 2)]
+ * that keep the half where sum_j sigmoid((P_ij - lambda)/tau) crosses k_sel (fp64; each row
+ * then sums to k_sel up to rounding).  k_sel = T gives soft_mask = 1 and lambda = -inf.
+ * soft_mask: device float[B,H,T,T]; lambda: device float[B,H,T]; both caller-owned.
+ * tau must be positive and finite (else SLA2_ERR_INVALID_ARG). */
+int sla2_route_soft(const sla2_params *p, const sla2_tensors *t, float tau, float *soft_mask,
+                    float *lambda, void *stream);
+
 /* Linear-branch precompute (SLA page, sections 2-3: h_j = phi(K_j)^T V_j, z_j =
  * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v, k_mean and, for
  * SLA2_BF16, lut; writes h_sum, z_sum, h and z (when given), and in FP8 mode k8, k_scale.

@@ -22,7 +22,8 @@ SLA2_F32, SLA2_BF16 = 0, 1
 SLA2_QK_NATIVE, SLA2_QK_FP8_E4M3 = 0, 1
 
 ENTRY_POINTS = ("sla2_buffer_sizes", "sla2_route", "sla2_linear_precompute", "sla2_attention_fwd",
-                "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_status_string", "sla2_last_error")
+                "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_route_soft", "sla2_status_string",
+                "sla2_last_error")
 
 
 class SLA2Error(RuntimeError):
@@ -70,7 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.sla2_status_string.argtypes = [ctypes.c_int]
     lib.sla2_last_error.restype = ctypes.c_char_p
     lib.sla2_last_error.argtypes = []
-    for name in ENTRY_POINTS[:6]:
+    lib.sla2_route_soft.argtypes = [P, T, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for name in ENTRY_POINTS[:7]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -124,6 +126,13 @@ def _stream(stream) -> Optional[int]:
 def sla2_route(params: Params, tensors: dict, stream=None) -> None:
     tt = _tensors(tensors)
     _check("sla2_route", lib.sla2_route(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
+
+
+def sla2_route_soft(params: Params, tensors: dict, tau: float, soft_mask, lam, stream=None) -> None:
+    """sla2_route plus the SoftTop-k mask: soft_mask float32 [B,H,T,T], lam float32 [B,H,T]."""
+    tt = _tensors(tensors)
+    _check("sla2_route_soft", lib.sla2_route_soft(ctypes.byref(params), ctypes.byref(tt), float(tau),
+                                                  _ptr(soft_mask), _ptr(lam), _stream(stream)))
 
 
 def sla2_linear_precompute(params: Params, tensors: dict, stream=None) -> None:

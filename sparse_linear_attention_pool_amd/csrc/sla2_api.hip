@@ -3,6 +3,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 
 #include "sla2_internal.hpp"
@@ -162,6 +163,30 @@ int sla2_route(const sla2_params* p, const sla2_tensors* t, void* stream) {
     REQUIRE(t->q_scale, "q_scale");
   }
   return hip_status(launch_route(g, *t, ws, (hipStream_t)stream), fn);
+}
+
+int sla2_route_soft(const sla2_params* p, const sla2_tensors* t, float tau, float* soft_mask, float* lambda,
+                    void* stream) {
+  const char* fn = "sla2_route_soft";
+  Geometry g;
+  Workspace ws;
+  int st = prepare(fn, p, t, &g, &ws);
+  if (st != SLA2_OK) return st;
+  REQUIRE(t->q, "q");
+  REQUIRE(t->k, "k");
+  REQUIRE(t->q_pool, "q_pool");
+  REQUIRE(t->k_pool, "k_pool");
+  REQUIRE(t->k_mean, "k_mean");
+  REQUIRE(t->lut, "lut");
+  REQUIRE(t->mask, "mask");
+  if (g.fp8) {
+    REQUIRE(t->q8, "q8");
+    REQUIRE(t->q_scale, "q_scale");
+  }
+  REQUIRE(soft_mask, "soft_mask");
+  REQUIRE(lambda, "lambda");
+  if (!(tau > 0.f) || !std::isfinite(tau)) return fail(SLA2_ERR_INVALID_ARG, "%s: tau must be positive and finite", fn);
+  return hip_status(launch_route_soft(g, *t, ws, (double)tau, soft_mask, lambda, (hipStream_t)stream), fn);
 }
 
 int sla2_linear_precompute(const sla2_params* p, const sla2_tensors* t, void* stream) {

@@ -39,6 +39,8 @@ struct Workspace {
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);
 
 hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
+                             float* soft_mask, float* lambda, hipStream_t s);
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
 hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
 hipError_t launch_selftest_mfma(int which, const void* a, const void* b, void* d, hipStream_t s);

@@ -453,6 +453,135 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
                      t.k_mean, mu_final, ws.qhat, ws.khatT);
 }
 
+// ---------------------------------------------------------------------------------------
+// SoftTop-k router mask (SLA2 page, section 4: for training the row's hard Top-k is replaced
+// by SoftTop-k, which keeps its row sum; section 6: a sigmoid with temperature tau and a
+// per-row offset lambda_i found by binary search so that each row sums to the Top-k count).
+// Input: P_c = softmax over the row of the router scores s_ij (SLA page, section 2 Q2 step 1),
+// the scores the hard Top-k ranks.  M_ij = sigmoid((P_ij - lambda_i) / tau).  The search
+// starts from [min P - tau (ln T + 2), max P + tau (ln T + 2)] (row sum above T - 1 at the
+// lower end, below 1 at the upper end) and halves it kSoftSteps times, keeping the half in
+// which the row sum crosses k_sel; lambda_i is the last midpoint.  k_sel = T gives M = 1 and
+// lambda = -inf.  One wave per query-block row, lane l holding the columns j = l + 64 m;
+// fp64 throughout, like the hard router.
+// ---------------------------------------------------------------------------------------
+constexpr int kSoftSteps = 60;
+
+// Sum over the wave, then lane 0's value on every lane: a branch on the result is then
+// uniform even though the butterfly adds in a different order on each lane.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return __shfl(v, 0);
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;   // exact, so every lane holds the same value
+}
+__device__ __forceinline__ double wave_min_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmin(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double sigmoid_f64(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+template <int MAXS, int D>
+__global__ __launch_bounds__(64) void softtopk_kernel(const double* __restrict__ qhat,
+                                                      const double* __restrict__ khatT, int T, int topk,
+                                                      double inv_sqrt_d, double tau, float* __restrict__ soft_mask,
+                                                      float* __restrict__ lambda) {
+  const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const double* qrow = qhat + ((size_t)bh * T + i) * D;
+  const double* kb = khatT + (size_t)bh * D * T;
+  double p[MAXS];
+  static_for<MAXS>([&](auto m) { p[m] = 0.0; });
+  for (int c = 0; c < D; ++c) {
+    const double qc = qrow[c];
+    static_for<MAXS>([&](auto m) {
+      const int j = 64 * m + lane;
+      if (j < T) p[m] = fma(qc, kb[(size_t)c * T + j], p[m]);
+    });
+  }
+  // P_c: softmax over the row's T columns
+  double mx = -INFINITY;
+  static_for<MAXS>([&](auto m) {
+    p[m] *= inv_sqrt_d;
+    if (64 * m + lane < T) mx = fmax(mx, p[m]);
+  });
+  mx = wave_max_f64(mx);
+  double z = 0.0;
+  static_for<MAXS>([&](auto m) {
+    p[m] = 64 * m + lane < T ? exp(p[m] - mx) : 0.0;
+    z += p[m];
+  });
+  z = wave_sum_f64(z);
+  double pmin = INFINITY, pmax = -INFINITY;
+  static_for<MAXS>([&](auto m) {
+    p[m] /= z;
+    if (64 * m + lane < T) {
+      pmin = fmin(pmin, p[m]);
+      pmax = fmax(pmax, p[m]);
+    }
+  });
+  pmin = wave_min_f64(pmin);
+  pmax = wave_max_f64(pmax);
+
+  double lam = -INFINITY;
+  if (topk < T) {
+    const double pad = tau * (log((double)T) + 2.0);
+    double lo = pmin - pad, hi = pmax + pad;
+    for (int it = 0; it < kSoftSteps; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      double f = 0.0;
+      static_for<MAXS>([&](auto m) {
+        if (64 * m + lane < T) f += sigmoid_f64((p[m] - mid) / tau);
+      });
+      f = wave_sum_f64(f);
+      if (f > (double)topk) lo = mid;   // row sum too large: the offset must grow
+      else hi = mid;
+    }
+    lam = 0.5 * (lo + hi);
+  }
+  float* mrow = soft_mask + ((size_t)bh * T + i) * T;
+  static_for<MAXS>([&](auto m) {
+    const int j = 64 * m + lane;
+    if (j < T) mrow[j] = topk < T ? (float)sigmoid_f64((p[m] - lam) / tau) : 1.f;
+  });
+  if (lane == 0) lambda[(size_t)bh * T + i] = (float)lam;
+}
+
+template <int D>
+static void launch_softtopk(const Geometry& g, const Workspace& ws, double tau, float* soft_mask, float* lambda,
+                            hipStream_t s) {
+  const dim3 grid(g.T, g.BH);
+  const int S = (g.T + 63) / 64;
+  const double isd = 1.0 / sqrt((double)g.D);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64), 0, s, ws.qhat, ws.khatT, g.T, g.topk, isd, tau, soft_mask, lambda);
+  };
+  if (S <= 1) go(softtopk_kernel<1, D>);
+  else if (S <= 2) go(softtopk_kernel<2, D>);
+  else if (S <= 4) go(softtopk_kernel<4, D>);
+  else if (S <= 8) go(softtopk_kernel<8, D>);
+  else if (S <= 16) go(softtopk_kernel<16, D>);
+  else if (S <= 32) go(softtopk_kernel<32, D>);
+  else go(softtopk_kernel<64, D>);
+}
+
+hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
+                             float* soft_mask, float* lambda, hipStream_t s) {
+  const hipError_t e = launch_route(g, t, ws, s);
+  if (e != hipSuccess) return e;
+  if (g.D == 128) launch_softtopk<128>(g, ws, tau, soft_mask, lambda, s);
+  else launch_softtopk<64>(g, ws, tau, soft_mask, lambda, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
   if (g.bf16) {
     launch_route_typed<uint16_t, 128>(g, t, ws, s);   // bf16 inputs have d = 128

@@ -87,6 +87,20 @@ def test_bf16_precompute_needs_the_lut(B):
     assert b"'lut'" in B.lib.sla2_last_error()
 
 
+def test_soft_route_rejects_bad_tau_before_any_launch(B):
+    p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
+    t = B.Tensors()
+    fake = 256 * 1024          # aligned, never dereferenced
+    for name in ("workspace", "q", "k", "q_pool", "k_pool", "k_mean", "lut", "mask"):
+        setattr(t, name, fake)
+    for tau in (0.0, -0.5, float("nan"), float("inf")):
+        assert B.lib.sla2_route_soft(ctypes.byref(p), ctypes.byref(t), tau, fake, fake, None) == \
+            B.SLA2_ERR_INVALID_ARG
+        assert b"tau" in B.lib.sla2_last_error()
+    assert B.lib.sla2_route_soft(ctypes.byref(p), ctypes.byref(t), 0.1, None, fake, None) == B.SLA2_ERR_INVALID_ARG
+    assert b"'soft_mask'" in B.lib.sla2_last_error()
+
+
 def test_backward_reports_unsupported(B):
     p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
     with pytest.raises(B.SLA2Error) as e:
