@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=sorted(I.CONFIGS))
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--soft-tau", type=float, default=0.001,
+                    help="temperature of the separately timed SoftTop-k router leg (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -244,6 +246,25 @@ def main():
                      "traffic": measured_traffic(w.name)},
         "passes": passes,
     }
+    if args.soft_tau > 0:
+        # the training router (not part of the inference step): sla2_route_soft on the same
+        # inputs, timed alone; its SoftTop-k kernel runs kSoftSteps fp64 sigmoid sums per row
+        T = w.T
+        soft = torch.empty((w.B, w.H, T, T), dtype=torch.float32, device=dev)
+        lam = torch.empty((w.B, w.H, T), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            Bn.sla2_route_soft(p, t, args.soft_tau, soft, lam, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for _ in range(args.steps):
+            Bn.sla2_route_soft(p, t, args.soft_tau, soft, lam, stream)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        t_soft = e0.elapsed_time(e1) / args.steps
+        passes["soft_route_ms"] = round(float(t_soft), 5)
+        passes["soft_route_tau"] = args.soft_tau
+        log(f"[bench] sla2_route_soft (tau {args.soft_tau}): {t_soft:.4f} ms")
     if args.cpu_heads > 0:
         log(f"[bench] timing the CPU oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_heads, w.H))

@@ -80,6 +80,7 @@ typedef struct sla2_sizes {
   size_t h, z, h_sum, z_sum;
   size_t o, lse;
   size_t workspace;
+  size_t workspace_bwd;   /* scratch of sla2_attention_bwd (0 where the backward is unsupported) */
 } sla2_sizes;
 
 typedef struct sla2_tensors {
@@ -111,6 +112,8 @@ typedef struct sla2_tensors {
                               exp(q_t . K~_s / sqrt(d)) (dequantised operands in FP8 mode)   */
   /* ---- scratch shared by the three calls ---- */
   void *workspace;         /* sla2_sizes.workspace bytes, 256-byte aligned                    */
+  /* ---- scratch of the backward pass only ---- */
+  void *workspace_bwd;     /* sla2_sizes.workspace_bwd bytes, 256-byte aligned                */
 } sla2_tensors;
 
 /* Host only, pure: fills *out with the byte size of every buffer for *p.
@@ -160,7 +163,21 @@ int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *st
  * the routed part of Z from the precompute. */
 int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream);
 
-/* Backward pass (SLA2 page, appendix A).  Not implemented: returns SLA2_ERR_UNSUPPORTED. */
+/* Backward pass (SLA2 page, appendix A: gradients of Q, K, V through phi(Q), phi(K) and the
+ * per-query-block dH_i, dZ_i, each key block collecting them from the query blocks that do not
+ * route to it; section 5: low-bit forward, 16-bit backward).  Gradients of sum(dout * o) with
+ * the routing held fixed (no gradient reaches W_q, W_k or the pooling), the FP8 quantiser
+ * passed straight through (dQ' -> dQ, dK' -> dK~), and key smoothing differentiated
+ * (dK = dK~ - mean over tokens of dK~ when smooth_k).
+ * Supported: dtype SLA2_BF16, qk_mode SLA2_QK_FP8_E4M3, d = 128 (else SLA2_ERR_UNSUPPORTED).
+ * Reads everything the three forward calls wrote for the same params and inputs: q, k, v,
+ * alpha, k_mean, lut, mask, q8, q_scale, k8, k_scale, h and z (so the precompute must have
+ * been given h and z), h_sum, z_sum, lse (so the forward must have been given lse), and the
+ * workspace; writes only workspace_bwd and the outputs.
+ *   dout:   device bf16 [B,H,N,d], the gradient of the loss with respect to o;
+ *   dq, dk, dv: device bf16 [B,H,N,d];
+ *   dalpha: device float [H,d], summed over the batch and the tokens.
+ * The matrix products take bf16 (and, for the scores, e4m3) operands with fp32 accumulation. */
 int sla2_attention_bwd(const sla2_params *p, const sla2_tensors *t, const void *dout,
                        void *dq, void *dk, void *dv, float *dalpha, void *stream);
 

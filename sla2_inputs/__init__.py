@@ -77,6 +77,9 @@ CONFIGS = {
                    0.03, True, 2, (21, 30, 52)),
     "C3": Workload("C3 Wan2.1-14B-720P-shaped, fp8 QK, 3% sparse", 1, 40, 75600, 128, "bf16", "fp8",
                    0.03, True, 3, (21, 45, 80)),
+    # fine-tuning step on the C1 shape: FP8 (QAT) forward, then the backward against dO ~ N(0,1)
+    "C4": Workload("C4 Wan2.1-1.3B-shaped fine-tuning step, fp8 QK (QAT), 5% sparse", 1, 12, 32760, 128,
+                   "bf16", "fp8", 0.05, False, 4, (21, 30, 52)),
 }
 
 

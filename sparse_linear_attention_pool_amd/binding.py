@@ -39,7 +39,7 @@ class Params(ctypes.Structure):
 
 
 SIZE_FIELDS = ("q_pool", "k_pool", "k_mean", "lut", "mask", "q8", "k8", "q_scale", "k_scale",
-               "h", "z", "h_sum", "z_sum", "o", "lse", "workspace")
+               "h", "z", "h_sum", "z_sum", "o", "lse", "workspace", "workspace_bwd")
 
 
 class Sizes(ctypes.Structure):
@@ -47,7 +47,8 @@ class Sizes(ctypes.Structure):
 
 
 TENSOR_FIELDS = ("q", "k", "v", "wq", "wk", "alpha", "q_pool", "k_pool", "k_mean", "lut", "mask",
-                 "q8", "q_scale", "k8", "k_scale", "h", "z", "h_sum", "z_sum", "o", "lse", "workspace")
+                 "q8", "q_scale", "k8", "k_scale", "h", "z", "h_sum", "z_sum", "o", "lse", "workspace",
+                 "workspace_bwd")
 
 
 class Tensors(ctypes.Structure):
@@ -153,6 +154,20 @@ def sla2_attention_bwd(params: Params, tensors: dict, dout, dq, dk, dv, dalpha, 
                                   _ptr(dv), _ptr(dalpha), _stream(stream)))
 
 
+def backward(params: Params, inputs: dict, buffers: dict, dout, stream=None) -> dict:
+    """sla2_attention_bwd after `forward` ran on the same inputs and buffers (allocated with
+    per_block_stats=True, with_lse=True, with_bwd=True).  Returns dq, dk, dv, dalpha."""
+    import torch
+    t = dict(buffers)
+    for key in ("q", "k", "v", "alpha", "wq", "wk"):
+        t[key] = inputs.get(key)
+    q = inputs["q"]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dalpha = torch.empty((params.H, params.d), dtype=torch.float32, device=q.device)
+    sla2_attention_bwd(params, t, dout, dq, dk, dv, dalpha, stream)
+    return {"dq": dq, "dk": dk, "dv": dv, "dalpha": dalpha}
+
+
 def sla2_selftest_mfma(which: int, a, b, d, stream=None) -> None:
     _check("sla2_selftest_mfma", lib.sla2_selftest_mfma(which, _ptr(a), _ptr(b), _ptr(d), _stream(stream)))
 
@@ -160,11 +175,13 @@ def sla2_selftest_mfma(which: int, a, b, d, stream=None) -> None:
 # --------------------------------------------------------------------------------------
 # device buffers (torch allocations sized by sla2_buffer_sizes)
 # --------------------------------------------------------------------------------------
-def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_stats: bool = True) -> dict:
+def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_stats: bool = True,
+             with_bwd: bool = False) -> dict:
     """Allocate every output and scratch buffer the three calls need, on `device`.
 
     per_block_stats=False leaves out h and z (bf16 modes only): the forward pass reads
-    only their sums, and the precompute then skips storing them.
+    only their sums, and the precompute then skips storing them.  with_bwd adds the
+    backward pass's scratch (its gradients also need h, z and with_lse).
     """
     import torch
     sz = sla2_buffer_sizes(params)
@@ -192,10 +209,14 @@ def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_st
         out["z"] = torch.empty((B, H, T, d), dtype=torch.float32, device=device)
     if with_lse:
         out["lse"] = torch.empty((B, H, N), dtype=torch.float32, device=device)
+    if with_bwd:
+        if sz["workspace_bwd"] == 0:
+            raise SLA2Error("allocate", SLA2_ERR_UNSUPPORTED, "no backward pass for these params")
+        out["workspace_bwd"] = torch.empty(sz["workspace_bwd"], dtype=torch.uint8, device=device)
     for name, t in out.items():
         want = sz[name]
         have = t.numel() * t.element_size()
-        if name == "workspace":
+        if name in ("workspace", "workspace_bwd"):
             if have < want:
                 raise RuntimeError("workspace too small")
         elif have != want:

@@ -117,6 +117,7 @@ int fill_sizes(const Geometry& g, sla2_sizes* s) {
   s->o = BH * N * D * es;
   s->lse = BH * N * 4;
   s->workspace = workspace_layout(g, nullptr, nullptr);
+  s->workspace_bwd = (g.bf16 && g.fp8 && g.D == 128) ? bwd_workspace_layout(g, nullptr, nullptr) : 0;
   return SLA2_OK;
 }
 
@@ -242,8 +243,40 @@ int sla2_attention_fwd(const sla2_params* p, const sla2_tensors* t, void* stream
 
 int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* dout, void* dq, void* dk,
                        void* dv, float* dalpha, void* stream) {
-  (void)p; (void)t; (void)dout; (void)dq; (void)dk; (void)dv; (void)dalpha; (void)stream;
-  return fail(SLA2_ERR_UNSUPPORTED, "sla2_attention_bwd: the backward pass is not implemented");
+  const char* fn = "sla2_attention_bwd";
+  Geometry g;
+  Workspace ws;
+  int st = prepare(fn, p, t, &g, &ws);
+  if (st != SLA2_OK) return st;
+  if (!g.bf16 || !g.fp8 || g.D != 128)
+    return fail(SLA2_ERR_UNSUPPORTED, "%s: implemented for bf16 inputs with FP8 Q.K^T and d = 128", fn);
+  REQUIRE(t->q, "q");
+  REQUIRE(t->k, "k");
+  REQUIRE(t->v, "v");
+  REQUIRE(t->alpha, "alpha");
+  REQUIRE(t->k_mean, "k_mean");
+  REQUIRE(t->lut, "lut");
+  REQUIRE(t->mask, "mask");
+  REQUIRE(t->q8, "q8");
+  REQUIRE(t->q_scale, "q_scale");
+  REQUIRE(t->k8, "k8");
+  REQUIRE(t->k_scale, "k_scale");
+  REQUIRE(t->h, "h");
+  REQUIRE(t->z, "z");
+  REQUIRE(t->h_sum, "h_sum");
+  REQUIRE(t->z_sum, "z_sum");
+  REQUIRE(t->lse, "lse");
+  REQUIRE(t->workspace_bwd, "workspace_bwd");
+  if (((uintptr_t)t->workspace_bwd & 255) != 0)
+    return fail(SLA2_ERR_INVALID_ARG, "%s: workspace_bwd must be 256-byte aligned", fn);
+  REQUIRE(dout, "dout");
+  REQUIRE(dq, "dq");
+  REQUIRE(dk, "dk");
+  REQUIRE(dv, "dv");
+  REQUIRE(dalpha, "dalpha");
+  BwdWorkspace bw;
+  bwd_workspace_layout(g, &bw, (char*)t->workspace_bwd);
+  return hip_status(launch_bwd(g, *t, ws, bw, dout, dq, dk, dv, dalpha, (hipStream_t)stream), fn);
 }
 
 int sla2_selftest_mfma(int which, const void* a, const void* b, void* d, void* stream) {

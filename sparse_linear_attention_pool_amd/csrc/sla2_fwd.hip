@@ -527,7 +527,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
         }
       }
     }
-    const float inv_den = 1.f / (rows4_sum(den) + A.eps);
+    // with every block routed the linear branch is an empty sum, 0 (the complement form would
+    // leave only rounding, amplified by 1/eps)
+    const float inv_den = topk < A.T ? 1.f / (rows4_sum(den) + A.eps) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -692,7 +694,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const int cc = d0 + x;
     float num = 0.f;
     for (int a = 0; a < D; ++a) num = fmaf(Ps[ql * D + a], Hs[cc * D + a], num);
-    const float os = acc[x] / l_tot, olin = num / den;
+    // with every block routed the linear branch is an empty sum, 0; the complement form would
+    // leave only rounding, amplified by 1/eps
+    const float os = acc[x] / l_tot, olin = topk < T ? num / den : 0.f;
     if (qok) o[((size_t)bh * N + qrow) * D + cc] = al[cc] * os + (1.f - al[cc]) * olin;
   }
   if (lse != nullptr) {

@@ -38,11 +38,35 @@ struct Workspace {
 
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);
 
+// Views into the caller's backward workspace (layout fixed by bwd_workspace_layout()).
+struct BwdWorkspace {
+  uint16_t* dos;        // [BH, 64T, D] alpha * dO in bf16 (rows past N zero)
+  uint16_t* dot;        // [BH, T, D, 64] dos transposed per block
+  uint16_t* qt;         // [BH, T, D, 64] dequantised e4m3 Q, transposed per block
+  uint16_t* kt;         // [BH, T, D, 64] dequantised e4m3 K~, transposed per block
+  int32_t* inv;         // [BH, T, T] per key block: the query blocks routing to it, ascending
+  int32_t* inv_cnt;     // [BH, T]
+  float* dsum;          // [BH, 64T] rowsum(dO_s * O_s)
+  float* dH;            // [BH, T, D, D] dH_i
+  float* dZ;            // [BH, T, D]
+  float* dH_tot;        // [BH, D, D]
+  float* dZ_tot;        // [BH, D]
+  float* dalpha_part;   // [BH, T, D]
+  float* dkt;           // [BH, 64T, D] dK~ in fp32, before the key-smoothing correction
+  float* colsum_part;   // [BH, ceil(N/256), D]
+};
+
+size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base);
+
 hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
 hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
                              float* soft_mask, float* lambda, hipStream_t s);
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
 hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_sum_parts(const float* parts, const float* zparts, int P, int D, int BH, float* out,
+                            float* zout, hipStream_t s);
+hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const BwdWorkspace& bw,
+                      const void* dout, void* dq, void* dk, void* dv, float* dalpha, hipStream_t s);
 hipError_t launch_selftest_mfma(int which, const void* a, const void* b, void* d, hipStream_t s);
 
 }  // namespace sla2

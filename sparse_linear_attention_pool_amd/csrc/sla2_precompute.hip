@@ -441,4 +441,11 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
   return hipGetLastError();
 }
 
+hipError_t launch_sum_parts(const float* parts, const float* zparts, int P, int D, int BH, float* out,
+                            float* zout, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_sums_kernel, dim3((D * D + 255) / 256, BH), dim3(256), 0, s, parts, zparts, P, D,
+                     out, zout, (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
 }  // namespace sla2

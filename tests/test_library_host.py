@@ -102,8 +102,27 @@ def test_soft_route_rejects_bad_tau_before_any_launch(B):
 
 
 def test_backward_reports_unsupported(B):
+    # implemented for bf16 inputs with FP8 Q.K^T and d = 128 only
     p = B.make_params(1, 2, 1024, 64, 4, "f32", "native")
     with pytest.raises(B.SLA2Error) as e:
-        B.sla2_attention_bwd(p, {}, None, None, None, None, None, stream=0)
+        B.sla2_attention_bwd(p, {"workspace": 256 * 1024}, None, None, None, None, None, stream=0)
     assert e.value.status == B.SLA2_ERR_UNSUPPORTED
     assert B.lib.sla2_status_string(-2) == b"unsupported"
+    assert B.sla2_buffer_sizes(p)["workspace_bwd"] == 0
+
+
+def test_backward_needs_the_forward_buffers(B):
+    p = B.make_params(1, 12, 32760, 128, 15, "bf16", "fp8")
+    sz = B.sla2_buffer_sizes(p)
+    assert sz["workspace_bwd"] > 0
+    fake = 256 * 1024          # aligned, never dereferenced: every call fails before a launch
+    have = {"workspace": fake}
+    for name in ("q", "k", "v", "alpha", "k_mean", "lut", "mask", "q8", "q_scale", "k8", "k_scale",
+                 "h", "z", "h_sum", "z_sum", "lse", "workspace_bwd"):
+        with pytest.raises(B.SLA2Error) as e:
+            B.sla2_attention_bwd(p, have, fake, fake, fake, fake, fake, stream=0)
+        assert e.value.status == B.SLA2_ERR_INVALID_ARG and f"'{name}'" in str(e.value), (name, str(e.value))
+        have[name] = fake
+    with pytest.raises(B.SLA2Error) as e:
+        B.sla2_attention_bwd(p, have, None, fake, fake, fake, fake, stream=0)
+    assert "'dout'" in str(e.value)
