@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=sorted(I.CONFIGS))
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time sla2_attention_bwd (default for the C4 fine-tuning workload)")
     ap.add_argument("--soft-tau", type=float, default=0.001,
                     help="temperature of the separately timed SoftTop-k router leg (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -162,7 +164,9 @@ def main():
     d_in["wq"] = None if inp["wq"] is None else torch.from_numpy(inp["wq"]).to(dev)
     d_in["wk"] = None if inp["wk"] is None else torch.from_numpy(inp["wk"]).to(dev)
     p = Bn.make_params(w.B, w.H, w.N, w.d, w.topk, w.dtype, w.qk_mode)
-    bufs = Bn.allocate(p, dev, per_block_stats=(w.dtype != "bf16"))
+    want_bwd = args.backward or args.config == "C4"
+    bufs = Bn.allocate(p, dev, per_block_stats=(w.dtype != "bf16") or want_bwd, with_lse=want_bwd,
+                       with_bwd=want_bwd)
     t = dict(bufs)
     t.update(d_in)
     stream = torch.cuda.current_stream(dev)
@@ -246,6 +250,30 @@ def main():
                      "traffic": measured_traffic(w.name)},
         "passes": passes,
     }
+    if want_bwd:
+        # the fine-tuning step's backward on the forward's buffers, timed alone
+        dout = torch.from_numpy(I.generate(w, with_dout=True)["dout"]).to(el).to(dev)
+        grads = {k: torch.empty_like(d_in["q"]) for k in ("dq", "dk", "dv")}
+        dal = torch.empty((w.H, w.d), dtype=torch.float32, device=dev)
+        def bwd():
+            Bn.sla2_attention_bwd(p, t, dout, grads["dq"], grads["dk"], grads["dv"], dal, stream)
+        for _ in range(2):
+            bwd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for _ in range(args.steps):
+            bwd()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        t_bwd = e0.elapsed_time(e1) / args.steps
+        # the four gradient products of the routed blocks (dP, dV, dQ, dK): 2 x the forward's two
+        f_bwd = 2 * f_sparse
+        passes["bwd_ms"] = round(float(t_bwd), 5)
+        passes["bwd_routed_TFLOPS"] = round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)
+        passes["train_step_ms"] = round(float(ms_step + t_bwd), 5)
+        log(f"[bench] sla2_attention_bwd: {t_bwd:.4f} ms ({passes['bwd_routed_TFLOPS']} TFLOP/s over the 4 routed "
+            f"gradient products)")
     if args.soft_tau > 0:
         # the training router (not part of the inference step): sla2_route_soft on the same
         # inputs, timed alone; its SoftTop-k kernel runs kSoftSteps fp64 sigmoid sums per row

@@ -128,6 +128,7 @@ struct BwdArgs {
   float* dalpha_part;      // [BH, T, D]
   float* dkt;              // [BH, 64T, D] dK~ (fp32)
   float* colsum_part;      // [BH, NCH, D]
+  float* dk_mean;          // [BH, D]
   // outputs
   uint16_t* dq;            // bf16 [BH, N, D]
   uint16_t* dk;
@@ -719,26 +720,48 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(BwdArgs A) {
   if (tid < kD) A.colsum_part[((size_t)bh * A.nch + ch) * kD + tid] = red[0][tid] + red[1][tid];
 }
 
-__global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs A) {
-  const int r = blockIdx.x * 2 + (threadIdx.x >> 7), bh = blockIdx.y, c = threadIdx.x & (kD - 1);
-  if (r >= A.N) return;
-  float mean = 0.f;
-  if (A.smooth_k) {
-    for (int ch = 0; ch < A.nch; ++ch) mean += A.colsum_part[((size_t)bh * A.nch + ch) * kD + c];
-    mean /= (float)A.N;
-  }
-  A.dk[((size_t)bh * A.N + r) * kD + c] = f32_to_bf16(A.dkt[((size_t)bh * A.T * 64 + r) * kD + c] - mean);
+// mean over the N tokens of dK~ (zero without key smoothing), from the chunk sums in fixed order
+__global__ __launch_bounds__(128) void bwd_mean_kernel(BwdArgs A) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  float s = 0.f;
+  if (A.smooth_k)
+    for (int ch = 0; ch < A.nch; ++ch) s += A.colsum_part[((size_t)bh * A.nch + ch) * kD + c];
+  A.dk_mean[(size_t)bh * kD + c] = A.smooth_k ? s / (float)A.N : 0.f;
 }
 
-// dalpha[h][c] = sum over batch and query blocks of the per-block partials
-__global__ __launch_bounds__(128) void bwd_dalpha_kernel(BwdArgs A) {
-  const int hidx = blockIdx.x, c = threadIdx.x;
+// dK = dK~ - mean: 16 bytes of a row per thread
+__global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs A) {
+  const int bh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;   // chunk of 8 features
+  const int r = e >> 4, c0 = 8 * (e & 15);
+  if (r >= A.N) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(A.dkt + ((size_t)bh * A.T * 64 + r) * kD + c0);
+  const f32x4* mu = reinterpret_cast<const f32x4*>(A.dk_mean + (size_t)bh * kD + c0);
+  const f32x4 a = src[0] - mu[0], b = src[1] - mu[1];
+  u32x4 out;
+  out.x = pack_bf16x2(a.x, a.y);
+  out.y = pack_bf16x2(a.z, a.w);
+  out.z = pack_bf16x2(b.x, b.y);
+  out.w = pack_bf16x2(b.z, b.w);
+  *reinterpret_cast<u32x4*>(A.dk + ((size_t)bh * A.N + r) * kD + c0) = out;
+}
+
+// dalpha[h][c] = sum over batch and query blocks of the per-block partials: 8 partial sums
+// per feature over interleaved blocks, combined in fixed order
+__global__ __launch_bounds__(1024) void bwd_dalpha_kernel(BwdArgs A) {
+  __shared__ float red[8][kD];
+  const int hidx = blockIdx.x, c = threadIdx.x & (kD - 1), u = threadIdx.x >> 7;
   float s = 0.f;
   for (int b = 0; b < A.B; ++b) {
     const int bh = b * A.H + hidx;
-    for (int i = 0; i < A.T; ++i) s += A.dalpha_part[((size_t)bh * A.T + i) * kD + c];
+    for (int i = u; i < A.T; i += 8) s += A.dalpha_part[((size_t)bh * A.T + i) * kD + c];
   }
-  A.dalpha[(size_t)hidx * kD + c] = s;
+  red[u][c] = s;
+  __syncthreads();
+  if (u == 0) {
+    float t = 0.f;
+    for (int k = 0; k < 8; ++k) t += red[k][c];
+    A.dalpha[(size_t)hidx * kD + c] = t;
+  }
 }
 
 }  // namespace
@@ -767,6 +790,7 @@ size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
   w.dalpha_part = (float*)take(BH * T * D * 4);
   w.dkt = (float*)take(BH * T * 64 * D * 4);
   w.colsum_part = (float*)take(BH * nch * D * 4);
+  w.dk_mean = (float*)take(BH * D * 4);
   if (ws) *ws = w;
   return off;
 }
@@ -806,6 +830,7 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   A.dalpha_part = bw.dalpha_part;
   A.dkt = bw.dkt;
   A.colsum_part = bw.colsum_part;
+  A.dk_mean = bw.dk_mean;
   A.dq = (uint16_t*)dq;
   A.dk = (uint16_t*)dk;
   A.dv = (uint16_t*)dv;
@@ -826,8 +851,9 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_key_kernel, blocks, dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_colsum_kernel, dim3(A.nch, g.BH), dim3(256), 0, s, A);
-  hipLaunchKernelGGL(bwd_dk_kernel, dim3((g.N + 1) / 2, g.BH), dim3(256), 0, s, A);
-  hipLaunchKernelGGL(bwd_dalpha_kernel, dim3(g.H), dim3(128), 0, s, A);
+  hipLaunchKernelGGL(bwd_mean_kernel, dim3(g.BH), dim3(128), 0, s, A);
+  hipLaunchKernelGGL(bwd_dk_kernel, dim3((g.N * 16 + 255) / 256, g.BH), dim3(256), 0, s, A);
+  hipLaunchKernelGGL(bwd_dalpha_kernel, dim3(g.H), dim3(1024), 0, s, A);
   return hipGetLastError();
 }
 

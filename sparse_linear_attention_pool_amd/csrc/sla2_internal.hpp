@@ -54,6 +54,7 @@ struct BwdWorkspace {
   float* dalpha_part;   // [BH, T, D]
   float* dkt;           // [BH, 64T, D] dK~ in fp32, before the key-smoothing correction
   float* colsum_part;   // [BH, ceil(N/256), D]
+  float* dk_mean;       // [BH, D]
 };
 
 size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base);
