@@ -9,7 +9,9 @@
 namespace sla2 {
 
 // Key blocks summed into one partial of h_sum / z_sum by the precompute kernels.
-constexpr int kChunk = 8;
+// 13 key blocks per workgroup: the C2 head count and length (12 x 512 blocks) then fill the
+// 512 workgroup slots of a 256-CU MI355X (two per CU) in one round, with no tail.
+constexpr int kChunk = 13;
 
 struct Geometry {
   int B, H, N, D, T, topk, P;   // P = ceil(T / kChunk)
