@@ -165,7 +165,7 @@ def main():
     d_in["wk"] = None if inp["wk"] is None else torch.from_numpy(inp["wk"]).to(dev)
     p = Bn.make_params(w.B, w.H, w.N, w.d, w.topk, w.dtype, w.qk_mode)
     want_bwd = args.backward or args.config == "C4"
-    bufs = Bn.allocate(p, dev, per_block_stats=(w.dtype != "bf16") or want_bwd, with_lse=want_bwd,
+    bufs = Bn.allocate(p, dev, per_block_stats=(w.dtype != "bf16"), with_lse=want_bwd,
                        with_bwd=want_bwd)
     t = dict(bufs)
     t.update(d_in)

@@ -160,7 +160,11 @@ int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *st
  * SLA2_F32 gathers the routed h_j, z_j; SLA2_BF16 evaluates phi(q) times the routed part of
  * H by re-association, as the sum over the routed keys s of (phi(q).phi(K~_s)) V_s (SLA page,
  * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and takes
- * the routed part of Z from the precompute. */
+ * the routed part of Z from the precompute.
+ * Training forward: when t->workspace_bwd is non-NULL (and the backward supports the params:
+ * SLA2_BF16, SLA2_QK_FP8_E4M3, d = 128) the call also stores in it, per query, the sparse
+ * output O_s, the linear output O_l (both bf16) and 1/(phi(q).Z_i + eps), which the backward
+ * reads; a workspace_bwd that is not 256-byte aligned is SLA2_ERR_INVALID_ARG. */
 int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Backward pass (SLA2 page, appendix A: gradients of Q, K, V through phi(Q), phi(K) and the
@@ -170,10 +174,13 @@ int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream
  * passed straight through (dQ' -> dQ, dK' -> dK~), and key smoothing differentiated
  * (dK = dK~ - mean over tokens of dK~ when smooth_k).
  * Supported: dtype SLA2_BF16, qk_mode SLA2_QK_FP8_E4M3, d = 128 (else SLA2_ERR_UNSUPPORTED).
- * Reads everything the three forward calls wrote for the same params and inputs: q, k, v,
- * alpha, k_mean, lut, mask, q8, q_scale, k8, k_scale, h and z (so the precompute must have
- * been given h and z), h_sum, z_sum, lse (so the forward must have been given lse), and the
- * workspace; writes only workspace_bwd and the outputs.
+ * Reads what the three forward calls wrote for the same params and inputs: q, k, v, alpha,
+ * k_mean, lut, mask, q8, q_scale, k8, k_scale, h_sum, z_sum, lse (so the forward must have
+ * been given lse), the workspace, and the O_s, O_l and 1/den that a training forward (one given
+ * this workspace_bwd) stored; h and z are not read.  Writes only workspace_bwd and the outputs.
+ * The linear branch never forms H_i or dH_i per block: the query side re-associates the routed
+ * part of dnum H_i^T over the routed key tiles, and each key block forms its dh_j as the total
+ * minus one product per routing query block.
  *   dout:   device bf16 [B,H,N,d], the gradient of the loss with respect to o;
  *   dq, dk, dv: device bf16 [B,H,N,d];
  *   dalpha: device float [H,d], summed over the batch and the tokens.

@@ -156,7 +156,8 @@ def sla2_attention_bwd(params: Params, tensors: dict, dout, dq, dk, dv, dalpha, 
 
 def backward(params: Params, inputs: dict, buffers: dict, dout, stream=None) -> dict:
     """sla2_attention_bwd after `forward` ran on the same inputs and buffers (allocated with
-    per_block_stats=True, with_lse=True, with_bwd=True).  Returns dq, dk, dv, dalpha."""
+    with_lse=True and with_bwd=True, which makes that forward store what the backward reads).
+    Returns dq, dk, dv, dalpha."""
     import torch
     t = dict(buffers)
     for key in ("q", "k", "v", "alpha", "wq", "wk"):
@@ -181,7 +182,7 @@ def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_st
 
     per_block_stats=False leaves out h and z (bf16 modes only): the forward pass reads
     only their sums, and the precompute then skips storing them.  with_bwd adds the
-    backward pass's scratch (its gradients also need h, z and with_lse).
+    backward pass's workspace (the backward also needs with_lse; it does not read h or z).
     """
     import torch
     sz = sla2_buffer_sizes(params)

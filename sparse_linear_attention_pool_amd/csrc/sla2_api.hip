@@ -238,7 +238,15 @@ int sla2_attention_fwd(const sla2_params* p, const sla2_tensors* t, void* stream
     REQUIRE(t->q_scale, "q_scale");
     REQUIRE(t->k_scale, "k_scale");
   }
-  return hip_status(launch_fwd(g, *t, ws, (hipStream_t)stream), fn);
+  // a backward workspace makes this a training forward: it also stores what the backward reads
+  BwdWorkspace bw;
+  const bool keep = t->workspace_bwd != nullptr && g.bf16 && g.fp8 && g.D == 128;
+  if (keep) {
+    if (((uintptr_t)t->workspace_bwd & 255) != 0)
+      return fail(SLA2_ERR_INVALID_ARG, "%s: workspace_bwd must be 256-byte aligned", fn);
+    bwd_workspace_layout(g, &bw, (char*)t->workspace_bwd);
+  }
+  return hip_status(launch_fwd(g, *t, ws, keep ? &bw : nullptr, (hipStream_t)stream), fn);
 }
 
 int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* dout, void* dq, void* dk,
@@ -261,8 +269,6 @@ int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* 
   REQUIRE(t->q_scale, "q_scale");
   REQUIRE(t->k8, "k8");
   REQUIRE(t->k_scale, "k_scale");
-  REQUIRE(t->h, "h");
-  REQUIRE(t->z, "z");
   REQUIRE(t->h_sum, "h_sum");
   REQUIRE(t->z_sum, "z_sum");
   REQUIRE(t->lse, "lse");

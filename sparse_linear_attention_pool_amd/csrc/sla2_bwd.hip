@@ -9,23 +9,29 @@
 // the FlashAttention backward; the linear branch goes through dH_i, dZ_i, symmetric to the
 // forward).  Straight-through quantiser: dQ' passes to Q and dK' to K~.
 //
-// Per query block i (bwd_query_kernel), over its routed key blocks:
-//   pass A: S = Q' K'^T / sqrt(d), P = exp(S - lse), O_s = P V, then Dq = rowsum(dO_s * O_s);
-//   linear: H_i, Z_i (totals minus the routed h_j, z_j), O_l, dalpha, dnum = dO_l / den,
-//           dden = -(dO_l . O_l) / den, dphi(q) = dnum H_i^T + dden Z_i, dH_i = phi(q)^T dnum,
-//           dZ_i = dden^T phi(q);
-//   pass B: dP = dO_s V^T, dS = P (dP - Dq), dQ' = dS K' / sqrt(d).
-// Per key block j (bwd_key_kernel), over the query blocks that route to it:
-//   dV = P^T dO_s, dK' = dS^T Q' / sqrt(d); linear: dh_j = dH_tot - sum of dH_i over those
-//   query blocks (the rest are the ones that do not route to j), dz_j likewise,
-//   dphi(k) = V dh_j^T + dz_j, dV += phi(k) dh_j.
-// Then dK = dK~ - mean over tokens (key smoothing) and dalpha summed over tokens and batch.
+// The forward run before it stores O_s, O_l and 1/den per query (den = phi(q).Z_i + eps).
+// With dO_s = alpha dO and dO_l = (1 - alpha) dO:
+//   D_q = rowsum(dO_s * O_s), dnum = dO_l / den, dden = -(dO_l . O_l) / den,
+//   dalpha = sum over tokens of dO * (O_s - O_l);
+// sparse branch, P recomputed from lse over each routed pair:
+//   dP = dO_s V^T, dS = P (dP - D_q), dQ' = dS K' / sqrt(d), dK' = dS^T Q' / sqrt(d),
+//   dV = P^T dO_s;
+// linear branch, O_l = phi(q) H_i / den with H_i, Z_i over the unrouted blocks:
+//   dphi(q) = dnum H_i^T + dden Z_i, dH_i = phi(q)^T dnum, dZ_i = dden^T phi(q),
+//   dh_j = sum of dH_i over the query blocks i that do not route to j (dz_j likewise),
+//   dphi(k) = V dh_j^T + dz_j, dV += phi(k) dh_j, then the softmax backward of phi.
+// Neither H_i nor dH_i is formed per pair.  Query side: H_i = H_tot - sum over the routed j of
+// phi(K_j)^T V_j, so dnum H_i^T = dnum H_tot^T - sum_j (dnum V_j^T) phi(K_j), evaluated on the
+// routed key tiles the sparse branch loads anyway.  Key side: with dH_i = (phi(q_i) / den)^T
+// dO_i diag(1 - alpha), dh_j = (G_tot - sum over the query blocks i routing to j of
+// (phi(q_i) / den)^T dO_i) diag(1 - alpha), one 128 x 128 product per routing pair, whose dO_i^T
+// operand is the tile the sparse branch's dV product reads.
 //
-// Matrix products run on the bf16 16x16x32 matrix cores (the scores on the e4m3 16x16x128
-// ones, exactly as the forward computed them) with both operands read from LDS tiles that hold
-// the contraction index contiguous: A as rows of the left factor, B as rows of the right
-// factor's transpose.  Tiles are staged synchronously; this first version favours a plain
-// structure over overlap.
+// Kernels: bwd_prep_kernel (per-token terms and the transposed operand tiles), the column sums
+// G_tot and dZ_tot, bwd_query_kernel (dQ), bwd_key_kernel (dK~, dV), then the key-smoothing
+// mean and dalpha.  Both main kernels copy each pair's tiles into LDS with direct-to-LDS loads
+// while the previous pair is processed (two stages), and run the products on the bf16
+// 16x16x32 matrix cores (the scores on the e4m3 16x16x128 ones, as the forward computed them).
 #include <math.h>
 
 #include "sla2_device.hpp"
@@ -37,6 +43,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kNT = 256;
+constexpr int kTTile = kD * kBlock * 2;   // bytes of one transposed bf16 tile: 128 rows x 64
+constexpr int kRec = 256;                 // floats per query block in the key side's record
+constexpr int kGChunk = 16;               // query blocks per partial of G_tot
 
 // Row-major LDS tile of RB-byte rows whose 16-byte chunks are XOR-swizzled by the row index:
 // 16 lanes reading one chunk column of 16 consecutive rows hit distinct banks.
@@ -53,21 +62,15 @@ struct LTile {
   __device__ __forceinline__ bf16x8 op(int r, int k0) const {       // 8 bf16 from element k0
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(chunk(r, k0 >> 3)));
   }
-  __device__ __forceinline__ i32x8 op8(int r, int g) const {        // 32 e4m3 codes, bytes 32g..
-    const u32x4 a = *reinterpret_cast<const u32x4*>(chunk(r, 2 * g));
-    const u32x4 b = *reinterpret_cast<const u32x4*>(chunk(r, 2 * g + 1));
-    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
 };
 
-// rows x RB bytes from global rows of stride ld bytes; rows >= nvalid are zero
+// rows x RB bytes from global rows of stride ld bytes
 template <int RB>
-__device__ __forceinline__ void stage(LTile<RB> dst, const uint8_t* src, size_t ld, int rows, int nvalid, int tid) {
+__device__ __forceinline__ void stage(LTile<RB> dst, const uint8_t* src, size_t ld, int rows, int tid) {
   constexpr int NC = RB / 16;
   for (int x = tid; x < rows * NC; x += kNT) {
     const int r = x / NC, c = x % NC;
-    const u32x4 v = r < nvalid ? *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + 16 * c) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(dst.chunk(r, c)) = v;
+    *reinterpret_cast<u32x4*>(dst.chunk(r, c)) = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + 16 * c);
   }
 }
 
@@ -80,6 +83,17 @@ __device__ __forceinline__ f32x4 mm(const LTile<RBA>& At, int m0, const LTile<RB
   return c;
 }
 
+// 16-byte chunk (4s + g) of row `row` of a staged 128-byte-row tile (64 bf16 per row): the
+// operand holding elements 32s + 8g .. 32s + 8g + 7
+__device__ __forceinline__ bf16x8 op128(const uint8_t* base, int row, int s, int g) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + row * 128 + 16 * ((4 * s + g) ^ (row & 7))));
+}
+// the same for a staged 256-byte-row tile (128 bf16 per row)
+__device__ __forceinline__ bf16x8 op256(const uint8_t* base, int row, int s, int g) {
+  return __builtin_bit_cast(bf16x8,
+                            *reinterpret_cast<const u32x4*>(base + row * 256 + 16 * ((4 * s + g) ^ (row & 15))));
+}
+
 // e4m3 (OCP: bias 7, no infinities, 0x7f / 0xff NaN never produced by the quantiser)
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
@@ -87,11 +101,24 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
-// column position of key (or query) x of a 64-block in the forward's V^T tiles: within each
-// 32-half, keys 4gg + e sit at 8gg + e and keys 16 + 4gg + e at 8gg + 4 + e
+// Column of token x of a 64-block in the transposed tiles (the forward's V^T order): within
+// each 32-half, tokens 4gg + e sit at 8gg + e and tokens 16 + 4gg + e at 8gg + 4 + e.  A 16 x 16
+// product's output (token rows 4g + r of two adjacent 16-row tiles) then packs, without a
+// transpose, into the B operand whose k-index is this column.
 __device__ __forceinline__ int vt_pos(int x) {
   const int s = x >> 5, rem = x & 31, h = rem >> 4, gg = (rem & 15) >> 2, e = rem & 3;
   return 32 * s + 8 * gg + 4 * h + e;
+}
+
+// 8 bf16 values as the B operand: v[4h + rr] from output tile 2s + h, row 4g + rr
+__device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
+  const uint32_t w[4] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 struct BwdArgs {
@@ -101,29 +128,36 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* alpha;      // [H, D]
   const float* k_mean;     // [BH, D]
-  const uint8_t* q8;       // [BH, 64T, D]
+  const uint8_t* q8;       // [BH, 64T, D] (pad rows code 0)
   const uint8_t* k8;
   const float* q_scale;    // [BH, T]
   const float* k_scale;
   const float* lse;        // [BH, N]
   const int32_t* lut;      // [BH, T, topk]
   const uint8_t* mask;     // [BH, T, T]
-  const uint16_t* h;       // bf16 [BH, T, D, D], h[j][c][a]
-  const float* z;          // [BH, T, D]
-  const float* h_sum;      // [BH, D, D] (transposed like h)
+  const float* h_sum;      // [BH, D, D], h_sum[c][a]
   const float* z_sum;      // [BH, D]
-  const uint16_t* vt;      // forward workspace: [BH, T, D, 64] V^T tiles, keys at vt_pos
+  const float* zrout;      // forward workspace: [BH, T, D] Z_R(i)
+  // stored by the forward
+  const uint16_t* os;      // [BH, N, D] O_s (bf16)
+  const uint16_t* ol;      // [BH, N, D] O_l (bf16)
+  const float* inv_den;    // [BH, 64T] 1 / den (0 when every block is routed)
   // backward workspace
-  uint16_t* dos;           // [BH, 64T, D] alpha * dO (rows past N zero)
-  uint16_t* dot;           // [BH, T, D, 64] dos transposed
-  uint16_t* qt;            // [BH, T, D, 64] Q'^T (dequantised e4m3)
-  uint16_t* kt;            // [BH, T, D, 64] K'^T
+  uint16_t* dos;           // [BH, 64T, D] alpha * dO rows (pad rows 0)
+  uint16_t* dot;           // [BH, T, D, 64] dO^T per block, tokens at vt_pos
+  uint16_t* q8t;           // [BH, T, D, 64] e4m3 values of Q8 (unscaled) transposed, vt_pos
+  uint16_t* phqdt;         // [BH, T, D, 64] (phi(q) / den)^T, vt_pos
+  uint16_t* k8t;           // [BH, T, D, 64] e4m3 values of K8 transposed, vt_pos
+  uint16_t* phkt;          // [BH, T, D, 64] phi(K~)^T, vt_pos (pad tokens 0)
+  uint16_t* htimg;         // [BH, D, D] bf16 H_tot rows a (h_sum transposed), LDS image
+  float* qrec;             // [BH, T, 256] per query block: lse[64], D_q[64], zeros
+  float* dden;             // [BH, 64T]
   int32_t* inv;            // [BH, T, T] query blocks routing to key block j, ascending
   int32_t* inv_cnt;        // [BH, T]
-  float* dsum;             // [BH, 64T] rowsum(dO_s * O_s)
-  float* dH;               // [BH, T, D, D] dH_i[a][c]
   float* dZ;               // [BH, T, D]
-  float* dH_tot;           // [BH, D, D]
+  float* gpart;            // [BH, PG, D, D] partials of G_tot
+  float* zpart;            // [BH, PG, D]
+  float* g_tot;            // [BH, D, D] G_tot[a][c] = sum over tokens of phi(q)[a] / den * dO[c]
   float* dZ_tot;           // [BH, D]
   float* dalpha_part;      // [BH, T, D]
   float* dkt;              // [BH, 64T, D] dK~ (fp32)
@@ -134,51 +168,164 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dalpha;           // [H, D]
-  int B, H, N, T, topk, nch;
-  float eps;
+  int B, H, N, T, topk, nch, pg, nblocks;
   int smooth_k;
 };
 
 // ---------------------------------------------------------------------------------------
-// Per (head, 64-token block b): alpha * dO rows and their transpose, and the transposed
-// dequantised e4m3 tiles of Q and K~.
+// Per (head, 64-token block b), four threads per token (32 features each).  As a query block:
+// D_q, dden, the dalpha and dZ_i column sums, alpha dO rows, and the transposed tiles dO^T,
+// (phi(q)/den)^T and Q8^T.  As a key block: K8^T and phi(K~)^T.  Block 0 also writes the bf16
+// image of H_tot with rows a.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
-  __shared__ uint16_t tr[kD * 64];   // [row c][col x], plain row-major
+  __shared__ uint16_t tr[kD * kBlock];        // [feature][vt_pos(token)]
+  __shared__ float red[kBlock][kD + 4];       // per-token values of one column sum
   const int b = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, hidx = bh % A.H;
-  const int x = tid >> 2, c0 = 32 * (tid & 3);   // token x of the block, features c0..c0+31
-  const int tok = 64 * b + x;
-  const size_t row = (size_t)bh * A.T * 64 + tok;
-  auto flush = [&](uint16_t* dst) {   // tr -> dst[bh][b][c][x], 16-byte chunks
+  const int x = tid >> 2, c0 = 32 * (tid & 3);
+  const int tok = kBlock * b + x;
+  const bool ok = tok < A.N;
+  const int px = vt_pos(x);
+  const size_t trow = (size_t)bh * A.N + (ok ? tok : 0);       // row of the [BH, N, D] tensors
+  const size_t prow = (size_t)bh * A.T * kBlock + tok;          // row of the padded [BH, 64T, D] ones
+  const size_t tile = ((size_t)bh * A.T + b) * kD * kBlock;     // block b's transposed tiles
+  auto flush = [&](uint16_t* dst) {
     __syncthreads();
-    uint16_t* base = dst + ((size_t)bh * A.T + b) * kD * 64;
-    for (int e = tid; e < kD * 64 / 8; e += kNT)
-      reinterpret_cast<u32x4*>(base)[e] = reinterpret_cast<const u32x4*>(tr)[e];
+    for (int e = tid; e < kD * kBlock / 8; e += kNT)
+      reinterpret_cast<u32x4*>(dst + tile)[e] = reinterpret_cast<const u32x4*>(tr)[e];
     __syncthreads();
   };
-  // alpha * dO
+  auto colsum = [&](float* dst) {   // dst[c] = sum over the 64 tokens of red[.][c]
+    __syncthreads();
+    if (tid < kD) {
+      float s = 0.f;
+      for (int t = 0; t < kBlock; ++t) s += red[t][tid];
+      dst[tid] = s;
+    }
+    __syncthreads();
+  };
+  auto load32 = [&](const uint16_t* src, float (&f)[32]) {   // features c0.. of row trow (0 past N)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 wv = ok ? *reinterpret_cast<const u32x4*>(src + trow * kD + c0 + 8 * u) : u32x4{0, 0, 0, 0};
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[8 * u + 2 * e] = bf16_lo(ww[e]);
+        f[8 * u + 2 * e + 1] = bf16_hi(ww[e]);
+      }
+    }
+  };
+  // softmax over the 128 features of a row held by the four threads of a token
+  auto softmax32 = [&](float (&f)[32]) {
+    float mx = f[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, f[e]);
+    mx = fmaxf(mx, dpp<0xB1>(mx));
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      f[e] = __expf(f[e] - mx);
+      s += f[e];
+    }
+    s += dpp<0xB1>(s);
+    s += dpp<0x4E>(s);
+    const float is = 1.f / s;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) f[e] *= is;
+  };
+
+  float dO[32], al[32];
+  load32(A.dout, dO);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) al[e] = A.alpha[(size_t)hidx * kD + c0 + e];
+  const float inv_den = ok ? A.inv_den[prow] : 0.f;   // pad rows are never written by the forward
+  float dq = 0.f, dd = 0.f;
+  {
+    float os[32], ol[32];
+    load32(A.os, os);
+    load32(A.ol, ol);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      dq = fmaf(al[e] * dO[e], os[e], dq);
+      dd = fmaf((1.f - al[e]) * dO[e], ol[e], dd);
+      red[x][c0 + e] = dO[e] * (os[e] - ol[e]);
+    }
+  }
+  dq += dpp<0xB1>(dq);
+  dq += dpp<0x4E>(dq);
+  dd += dpp<0xB1>(dd);
+  dd += dpp<0x4E>(dd);
+  const float dden = -dd * inv_den;
+  colsum(A.dalpha_part + ((size_t)bh * A.T + b) * kD);
+
+  // alpha dO rows and dO^T
   {
     uint16_t out[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const int c = c0 + e;
-      float val = 0.f;
-      if (tok < A.N) val = A.alpha[(size_t)hidx * kD + c] * bf16_to_f32(A.dout[((size_t)bh * A.N + tok) * kD + c]);
-      out[e] = f32_to_bf16(val);
-      tr[c * 64 + x] = out[e];
+      out[e] = f32_to_bf16(al[e] * dO[e]);
+      tr[(c0 + e) * kBlock + px] = f32_to_bf16(dO[e]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      reinterpret_cast<u32x4*>(A.dos + row * kD + c0)[u] = reinterpret_cast<const u32x4*>(out)[u];
-    flush(A.dot);
+      reinterpret_cast<u32x4*>(A.dos + prow * kD + c0)[u] = reinterpret_cast<const u32x4*>(out)[u];
   }
-  // Q' and K' = e4m3 code * block scale (pad rows hold code 0)
-  for (int which = 0; which < 2; ++which) {
-    const uint8_t* codes = (which == 0 ? A.q8 : A.k8) + row * kD + c0;
-    const float sc = (which == 0 ? A.q_scale : A.k_scale)[(size_t)bh * A.T + b];
+  flush(A.dot);
+
+  // phi(q) / den and the column sums dZ_i = sum_q dden phi(q)
+  {
+    float f[32];
+    load32(A.q, f);
+    softmax32(f);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) tr[(c0 + e) * 64 + x] = f32_to_bf16(e4m3_value(codes[e]) * sc);
-    flush(which == 0 ? A.qt : A.kt);
+    for (int e = 0; e < 32; ++e) {
+      const float ph = ok ? f[e] : 0.f;
+      tr[(c0 + e) * kBlock + px] = f32_to_bf16(ph * inv_den);
+      red[x][c0 + e] = dden * ph;
+    }
+  }
+  flush(A.phqdt);
+  colsum(A.dZ + ((size_t)bh * A.T + b) * kD);
+
+  // e4m3 values of the Q and K~ codes (exact in bf16), transposed
+  for (int which = 0; which < 2; ++which) {
+    const uint8_t* codes = (which == 0 ? A.q8 : A.k8) + prow * kD + c0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) tr[(c0 + e) * kBlock + px] = f32_to_bf16(e4m3_value(codes[e]));
+    flush(which == 0 ? A.q8t : A.k8t);
+  }
+
+  // phi(K~)^T (pad tokens 0)
+  {
+    float f[32];
+    load32(A.k, f);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) f[e] -= A.k_mean[(size_t)bh * kD + c0 + e];
+    softmax32(f);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) tr[(c0 + e) * kBlock + px] = f32_to_bf16(ok ? f[e] : 0.f);
+  }
+  flush(A.phkt);
+
+  // per-query record of the key side, and dden
+  float* rec = A.qrec + ((size_t)bh * A.T + b) * kRec;
+  if ((tid & 3) == 0) {
+    rec[x] = ok ? A.lse[trow] : 0.f;
+    rec[kBlock + x] = dq;   // 0 past N (dO is 0 there)
+    A.dden[prow] = dden;
+  }
+  if (tid >= 2 * kBlock) rec[tid] = 0.f;
+
+  // H_tot with rows a: image[a] chunk k at k ^ (a % 16)
+  if (b == 0) {
+    const float* hs = A.h_sum + (size_t)bh * kD * kD;
+    uint16_t* img = A.htimg + (size_t)bh * kD * kD;
+    for (int e = tid; e < kD * kD; e += kNT) {
+      const int c = e / kD, a = e % kD;
+      img[a * kD + 8 * ((c >> 3) ^ (a & 15)) + (c & 7)] = f32_to_bf16(hs[e]);
+    }
   }
 }
 
@@ -199,512 +346,610 @@ __global__ __launch_bounds__(64) void bwd_invlut_kernel(BwdArgs A) {
   if (lane == 0) A.inv_cnt[(size_t)bh * A.T + j] = base;
 }
 
-// ---------------------------------------------------------------------------------------
-// Query side.  Wave w owns queries 16w..16w+15 of block i; results in the matrix-core output
-// layout: lane (g = l/16, l16 = l%16) holds rows 16w + 4g + r (r < 4) of column l16 of each
-// 16-wide column tile.
-// ---------------------------------------------------------------------------------------
-namespace qlds {
-constexpr int QS = 0;                 // Q8 rows of block i        64 x 128 B
-constexpr int DOS = QS + 8192;        // alpha * dO rows           64 x 256 B
-constexpr int SMALL = DOS + 16384;    // lse, Dq, den, m, 1/s, dden, Z_i, alpha partials
-constexpr int U = SMALL + 4096;       // union of the phases
-// sparse phases
-constexpr int PS = U;                 // P or dS                   64 x 128 B
-constexpr int KS = PS + 8192;         // K8 rows of block j        64 x 128 B
-constexpr int VT = KS + 8192;         // V^T (forward tile)        128 x 128 B
-constexpr int VS = VT + 16384;        // V rows                    64 x 256 B
-constexpr int KT = VS + 16384;        // K'^T                      128 x 128 B
-// linear phase
-constexpr int HT = U;                 // H_i^T [c][a]              128 x 256 B
-constexpr int HN = HT + 32768;        // H_i [a][c]                128 x 256 B
-constexpr int PHQ = HN + 32768;       // phi(q) [q][a]             64 x 256 B
-constexpr int PHQT = PHQ + 16384;     // phi(q)^T [a][q]           128 x 128 B
-constexpr int DNUM = PHQT + 16384;    // dnum [q][c]               64 x 256 B
-constexpr int DNUMT = DNUM + 16384;   // dnum^T [c][q]             128 x 128 B
-constexpr int BYTES = DNUMT + 16384;
-static_assert(KT + 16384 <= BYTES, "sparse phase fits the union");
-}  // namespace qlds
-
-__global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sm[qlds::BYTES];
-  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4, hidx = bh % A.H;
-  const int q0 = 16 * w;
-  const int T = A.T, topk = A.topk;
-  float* lseS = reinterpret_cast<float*>(sm + qlds::SMALL);
-  float* dqS = lseS + 64;
-  float* denS = dqS + 64;
-  float* mqS = denS + 64;
-  float* isS = mqS + 64;
-  float* ddenS = isS + 64;
-  float* ZS = ddenS + 64;            // 128
-  float* alS = ZS + 128;             // 4 x 128
-  const LTile<128> QS{sm + qlds::QS}, PS{sm + qlds::PS}, KS{sm + qlds::KS}, VT{sm + qlds::VT}, KT{sm + qlds::KT};
-  const LTile<256> DOS{sm + qlds::DOS}, VS{sm + qlds::VS}, HT{sm + qlds::HT}, HN{sm + qlds::HN},
-      PHQ{sm + qlds::PHQ}, DNUM{sm + qlds::DNUM};
-  const LTile<128> PHQT{sm + qlds::PHQT}, DNUMT{sm + qlds::DNUMT};
-  const int32_t* lut = A.lut + ((size_t)bh * T + i) * topk;
-  const float inv_sqrt_d = 1.f / sqrtf((float)kD);
-  const int nq = min(64, A.N - 64 * i);   // valid queries of this block
-
-  stage<128>(QS, A.q8 + ((size_t)bh * T * 64 + 64 * i) * kD, kD, 64, 64, tid);
-  stage<256>(DOS, reinterpret_cast<const uint8_t*>(A.dos + ((size_t)bh * T * 64 + 64 * i) * kD), 2 * kD, 64, 64, tid);
-  if (tid < 64) lseS[tid] = tid < nq ? A.lse[(size_t)bh * A.N + 64 * i + tid] : 0.f;
-  __syncthreads();
-  const float qsc = A.q_scale[(size_t)bh * T + i];
-
-  // scores of this wave's queries against key block j: S[nt] = 16 x 16 tiles (keys 16nt..)
-  auto scores = [&](int j, f32x4 (&S)[4]) {
-    const float cj = kLog2e * inv_sqrt_d * qsc * A.k_scale[(size_t)bh * T + j];
-    const int nk = min(64, A.N - 64 * j);
+// Partials of G_tot[a][c] = sum over tokens of (phi(q)/den)[a] dO[c] over kGChunk query blocks,
+// and of dZ_tot.  Wave w: rows a = 32w..32w+31.
+__global__ __launch_bounds__(256) void bwd_gtot_kernel(BwdArgs A) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sm[2 * kTTile];
+  const LTile<128> PT{sm}, OT{sm + kTTile};
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  f32x4 acc[2][8];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 s = mfma_fp8(QS.op8(q0 + l16, g), KS.op8(16 * nt + l16, g), f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int at = 0; at < 2; ++at)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = q0 + 4 * g + r, key = 16 * nt + l16;
-        const bool ok = qq < nq && key < nk;
-        s[r] = ok ? __builtin_amdgcn_exp2f(s[r] * cj - lseS[qq] * kLog2e) : 0.f;   // P
-      }
-      S[nt] = s;
-    }
-  };
-
-  // ---------------- pass A: O_s and Dq
-  f32x4 os[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) os[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < topk; ++r) {
-    const int j = lut[r];
-    stage<128>(KS, A.k8 + ((size_t)bh * T * 64 + 64 * j) * kD, kD, 64, 64, tid);
-    stage<128>(VT, reinterpret_cast<const uint8_t*>(A.vt + ((size_t)bh * T + j) * kD * 64), 128, 128, 128, tid);
+    for (int ct = 0; ct < 8; ++ct) acc[at][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int b0 = p * kGChunk, b1 = min(A.T, b0 + kGChunk);
+  for (int b = b0; b < b1; ++b) {
     __syncthreads();
-    f32x4 P[4];
-    scores(j, P);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) *PS.el16(q0 + 4 * g + rr, vt_pos(16 * nt + l16)) = f32_to_bf16(P[nt][rr]);
+    const size_t tile = ((size_t)bh * A.T + b) * kD * kBlock;
+    stage<128>(PT, reinterpret_cast<const uint8_t*>(A.phqdt + tile), 128, kD, tid);
+    stage<128>(OT, reinterpret_cast<const uint8_t*>(A.dot + tile), 128, kD, tid);
     __syncthreads();
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) os[nt] = mm<64>(PS, q0, VT, 16 * nt, l16, g, os[nt]);
-    __syncthreads();
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[at][ct] = mm<64>(PT, 32 * w + 16 * at, OT, 16 * ct, l16, g, acc[at][ct]);
   }
-  // Dq = sum_c dO_s * O_s
-  {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  float* out = A.gpart + ((size_t)bh * A.pg + p) * kD * kD;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+  for (int at = 0; at < 2; ++at)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part[rr] += bf16_to_f32(*DOS.el16(q0 + 4 * g + rr, 16 * nt + l16)) * os[nt][rr];
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float dsum = row16_sum(part[rr]);
-      if (l16 == 0) {
-        dqS[q0 + 4 * g + rr] = dsum;
-        if (q0 + 4 * g + rr < nq) A.dsum[(size_t)bh * T * 64 + 64 * i + q0 + 4 * g + rr] = dsum;
-      }
-    }
-  }
-
-  // ---------------- linear branch
-  // Z_i and H_i^T: totals minus the routed blocks
+      for (int r = 0; r < 4; ++r) out[(32 * w + 16 * at + 4 * g + r) * kD + 16 * ct + l16] = acc[at][ct][r];
   if (tid < kD) {
-    float zz = A.z_sum[(size_t)bh * kD + tid];
-    for (int r = 0; r < topk; ++r) zz -= A.z[((size_t)bh * T + lut[r]) * kD + tid];
-    ZS[tid] = zz;
+    float z = 0.f;
+    for (int b = b0; b < b1; ++b) z += A.dZ[((size_t)bh * A.T + b) * kD + tid];
+    A.zpart[((size_t)bh * A.pg + p) * kD + tid] = z;
   }
-  {
-    const int c = tid >> 1, a0 = 64 * (tid & 1);
-    float hh[64];
-    const float* hs = A.h_sum + (size_t)bh * kD * kD + c * kD + a0;
-#pragma unroll
-    for (int e = 0; e < 64; ++e) hh[e] = hs[e];
-    for (int r = 0; r < topk; ++r) {
-      const u32x4* hj = reinterpret_cast<const u32x4*>(A.h + (((size_t)bh * T + lut[r]) * kD + c) * kD + a0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const u32x4 wv = hj[u];
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hh[8 * u + 2 * e] -= bf16_lo(ww[e]);
-          hh[8 * u + 2 * e + 1] -= bf16_hi(ww[e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 64; ++e) {
-      const uint16_t bv = f32_to_bf16(hh[e]);
-      *HT.el16(c, a0 + e) = bv;
-      *HN.el16(a0 + e, c) = bv;
-    }
-  }
-  __syncthreads();
-  // phi(q): four threads per query row (32 features each); den = phi(q).Z_i + eps
-  {
-    const int qq = tid >> 2, a0 = 32 * (tid & 3);
-    const int tok = min(64 * i + qq, A.N - 1);
-    const uint16_t* qr = A.q + ((size_t)bh * A.N + tok) * kD + a0;
-    float x[32];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = bf16_to_f32(qr[e]);
-      mx = fmaxf(mx, x[e]);
-    }
-    mx = fmaxf(mx, dpp<0xB1>(mx));
-    mx = fmaxf(mx, dpp<0x4E>(mx));
-    float sm_ = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = __expf(x[e] - mx);
-      sm_ += x[e];
-    }
-    sm_ += dpp<0xB1>(sm_);
-    sm_ += dpp<0x4E>(sm_);
-    const float is = 1.f / sm_;
-    float dz = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float ph = x[e] * is;
-      dz = fmaf(ph, ZS[a0 + e], dz);
-      const uint16_t bv = f32_to_bf16(ph);
-      *PHQ.el16(qq, a0 + e) = bv;
-      *PHQT.el16(a0 + e, qq) = bv;
-    }
-    dz += dpp<0xB1>(dz);
-    dz += dpp<0x4E>(dz);
-    if ((tid & 3) == 0) {
-      denS[qq] = dz + A.eps;
-      mqS[qq] = mx;
-      isS[qq] = is;
-    }
-  }
-  __syncthreads();
-  // O_l, dalpha, dnum, dden.  With every block routed the linear branch is an empty sum: O_l
-  // and its gradients are 0 (the complement form would leave rounding amplified by 1/eps).
-  const bool lin = topk < T;
-  {
-    float alp[4][8], ddp[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ddp[rr] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-      num = mm<128>(PHQ, q0, HT, 16 * nt, l16, g, num);
-      const int c = 16 * nt + l16;
-      const float al = A.alpha[(size_t)hidx * kD + c];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int qq = q0 + 4 * g + rr;
-        const bool ok = qq < nq;
-        const float den = denS[qq];
-        const float ol = lin ? num[rr] / den : 0.f;
-        const float dO = ok ? bf16_to_f32(A.dout[((size_t)bh * A.N + 64 * i + qq) * kD + c]) : 0.f;
-        alp[rr][nt] = dO * (os[nt][rr] - ol);
-        const float dol = (1.f - al) * dO;
-        const float dn = lin ? dol / den : 0.f;
-        ddp[rr] = fmaf(-dol, ol, ddp[rr]);
-        const uint16_t bv = f32_to_bf16(dn);
-        *DNUM.el16(qq, c) = bv;
-        *DNUMT.el16(c, qq) = bv;
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float t = row16_sum(ddp[rr]);
-      if (l16 == 0) ddenS[q0 + 4 * g + rr] = t / denS[q0 + 4 * g + rr];
-    }
-    // dalpha partial of this wave: sum over its 16 queries, per feature
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const float t = rows4_sum(alp[0][nt] + alp[1][nt] + alp[2][nt] + alp[3][nt]);
-      if (g == 0) alS[w * kD + 16 * nt + l16] = t;
-    }
-  }
-  __syncthreads();
-  if (tid < kD)
-    A.dalpha_part[((size_t)bh * T + i) * kD + tid] = (alS[tid] + alS[kD + tid]) + (alS[2 * kD + tid] + alS[3 * kD + tid]);
-  // dphi(q) = dnum H_i^T + dden Z_i, then the softmax backward -> dq (linear part)
-  f32x4 dql[8];
-  {
-    float dphi[8][4], ph[8][4], dot_[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-      t = mm<128>(DNUM, q0, HN, 16 * nt, l16, g, t);
-      const int a = 16 * nt + l16;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int qq = q0 + 4 * g + rr;
-        const int tok = min(64 * i + qq, A.N - 1);
-        dphi[nt][rr] = t[rr] + ddenS[qq] * ZS[a];
-        ph[nt][rr] = __expf(bf16_to_f32(A.q[((size_t)bh * A.N + tok) * kD + a]) - mqS[qq]) * isS[qq];
-        dot_[rr] = fmaf(ph[nt][rr], dphi[nt][rr], dot_[rr]);
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) dot_[rr] = row16_sum(dot_[rr]);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dql[nt][rr] = ph[nt][rr] * (dphi[nt][rr] - dot_[rr]);
-  }
-  // dH_i = phi(q)^T dnum (wave w: rows a of tiles 2w, 2w+1), dZ_i = dden^T phi(q)
-  {
-    float* dHi = A.dH + ((size_t)bh * T + i) * kD * kD;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int a0 = 16 * (2 * w + mt);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-        t = mm<64>(PHQT, a0, DNUMT, 16 * nt, l16, g, t);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dHi[(size_t)(a0 + 4 * g + rr) * kD + 16 * nt + l16] = t[rr];
-      }
-    }
-    if (tid < kD) {
-      float zz = 0.f;
-      for (int qq = 0; qq < nq; ++qq) {
-        const float ph = __expf(bf16_to_f32(A.q[((size_t)bh * A.N + 64 * i + qq) * kD + tid]) - mqS[qq]) * isS[qq];
-        zz = fmaf(ddenS[qq], ph, zz);
-      }
-      A.dZ[((size_t)bh * T + i) * kD + tid] = zz;
-    }
-  }
-  __syncthreads();
+}
 
-  // ---------------- pass B: dQ' = dS K' / sqrt(d)
-  f32x4 dqs[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) dqs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < topk; ++r) {
-    const int j = lut[r];
-    const int nk = min(64, A.N - 64 * j);
-    stage<128>(KS, A.k8 + ((size_t)bh * T * 64 + 64 * j) * kD, kD, 64, 64, tid);
-    stage<256>(VS, reinterpret_cast<const uint8_t*>(A.v + ((size_t)bh * A.N + 64 * j) * kD), 2 * kD, 64, nk, tid);
-    stage<128>(KT, reinterpret_cast<const uint8_t*>(A.kt + ((size_t)bh * T + j) * kD * 64), 128, 128, 128, tid);
-    __syncthreads();
-    f32x4 P[4];
-    scores(j, P);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp = mm<128>(DOS, q0, VS, 16 * nt, l16, g, dp);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int qq = q0 + 4 * g + rr;
-        *PS.el16(qq, 16 * nt + l16) = f32_to_bf16(P[nt][rr] * (dp[rr] - dqS[qq]));
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) dqs[nt] = mm<64>(PS, q0, KT, 16 * nt, l16, g, dqs[nt]);
-    __syncthreads();
-  }
-
-  // dq = dQ' / sqrt(d) + dq (linear)
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int qq = q0 + 4 * g + rr;
-      if (qq < nq)
-        A.dq[((size_t)bh * A.N + 64 * i + qq) * kD + 16 * nt + l16] = f32_to_bf16(dqs[nt][rr] * inv_sqrt_d + dql[nt][rr]);
-    }
+// Entry x of a list held in a register (lane x holds entry x) when it has at most 64 entries,
+// else read from memory.
+__device__ __forceinline__ int list_entry(bool in_reg, int regv, const int32_t* mem, int x) {
+  return in_reg ? __builtin_amdgcn_readlane(regv, x) : __builtin_amdgcn_readfirstlane(mem[x]);
 }
 
 // ---------------------------------------------------------------------------------------
-// Key side.  Wave w owns keys 16w..16w+15 of block j (rows of every product below).
+// Query side.  One workgroup of four waves per (head, query block i); wave w owns queries
+// 16w..16w+15, one per lane column (l % 16).  Products are computed transposed so that each
+// lane holds one query and the pair's keys 16mt + 4g + r: S^T = K8 Q8^T, dP^T = V dO_s^T,
+// U^T = V dnum^T, then dQ'^T += K8^T dS^T and C^T += phi(K)^T U^T with dS^T and U^T packed
+// straight into B operands (keys at vt_pos, the order of the transposed tiles).
 // ---------------------------------------------------------------------------------------
-namespace klds {
-constexpr int KS = 0;                 // K8 rows of block j        64 x 128 B
-constexpr int VS = KS + 8192;         // V rows of block j         64 x 256 B
-constexpr int SMALL = VS + 16384;     // lse_i, Dq_i, dz_j, phi(k) max / inverse sums
-constexpr int U = SMALL + 4096;
-// sparse phase
-constexpr int QS = U;                 // Q8 rows of block i        64 x 128 B
-constexpr int DOS = QS + 8192;        // alpha * dO rows           64 x 256 B
-constexpr int QT = DOS + 16384;       // Q'^T                      128 x 128 B
-constexpr int DOT = QT + 16384;       // (alpha * dO)^T            128 x 128 B
-constexpr int PS = DOT + 16384;       // P^T [key][q]              64 x 128 B
-constexpr int DSS = PS + 8192;        // dS^T [key][q]             64 x 128 B
-// linear phase
-constexpr int DHN = U;                // dh_j [a][c]               128 x 256 B
-constexpr int DHT = DHN + 32768;      // dh_j^T [c][a]             128 x 256 B
-constexpr int PHK = DHT + 32768;      // phi(k) [key][a]           64 x 256 B
-constexpr int BYTES = PHK + 16384;
-static_assert(DSS + 8192 <= BYTES, "sparse phase fits the union");
-}  // namespace klds
+namespace qlds {
+constexpr int K8 = 0;                 // e4m3 rows of key block j       64 x 128 B
+constexpr int V = K8 + 8192;          // V rows                          64 x 256 B
+constexpr int KT = V + 16384;         // K8 values^T                     128 x 128 B
+constexpr int PT = KT + 16384;        // phi(K~)^T                       128 x 128 B
+constexpr int STAGE = PT + 16384;
+static_assert(STAGE >= 2 * kD * kD, "the H_tot image fits in a stage");
+}  // namespace qlds
 
-__global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sm[klds::BYTES];
-  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int k0 = 16 * w;
-  const int T = A.T;
-  float* lseS = reinterpret_cast<float*>(sm + klds::SMALL);
-  float* dqS = lseS + 64;
-  float* dzS = dqS + 64;      // 128
-  float* mkS = dzS + 128;     // 64
-  float* isS = mkS + 64;      // 64
-  const LTile<128> KS{sm + klds::KS}, QS{sm + klds::QS}, QT{sm + klds::QT}, DOT{sm + klds::DOT}, PS{sm + klds::PS},
-      DSS{sm + klds::DSS};
-  const LTile<256> VS{sm + klds::VS}, DOS{sm + klds::DOS}, DHN{sm + klds::DHN}, DHT{sm + klds::DHT},
-      PHK{sm + klds::PHK};
-  const float inv_sqrt_d = 1.f / sqrtf((float)kD);
-  const int nk = min(64, A.N - 64 * j);
-  const float ksc = A.k_scale[(size_t)bh * T + j];
-  const int cnt = A.inv_cnt[(size_t)bh * T + j];
-  const int32_t* inv = A.inv + ((size_t)bh * T + j) * T;
+struct QSrc {
+  __amdgpu_buffer_rsrc_t k8, v, kt, pt, him;
+};
 
-  stage<128>(KS, A.k8 + ((size_t)bh * T * 64 + 64 * j) * kD, kD, 64, 64, tid);
-  stage<256>(VS, reinterpret_cast<const uint8_t*>(A.v + ((size_t)bh * A.N + 64 * j) * kD), 2 * kD, 64, nk, tid);
+// key block j's tiles into a stage: 14 16-byte copies per thread
+__device__ __forceinline__ void q_dma(const QSrc& s, int j, int N, int tid, uint8_t* st) {
+  const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_for<2>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+    lds_dma(s.k8, st + qlds::K8 + 4096 * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * 8192);
+  });
+  static_for<4>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 4, pc = qd & 15;
+    const int tok = min(kBlock * j + row, N - 1);   // rows past N: a finite row, masked later
+    lds_dma(s.v, st + qlds::V + 4096 * P + wofs, tok * 256 + 16 * (pc ^ (row & 15)), 0);
+  });
+  static_for<4>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+    const int vo = row * 128 + 16 * (pc ^ (row & 7));
+    lds_dma(s.kt, st + qlds::KT + 4096 * P + wofs, vo, j * kTTile);
+    lds_dma(s.pt, st + qlds::PT + 4096 * P + wofs, vo, j * kTTile);
+  });
+}
 
-  f32x4 dv[8], dk[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    dv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+// the 32 KB image of H_tot (rows a) into a stage
+__device__ __forceinline__ void q_dma_himage(const QSrc& s, int tid, uint8_t* st) {
+  const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_for<8>([&](auto P) { lds_dma(s.him, st + 4096 * P + wofs, 16 * (tid + kNT * P), 0); });
+}
+
+struct QState {
+  f32x4 dqa[8];   // dQ'^T: features 16ct + 4g + r of this lane's query (scales folded in)
+  f32x4 cra[8];   // C^T = sum over routed pairs of phi(K)^T U^T, same layout
+};
+
+struct QOps {
+  i32x8 q8;       // e4m3 codes of features 32g..32g+31
+  bf16x8 dso[4];  // alpha dO, features 32s + 8g + e
+  bf16x8 dno[4];  // dnum = (1 - alpha) dO / den, same features
+  float lse_l;    // lse * log2(e)
+  float dq_l;     // D_q
+};
+
+// One routed pair: key block j = LUT entry r in stage STG, K scale ksc.  The next block's tiles
+// (after the last, the H_tot image) are copied into the other stage meanwhile.
+template <int STG>
+__device__ __forceinline__ void q_iteration(const BwdArgs& A, QState& st, uint8_t* smem0, uint8_t* smem1,
+                                            const QSrc& src, bool lut_reg, int lutv, const int32_t* lutG,
+                                            int r, int topk, int bh, float sq, float& ksc, const QOps& qo,
+                                            int nvalid, int l16, int g, int tid) {
+  const uint8_t* stg = STG == 0 ? smem0 : smem1;
+  uint8_t* next = STG == 0 ? smem1 : smem0;
+  float ksc_next = 1.f;
+  if (r + 1 < topk) {
+    const int jn = list_entry(lut_reg, lutv, lutG, r + 1);
+    ksc_next = A.k_scale[(size_t)bh * A.T + jn];
+    q_dma(src, jn, A.N, tid, next);
+  } else {
+    q_dma_himage(src, tid, next);
   }
-  for (int x = 0; x < cnt; ++x) {
-    const int i = inv[x];
-    const int nq = min(64, A.N - 64 * i);
-    __syncthreads();   // the previous block's tiles are consumed
-    stage<128>(QS, A.q8 + ((size_t)bh * T * 64 + 64 * i) * kD, kD, 64, 64, tid);
-    stage<256>(DOS, reinterpret_cast<const uint8_t*>(A.dos + ((size_t)bh * T * 64 + 64 * i) * kD), 2 * kD, 64, 64, tid);
-    stage<128>(QT, reinterpret_cast<const uint8_t*>(A.qt + ((size_t)bh * T + i) * kD * 64), 128, 128, 128, tid);
-    stage<128>(DOT, reinterpret_cast<const uint8_t*>(A.dot + ((size_t)bh * T + i) * kD * 64), 128, 128, 128, tid);
-    if (tid < 64) {
-      lseS[tid] = tid < nq ? A.lse[(size_t)bh * A.N + 64 * i + tid] : 0.f;
-      dqS[tid] = tid < nq ? A.dsum[(size_t)bh * T * 64 + 64 * i + tid] : 0.f;
-    }
-    __syncthreads();
-    const float cij = kLog2e * inv_sqrt_d * ksc * A.q_scale[(size_t)bh * T + i];
+  __builtin_amdgcn_sched_barrier(0);
+
+  const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
+  f32x4 S[4], dP[4], U[4];
+  static_for<4>([&](auto mt) {
+    S[mt] = mfma_fp8(lds_fp8_row(stg + qlds::K8, 16 * mt + l16, g), qo.q8, f32x4{0.f, 0.f, 0.f, 0.f});
+    dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 s = mfma_fp8(KS.op8(k0 + l16, g), QS.op8(16 * nt + l16, g), f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp = mm<128>(VS, k0, DOS, 16 * nt, l16, g, dp);
-      const int qq = 16 * nt + l16;
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 a = op256(stg + qlds::V, 16 * mt + l16, s, g);
+      dP[mt] = mfma_bf16(a, qo.dso[s], dP[mt]);
+      U[mt] = mfma_bf16(a, qo.dno[s], U[mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // P^T and dS^T (times k_scale / sqrt(d), the factor of dQ' = dS K' / sqrt(d)) as B operands
+  const float cj = kLog2e * inv_sqrt_d * sq * ksc, fs = ksc * inv_sqrt_d;
+  bf16x8 dso_[2], uo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float dv8[8], uv8[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + 4 * g + rr;
-        const bool ok = qq < nq && key < nk;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[rr] * cij - lseS[qq] * kLog2e) : 0.f;
-        *PS.el16(key, qq) = f32_to_bf16(p);
-        *DSS.el16(key, qq) = f32_to_bf16(p * (dp[rr] - dqS[qq]));
+        const int mt = 2 * s + h, key = 16 * mt + 4 * g + rr;
+        float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
+        if (key >= nvalid) p = 0.f;
+        dv8[4 * h + rr] = p * (dP[mt][rr] - qo.dq_l) * fs;
+        uv8[4 * h + rr] = U[mt][rr];
       }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      dv[nt] = mm<64>(PS, k0, DOT, 16 * nt, l16, g, dv[nt]);
-      dk[nt] = mm<64>(DSS, k0, QT, 16 * nt, l16, g, dk[nt]);
-    }
+    dso_[s] = pack8(dv8);
+    uo[s] = pack8(uv8);
   }
-  __syncthreads();
 
-  // ---------------- linear branch
-  // dh_j = dH_tot - sum of dH_i over the query blocks routing to j; dz_j likewise
-  {
-    const int a = tid >> 1, c0 = 64 * (tid & 1);
-    float dd[64];
-    const float* tot = A.dH_tot + (size_t)bh * kD * kD + a * kD + c0;
+  static_for<8>([&](auto ct) {
 #pragma unroll
-    for (int e = 0; e < 64; ++e) dd[e] = tot[e];
-    for (int x = 0; x < cnt; ++x) {
-      const f32x4* di = reinterpret_cast<const f32x4*>(A.dH + (((size_t)bh * T + inv[x]) * kD + a) * kD + c0);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const f32x4 t = di[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dd[4 * u + e] -= t[e];
-      }
+    for (int s = 0; s < 2; ++s) {
+      st.dqa[ct] = mfma_bf16(op128(stg + qlds::KT, 16 * ct + l16, s, g), dso_[s], st.dqa[ct]);
+      st.cra[ct] = mfma_bf16(op128(stg + qlds::PT, 16 * ct + l16, s, g), uo[s], st.cra[ct]);
     }
-#pragma unroll
-    for (int e = 0; e < 64; ++e) {
-      const uint16_t bv = f32_to_bf16(dd[e]);
-      *DHN.el16(a, c0 + e) = bv;
-      *DHT.el16(c0 + e, a) = bv;
-    }
-  }
-  if (tid < kD) {
-    float zz = A.dZ_tot[(size_t)bh * kD + tid];
-    for (int x = 0; x < cnt; ++x) zz -= A.dZ[((size_t)bh * T + inv[x]) * kD + tid];
-    dzS[tid] = zz;
-  }
-  // phi(k~): four threads per key row
-  const float* mu = A.k_mean + (size_t)bh * kD;
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  wait_dma();
+  lds_barrier();
+  ksc = ksc_next;
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[qlds::STAGE];   // stage of even LUT entries
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[qlds::STAGE];   // stage of odd LUT entries
+  __shared__ float zS[kD];                                                // Z_i
+  const int lid = xcd_remap(blockIdx.x, A.nblocks);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / A.T), i = __builtin_amdgcn_readfirstlane(lid % A.T);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int hidx = bh % A.H, T = A.T, N = A.N, topk = A.topk;
+  const int qq = kBlock * i + 16 * w + l16;   // this lane's query
+  const bool qok = qq < N;
+  const int32_t* lutG = A.lut + ((size_t)bh * T + i) * topk;
+  const bool lut_reg = topk <= 64;
+  const int lutv = (lut_reg && lane < topk) ? lutG[lane] : 0;
+
+  QSrc src;
+  src.k8 = rsrc(A.k8 + (size_t)bh * T * kBlock * kD, (size_t)T * kBlock * kD);
+  src.v = rsrc(A.v + (size_t)bh * N * kD, (size_t)N * kD * 2);
+  src.kt = rsrc(A.k8t + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.pt = rsrc(A.phkt + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.him = rsrc(A.htimg + (size_t)bh * kD * kD, (size_t)kD * kD * 2);
+  const int j0 = __builtin_amdgcn_readfirstlane(lutG[0]);
+  float ksc = A.k_scale[(size_t)bh * T + j0];
+  q_dma(src, j0, N, tid, smem0);
+
+  QOps qo;
   {
-    const int kk = tid >> 2, a0 = 32 * (tid & 3);
-    const int tok = min(64 * j + kk, A.N - 1);
-    const uint16_t* kr = A.k + ((size_t)bh * A.N + tok) * kD + a0;
-    float x[32];
+    const uint8_t* s8 = A.q8 + ((size_t)bh * T * kBlock + qq) * kD + 32 * g;   // pad rows: code 0
+    const u32x4 a = *reinterpret_cast<const u32x4*>(s8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
+    qo.q8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+  const float invd = qok ? A.inv_den[(size_t)bh * T * kBlock + qq] : 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = 32 * s + 8 * g;
+    const u32x4 raw = qok ? *reinterpret_cast<const u32x4*>(A.dout + ((size_t)bh * N + qq) * kD + c) : u32x4{0, 0, 0, 0};
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(A.alpha + (size_t)hidx * kD + c);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(A.alpha + (size_t)hidx * kD + c + 4);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    float d8[8], n8[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_lo(rw[e]), hi = bf16_hi(rw[e]);
+      d8[2 * e] = av[2 * e] * lo;
+      d8[2 * e + 1] = av[2 * e + 1] * hi;
+      n8[2 * e] = (1.f - av[2 * e]) * lo * invd;
+      n8[2 * e + 1] = (1.f - av[2 * e + 1]) * hi * invd;
+    }
+    qo.dso[s] = pack8(d8);
+    qo.dno[s] = pack8(n8);
+  }
+  qo.lse_l = qok ? A.lse[(size_t)bh * N + qq] * kLog2e : 0.f;
+  qo.dq_l = A.qrec[((size_t)bh * T + i) * kRec + kBlock + 16 * w + l16];
+  const float dden_l = A.dden[(size_t)bh * T * kBlock + qq];
+  const float sq = A.q_scale[(size_t)bh * T + i];
+  if (tid < kD) zS[tid] = A.z_sum[(size_t)bh * kD + tid] - A.zrout[((size_t)bh * T + i) * kD + tid];
+  // only block T-1 can be partial, and only as the last LUT entry (rows are ascending)
+  const int nlast = N - kBlock * (T - 1);
+  const bool last_partial = list_entry(lut_reg, lutv, lutG, topk - 1) == T - 1 && nlast < kBlock;
+
+  QState st;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    st.dqa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.cra[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  wait_dma();
+  lds_barrier();
+
+  for (int r = 0; r < topk; r += 2) {
+    q_iteration<0>(A, st, smem0, smem1, src, lut_reg, lutv, lutG, r, topk, bh, sq, ksc, qo,
+                   (last_partial && r == topk - 1) ? nlast : kBlock, l16, g, tid);
+    if (r + 1 < topk)
+      q_iteration<1>(A, st, smem0, smem1, src, lut_reg, lutv, lutG, r + 1, topk, bh, sq, ksc, qo,
+                     (last_partial && r + 1 == topk - 1) ? nlast : kBlock, l16, g, tid);
+  }
+
+  // ---------------- epilogue: the H_tot image is in the stage after the last tile's
+  const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
+  // phi(q) at features a = 16at + 4g + r (the layout of the accumulators)
+  float ph[8][4];
+  {
+    const uint16_t* qr = A.q + ((size_t)bh * N + min(qq, N - 1)) * kD + 4 * g;
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = bf16_to_f32(kr[e]) - mu[a0 + e];
-      mx = fmaxf(mx, x[e]);
-    }
-    mx = fmaxf(mx, dpp<0xB1>(mx));
-    mx = fmaxf(mx, dpp<0x4E>(mx));
-    float s = 0.f;
+    for (int at = 0; at < 8; ++at) {
+      const u32x2 wv = *reinterpret_cast<const u32x2*>(qr + 16 * at);
+      ph[at][0] = bf16_lo(wv.x);
+      ph[at][1] = bf16_hi(wv.x);
+      ph[at][2] = bf16_lo(wv.y);
+      ph[at][3] = bf16_hi(wv.y);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = __expf(x[e] - mx);
-      s += x[e];
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, ph[at][r]);
     }
-    s += dpp<0xB1>(s);
-    s += dpp<0x4E>(s);
-    const float is = 1.f / s;
+    mx = rows4_max(mx);
+    float sm = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) *PHK.el16(kk, a0 + e) = f32_to_bf16(kk < nk ? x[e] * is : 0.f);
-    if ((tid & 3) == 0) {
-      mkS[kk] = mx;
-      isS[kk] = is;
+    for (int at = 0; at < 8; ++at)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ph[at][r] = __expf(ph[at][r] - mx);
+        sm += ph[at][r];
+      }
+    const float is = 1.f / rows4_sum(sm);
+#pragma unroll
+    for (int at = 0; at < 8; ++at)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[at][r] *= is;
+  }
+  // dphi(q)^T = H_tot dnum^T - C^T + Z_i dden, then the softmax backward
+  float dphi[8][4], dotp = 0.f;
+#pragma unroll
+  for (int at = 0; at < 8; ++at) {
+    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t = mfma_bf16(op256(Hs, 16 * at + l16, s, g), qo.dno[s], t);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dphi[at][r] = t[r] - st.cra[at][r] + zS[16 * at + 4 * g + r] * dden_l;
+      dotp = fmaf(ph[at][r], dphi[at][r], dotp);
     }
   }
-  __syncthreads();
-  // dphi(k) = V dh_j^T + dz_j -> dk~ (linear part); dV += phi(k) dh_j
-  float dkl[8][4];
-  {
-    float dphi[8][4], ph[8][4], dot_[4] = {0.f, 0.f, 0.f, 0.f};
+  dotp = rows4_sum(dotp);
+  if (qok) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-      t = mm<128>(VS, k0, DHN, 16 * nt, l16, g, t);
-      dv[nt] = mm<128>(PHK, k0, DHT, 16 * nt, l16, g, dv[nt]);
-      const int a = 16 * nt + l16;
+    for (int ct = 0; ct < 8; ++ct) {
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = st.dqa[ct][r] + ph[ct][r] * (dphi[ct][r] - dotp);
+      u32x2 sv;
+      sv.x = pack_bf16x2(o[0], o[1]);
+      sv.y = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<u32x2*>(A.dq + ((size_t)bh * N + qq) * kD + 16 * ct + 4 * g) = sv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Key side.  One workgroup of four waves per (head, key block j); wave w owns keys
+// 16w..16w+15, one per lane column.  Per routing query block i: S = Q8 K8^T, dP = dO_s V^T,
+// dV^T += dO^T P, dK'^T += Q8^T dS (queries at vt_pos), and C[a][c] += (phi(q)/den)^T dO over
+// the wave's rows a = 32w..32w+31, sharing the dO^T operands of the dV product.
+// ---------------------------------------------------------------------------------------
+namespace klds {
+constexpr int Q8 = 0;                 // e4m3 rows of query block i      64 x 128 B
+constexpr int DOS = Q8 + 8192;        // alpha dO rows                    64 x 256 B
+constexpr int DOT = DOS + 16384;      // dO^T                             128 x 128 B
+constexpr int QT = DOT + 16384;       // Q8 values^T                      128 x 128 B
+constexpr int PT = QT + 16384;        // (phi(q)/den)^T                   128 x 128 B
+constexpr int REC = PT + 16384;       // lse[64], D_q[64], zeros          1 KB
+constexpr int STAGE = REC + 1024;
+static_assert(STAGE >= 2 * 2 * kD * kD, "the two dh_j images fit in a stage");
+}  // namespace klds
+
+struct KSrc {
+  __amdgpu_buffer_rsrc_t q8, dos, dot, qt, pt, rec;
+};
+
+// query block i's tiles into a stage: 18 16-byte copies per thread (19 in wave 0)
+__device__ __forceinline__ void k_dma(const KSrc& s, int i, int tid, uint8_t* st) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wofs = 1024 * w;
+  static_for<2>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+    lds_dma(s.q8, st + klds::Q8 + 4096 * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), i * 8192);
+  });
+  static_for<4>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 4, pc = qd & 15;
+    lds_dma(s.dos, st + klds::DOS + 4096 * P + wofs, row * 256 + 16 * (pc ^ (row & 15)), i * 16384);
+  });
+  static_for<4>([&](auto P) {
+    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+    const int vo = row * 128 + 16 * (pc ^ (row & 7));
+    lds_dma(s.dot, st + klds::DOT + 4096 * P + wofs, vo, i * kTTile);
+    lds_dma(s.qt, st + klds::QT + 4096 * P + wofs, vo, i * kTTile);
+    lds_dma(s.pt, st + klds::PT + 4096 * P + wofs, vo, i * kTTile);
+  });
+  if (w == 0) lds_dma(s.rec, st + klds::REC, 16 * (tid & 63), i * (kRec * 4));
+}
+
+struct KState {
+  f32x4 dva[8];      // dV^T: features 16ct + 4g + r of this lane's key (alpha applied after)
+  f32x4 dka[8];      // dK'^T (scales folded in)
+  f32x4 cra[2][8];   // C[a][c], a = 32w + 16at + 4g + r, c = 16ct + l%16
+  float dz;          // threads < 128: sum of dZ_i over the routing query blocks, feature tid
+};
+
+struct KOps {
+  i32x8 k8;          // e4m3 codes of features 32g..32g+31 of this lane's key
+  bf16x8 v[4];       // V of this lane's key, features 32s + 8g + e
+};
+
+template <int STG>
+__device__ __forceinline__ void k_iteration(const BwdArgs& A, KState& st, uint8_t* smem0, uint8_t* smem1,
+                                            const KSrc& src, bool inv_reg, int invv, const int32_t* invG,
+                                            int x, int cnt, int bh, float ksc, int& i, float& sq,
+                                            const KOps& ko, bool kok, int w, int l16, int g, int tid) {
+  const uint8_t* stg = STG == 0 ? smem0 : smem1;
+  uint8_t* next = STG == 0 ? smem1 : smem0;
+  // dZ_i is loaded before the copies are issued: waiting for it then never waits for them
+  const float dzi = tid < kD ? A.dZ[((size_t)bh * A.T + i) * kD + tid] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+  int i_next = 0;
+  float sq_next = 1.f;
+  if (x + 1 < cnt) {
+    i_next = list_entry(inv_reg, invv, invG, x + 1);
+    sq_next = A.q_scale[(size_t)bh * A.T + i_next];
+    k_dma(src, i_next, tid, next);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
+  const int nq = min(kBlock, A.N - kBlock * i);
+  f32x4 S[4], dP[4];
+  static_for<4>([&](auto mt) {
+    S[mt] = mfma_fp8(lds_fp8_row(stg + klds::Q8, 16 * mt + l16, g), ko.k8, f32x4{0.f, 0.f, 0.f, 0.f});
+    dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dP[mt] = mfma_bf16(op256(stg + klds::DOS, 16 * mt + l16, s, g), ko.v[s], dP[mt]);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // P and dS (times q_scale / sqrt(d), the factor of dK' = dS^T Q' / sqrt(d)) as B operands
+  const float cij = kLog2e * inv_sqrt_d * sq * ksc, fk = sq * inv_sqrt_d;
+  const float* rec = reinterpret_cast<const float*>(stg + klds::REC);
+  bf16x8 po[2], dso_[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float p8[8], d8[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q0 = 16 * (2 * s + h) + 4 * g;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(rec + q0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(rec + kBlock + q0);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int kk = k0 + 4 * g + rr;
-        const int tok = min(64 * j + kk, A.N - 1);
-        dphi[nt][rr] = t[rr] + dzS[a];
-        ph[nt][rr] = __expf(bf16_to_f32(A.k[((size_t)bh * A.N + tok) * kD + a]) - mu[a] - mkS[kk]) * isS[kk];
-        dot_[rr] = fmaf(ph[nt][rr], dphi[nt][rr], dot_[rr]);
+        float p = __builtin_amdgcn_exp2f(fmaf(S[2 * s + h][rr], cij, -l4[rr] * kLog2e));
+        if (q0 + rr >= nq || !kok) p = 0.f;
+        p8[4 * h + rr] = p;
+        d8[4 * h + rr] = p * (dP[2 * s + h][rr] - d4[rr]) * fk;
       }
     }
+    po[s] = pack8(p8);
+    dso_[s] = pack8(d8);
+  }
+
+  bf16x8 fa[2][2];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) dot_[rr] = row16_sum(dot_[rr]);
+  for (int at = 0; at < 2; ++at)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int s = 0; s < 2; ++s) fa[at][s] = op128(stg + klds::PT, 32 * w + 16 * at + l16, s, g);
+  static_for<8>([&](auto ct) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) dkl[nt][rr] = ph[nt][rr] * (dphi[nt][rr] - dot_[rr]);
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 fo = op128(stg + klds::DOT, 16 * ct + l16, s, g);
+      st.dva[ct] = mfma_bf16(fo, po[s], st.dva[ct]);
+      st.dka[ct] = mfma_bf16(op128(stg + klds::QT, 16 * ct + l16, s, g), dso_[s], st.dka[ct]);
+      st.cra[0][ct] = mfma_bf16(fa[0][s], fo, st.cra[0][ct]);
+      st.cra[1][ct] = mfma_bf16(fa[1][s], fo, st.cra[1][ct]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  st.dz += dzi;
+  wait_dma();
+  lds_barrier();
+  i = i_next;
+  sq = sq_next;
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[klds::STAGE];   // stage of even list entries
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[klds::STAGE];   // stage of odd list entries
+  __shared__ float dzS[kD], alS[kD];
+  const int lid = xcd_remap(blockIdx.x, A.nblocks);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / A.T), j = __builtin_amdgcn_readfirstlane(lid % A.T);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int hidx = bh % A.H, T = A.T, N = A.N;
+  const int kk = kBlock * j + 16 * w + l16;   // this lane's key
+  const bool kok = kk < N;
+  const int cnt = __builtin_amdgcn_readfirstlane(A.inv_cnt[(size_t)bh * T + j]);
+  const int32_t* invG = A.inv + ((size_t)bh * T + j) * T;
+  const bool inv_reg = cnt <= 64;
+  const int invv = (inv_reg && lane < cnt) ? invG[lane] : 0;
+
+  KSrc src;
+  src.q8 = rsrc(A.q8 + (size_t)bh * T * kBlock * kD, (size_t)T * kBlock * kD);
+  src.dos = rsrc(A.dos + (size_t)bh * T * kBlock * kD, (size_t)T * kBlock * kD * 2);
+  src.dot = rsrc(A.dot + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.qt = rsrc(A.q8t + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.pt = rsrc(A.phqdt + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.rec = rsrc(A.qrec + (size_t)bh * T * kRec, (size_t)T * kRec * 4);
+  int i = 0;
+  float sq = 1.f;
+  if (cnt > 0) {
+    i = list_entry(inv_reg, invv, invG, 0);
+    sq = A.q_scale[(size_t)bh * T + i];
+    k_dma(src, i, tid, smem0);
+  }
+
+  KOps ko;
+  {
+    const uint8_t* s8 = A.k8 + ((size_t)bh * T * kBlock + kk) * kD + 32 * g;   // pad rows: code 0
+    const u32x4 a = *reinterpret_cast<const u32x4*>(s8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
+    ko.k8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
   }
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
+  for (int s = 0; s < 4; ++s)
+    ko.v[s] = __builtin_bit_cast(bf16x8, kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + 32 * s + 8 * g)
+                                             : u32x4{0, 0, 0, 0});
+  const float ksc = A.k_scale[(size_t)bh * T + j];
+  if (tid < kD) alS[tid] = A.alpha[(size_t)hidx * kD + tid];
+
+  KState st;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int kk = k0 + 4 * g + rr, c = 16 * nt + l16;
-      if (kk < nk) {
-        A.dv[((size_t)bh * A.N + 64 * j + kk) * kD + c] = f32_to_bf16(dv[nt][rr]);
-        A.dkt[((size_t)bh * T * 64 + 64 * j + kk) * kD + c] = dk[nt][rr] * inv_sqrt_d + dkl[nt][rr];
+  for (int ct = 0; ct < 8; ++ct) {
+    st.dva[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.dka[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.cra[0][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.cra[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  st.dz = 0.f;
+  wait_dma();
+  lds_barrier();
+
+  for (int x = 0; x < cnt; x += 2) {
+    k_iteration<0>(A, st, smem0, smem1, src, inv_reg, invv, invG, x, cnt, bh, ksc, i, sq, ko, kok, w, l16, g, tid);
+    if (x + 1 < cnt)
+      k_iteration<1>(A, st, smem0, smem1, src, inv_reg, invv, invG, x + 1, cnt, bh, ksc, i, sq, ko, kok, w, l16, g,
+                     tid);
+  }
+
+  // ---------------- epilogue
+  // dh_j = (G_tot - C) diag(1 - alpha) as bf16 images with rows a and rows c; dz_j
+  if (tid < kD) dzS[tid] = A.dZ_tot[(size_t)bh * kD + tid] - st.dz;
+  const LTile<256> DH{smem0}, DHT{smem0 + 2 * kD * kD};
+  {
+    const float* gt = A.g_tot + (size_t)bh * kD * kD;
+#pragma unroll
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = 32 * w + 16 * at + 4 * g + r, c = 16 * ct + l16;
+          const uint16_t bv = f32_to_bf16((gt[a * kD + c] - st.cra[at][ct][r]) * (1.f - alS[c]));
+          *DH.el16(a, c) = bv;
+          *DHT.el16(c, a) = bv;
+        }
+  }
+  __syncthreads();
+
+  // phi(k~) of this lane's key: as B operand (features 32s + 8g + e) and at the accumulator
+  // features 16at + 4g + r
+  bf16x8 pko[4];
+  float pk[8][4];
+  {
+    const uint16_t* kr = A.k + ((size_t)bh * N + min(kk, N - 1)) * kD;
+    const float* mu = A.k_mean + (size_t)bh * kD;
+    float fb[4][8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fb[s][2 * e] = bf16_lo(ww[e]) - mu[32 * s + 8 * g + 2 * e];
+        fb[s][2 * e + 1] = bf16_hi(ww[e]) - mu[32 * s + 8 * g + 2 * e + 1];
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fb[s][e]);
     }
+    mx = rows4_max(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        fb[s][e] = __expf(fb[s][e] - mx);
+        sm += fb[s][e];
+      }
+    const float rsum = 1.f / rows4_sum(sm);
+    const float is = kok ? rsum : 0.f;   // pad keys: phi(k) = 0
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fb[s][e] *= is;
+      pko[s] = pack8(fb[s]);
+    }
+#pragma unroll
+    for (int at = 0; at < 8; ++at) {
+      const u32x2 wv = *reinterpret_cast<const u32x2*>(kr + 16 * at + 4 * g);
+      const float raw[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pk[at][r] = __expf(raw[r] - mu[16 * at + 4 * g + r] - mx) * is;
+    }
+  }
+  // dphi(k)^T = dh_j V^T + dz_j; dV^T = alpha dV_sparse^T + dh_j^T phi(k)^T
+  float dphi[8][4], dotp = 0.f;
+#pragma unroll
+  for (int at = 0; at < 8; ++at) {
+    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), ko.v[s], t);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dphi[at][r] = t[r] + dzS[16 * at + 4 * g + r];
+      dotp = fmaf(pk[at][r], dphi[at][r], dotp);
+    }
+  }
+  dotp = rows4_sum(dotp);
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.dva[ct][r] *= alS[16 * ct + 4 * g + r];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st.dva[ct] = mfma_bf16(DHT.op(16 * ct + l16, 32 * s + 8 * g), pko[s], st.dva[ct]);
+  }
+  if (kok) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = st.dka[ct][r] + pk[ct][r] * (dphi[ct][r] - dotp);
+      *reinterpret_cast<f32x4*>(A.dkt + ((size_t)bh * T * kBlock + kk) * kD + 16 * ct + 4 * g) = o;
+      u32x2 sv;
+      sv.x = pack_bf16x2(st.dva[ct][0], st.dva[ct][1]);
+      sv.y = pack_bf16x2(st.dva[ct][2], st.dva[ct][3]);
+      *reinterpret_cast<u32x2*>(A.dv + ((size_t)bh * N + kk) * kD + 16 * ct + 4 * g) = sv;
+    }
+  }
 }
 
 // Column sums of dK~ over chunks of 256 tokens, then per head: mean over the N tokens.
@@ -767,8 +1012,9 @@ __global__ __launch_bounds__(1024) void bwd_dalpha_kernel(BwdArgs A) {
 }  // namespace
 
 size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
-  const size_t BH = g.BH, T = g.T, D = g.D;
+  const size_t BH = g.BH, T = g.T, D = g.D, N = g.N;
   const size_t nch = (g.N + 255) / 256;
+  const size_t pg = (g.T + kGChunk - 1) / kGChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -776,16 +1022,24 @@ size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
     return base ? base + o : nullptr;
   };
   BwdWorkspace w;
+  w.os = (uint16_t*)take(BH * N * D * 2);
+  w.ol = (uint16_t*)take(BH * N * D * 2);
+  w.inv_den = (float*)take(BH * T * 64 * 4);
   w.dos = (uint16_t*)take(BH * T * 64 * D * 2);
   w.dot = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.qt = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.kt = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.q8t = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.phqdt = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.k8t = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.phkt = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.htimg = (uint16_t*)take(BH * D * D * 2);
+  w.qrec = (float*)take(BH * T * kRec * 4);
+  w.dden = (float*)take(BH * T * 64 * 4);
   w.inv = (int32_t*)take(BH * T * T * 4);
   w.inv_cnt = (int32_t*)take(BH * T * 4);
-  w.dsum = (float*)take(BH * T * 64 * 4);
-  w.dH = (float*)take(BH * T * D * D * 4);
   w.dZ = (float*)take(BH * T * D * 4);
-  w.dH_tot = (float*)take(BH * D * D * 4);
+  w.gpart = (float*)take(BH * pg * D * D * 4);
+  w.zpart = (float*)take(BH * pg * D * 4);
+  w.g_tot = (float*)take(BH * D * D * 4);
   w.dZ_tot = (float*)take(BH * D * 4);
   w.dalpha_part = (float*)take(BH * T * D * 4);
   w.dkt = (float*)take(BH * T * 64 * D * 4);
@@ -811,21 +1065,27 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   A.lse = t.lse;
   A.lut = t.lut;
   A.mask = t.mask;
-  A.h = (const uint16_t*)t.h;
-  A.z = t.z;
   A.h_sum = t.h_sum;
   A.z_sum = t.z_sum;
-  A.vt = ws.vt;
+  A.zrout = ws.zrout;
+  A.os = bw.os;
+  A.ol = bw.ol;
+  A.inv_den = bw.inv_den;
   A.dos = bw.dos;
   A.dot = bw.dot;
-  A.qt = bw.qt;
-  A.kt = bw.kt;
+  A.q8t = bw.q8t;
+  A.phqdt = bw.phqdt;
+  A.k8t = bw.k8t;
+  A.phkt = bw.phkt;
+  A.htimg = bw.htimg;
+  A.qrec = bw.qrec;
+  A.dden = bw.dden;
   A.inv = bw.inv;
   A.inv_cnt = bw.inv_cnt;
-  A.dsum = bw.dsum;
-  A.dH = bw.dH;
   A.dZ = bw.dZ;
-  A.dH_tot = bw.dH_tot;
+  A.gpart = bw.gpart;
+  A.zpart = bw.zpart;
+  A.g_tot = bw.g_tot;
   A.dZ_tot = bw.dZ_tot;
   A.dalpha_part = bw.dalpha_part;
   A.dkt = bw.dkt;
@@ -841,15 +1101,17 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   A.T = g.T;
   A.topk = g.topk;
   A.nch = (g.N + 255) / 256;
-  A.eps = g.eps;
+  A.pg = (g.T + kGChunk - 1) / kGChunk;
+  A.nblocks = g.BH * g.T;
   A.smooth_k = g.smooth_k ? 1 : 0;
   const dim3 blocks(g.T, g.BH);
   hipLaunchKernelGGL(bwd_prep_kernel, blocks, dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_invlut_kernel, blocks, dim3(64), 0, s, A);
-  hipLaunchKernelGGL(bwd_query_kernel, blocks, dim3(256), 0, s, A);
-  hipError_t e = launch_sum_parts(bw.dH, bw.dZ, g.T, g.D, g.BH, bw.dH_tot, bw.dZ_tot, s);
+  hipLaunchKernelGGL(bwd_gtot_kernel, dim3(A.pg, g.BH), dim3(256), 0, s, A);
+  hipError_t e = launch_sum_parts(bw.gpart, bw.zpart, A.pg, g.D, g.BH, bw.g_tot, bw.dZ_tot, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_key_kernel, blocks, dim3(256), 0, s, A);
+  hipLaunchKernelGGL(bwd_query_kernel, dim3(A.nblocks), dim3(256), 0, s, A);
+  hipLaunchKernelGGL(bwd_key_kernel, dim3(A.nblocks), dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_colsum_kernel, dim3(A.nch, g.BH), dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_mean_kernel, dim3(g.BH), dim3(128), 0, s, A);
   hipLaunchKernelGGL(bwd_dk_kernel, dim3((g.N * 16 + 255) / 256, g.BH), dim3(256), 0, s, A);

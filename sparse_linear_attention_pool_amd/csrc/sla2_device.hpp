@@ -123,6 +123,39 @@ __device__ __forceinline__ float wave_sum(float v) {
   return rows4_sum(row16_sum(v));
 }
 
+// ---------------------------------------------------------------- LDS staging
+// Barrier for LDS hand-offs inside a loop over staged tiles: this wave's LDS writes are retired,
+// then all waves meet.  Unlike __syncthreads() it does not drain the vector-memory loads in
+// flight (the prefetched tile), which the compiler waits for where they are used.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 0xF | (3 << 14));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Tiles move from memory straight into LDS (buffer loads with the LDS destination): lane l
+// of a wave writes the 16 bytes at its wave's LDS pointer + 16 l, so each thread loads the
+// chunk that belongs at its LDS slot.  A swizzle of the LDS rows (chunk c of row r at
+// position c ^ (r & 7), or c ^ (r & 15) for 256-byte rows) is applied to the memory address
+// instead.  Callers keep every read inside the buffer.
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// All of this wave's tile copies have landed in LDS (they count as vector-memory loads).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
+
+// 32 e4m3 codes of one 128-byte LDS row (logical chunks 2g and 2g+1): the A operand of a
+// 16x16x128 matrix-core product for row `row`.
+__device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g) {
+  const uint8_t* r = base + row * 128;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g) ^ (row & 7)));
+  const u32x4 b = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g + 1) ^ (row & 7)));
+  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
 // ---------------------------------------------------------------- launch order
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup id w runs on XCD w % 8).
 // Returns a logical id such that consecutive logical ids run on the same XCD, so that

@@ -41,6 +41,9 @@ struct FwdArgs {
   const float* k_mean;    // [BH, D] (lse of the native mode is shifted to the smoothed keys)
   uint16_t* o;            // [BH, N, D]
   float* lse;             // [BH, N] or null
+  uint16_t* os;           // [BH, N, D] O_s for the backward pass, or null (then ol, inv_den too)
+  uint16_t* ol;           // [BH, N, D] O_l
+  float* inv_den;         // [BH, 64T] 1 / (phi(q).Z_i + eps)
   int N, T, H, topk, nblocks;
   float eps;
 };
@@ -64,17 +67,6 @@ struct FwdLds {
   static_assert(128 * 256 <= BYTES, "epilogue H^T tile must fit in the staging buffers");
 };
 
-// Barrier for LDS hand-offs inside the routed-block loop: this wave's LDS writes are retired,
-// then all waves meet.  Unlike __syncthreads() it does not drain the vector-memory loads in
-// flight (the prefetched tile), which the compiler waits for where they are used.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 0xF | (3 << 14));   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // This thread's share of one key block's tiles, in registers.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t k, phik8, vt, hbf;   // k: e4m3 codes of K~ (FP8) or bf16 K (native)
@@ -91,14 +83,6 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
   s.hbf = __builtin_amdgcn_make_buffer_rsrc((void*)(A.hbf + (size_t)bh * D * D), 0, 2 * D * D, 0x00020000);
   return s;
-}
-
-// Tiles move from memory straight into LDS (buffer loads with the LDS destination): lane l
-// of a wave writes the 16 bytes at its wave's LDS pointer + 16 l, so each thread loads the
-// chunk that belongs at its LDS slot.  The swizzle (chunk c of row r at position c ^ (r & 7),
-// or c ^ (r & 15) for 256-byte rows) is applied to the memory address instead.
-__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 // The tile of key block j (K, phi(K~) codes, V^T) into the LDS stage at `stage`.
@@ -134,18 +118,6 @@ template <int NT>
 __device__ __forceinline__ void dma_himage(const TileSrc& src, int tid, uint8_t* dst) {
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
   static_for<2048 / NT>([&](auto P) { lds_dma(src.hbf, dst + 16 * NT * P + wofs, 16 * (tid + NT * P), 0); });
-}
-
-// All of this wave's tile copies have landed in LDS (they count as vector-memory loads).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
-
-// 32 e4m3 codes of one 128-byte LDS row (logical chunks 2g and 2g+1): the A operand of a
-// 16x16x128 matrix-core product for row `row`.
-__device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g) {
-  const uint8_t* r = base + row * 128;
-  const u32x4 a = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g) ^ (row & 7)));
-  const u32x4 b = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g + 1) ^ (row & 7)));
-  return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 constexpr int kLutReg = 64;   // LUT rows up to this long live in one register (lane x holds entry x)
@@ -551,9 +523,26 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
         u32x2 sv;
         sv.x = pack_bf16x2(ov[0], ov[1]);
         sv.y = pack_bf16x2(ov[2], ov[3]);
-        *reinterpret_cast<u32x2*>(A.o + ((size_t)bh * A.N + qrow[qt]) * D + 16 * dt + 4 * g) = sv;
+        const size_t e0 = ((size_t)bh * A.N + qrow[qt]) * D + 16 * dt + 4 * g;
+        *reinterpret_cast<u32x2*>(A.o + e0) = sv;
+        if (A.os != nullptr) {   // the two branches, for the backward pass
+          float sv4[4], lv4[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            sv4[rr] = st.acc[qt][dt][rr] * inv_l;
+            lv4[rr] = fmaf(-kCodes2, st.accl[qt][dt][rr], ol[rr]) * inv_den;
+          }
+          u32x2 s2, l2;
+          s2.x = pack_bf16x2(sv4[0], sv4[1]);
+          s2.y = pack_bf16x2(sv4[2], sv4[3]);
+          l2.x = pack_bf16x2(lv4[0], lv4[1]);
+          l2.y = pack_bf16x2(lv4[2], lv4[3]);
+          *reinterpret_cast<u32x2*>(A.os + e0) = s2;
+          *reinterpret_cast<u32x2*>(A.ol + e0) = l2;
+        }
       }
     }
+    if (A.os != nullptr && g == 0 && qok[qt]) A.inv_den[(size_t)bh * A.T * kBlock + qrow[qt]] = inv_den;
     if (A.lse != nullptr) {
       // native mode scored the raw keys: log-sum-exp over K~ = K - mu is lower by q.mu/sqrt(d)
       float shift = 0.f;
@@ -710,7 +699,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const BwdWorkspace* bw,
+                      hipStream_t s) {
   if (g.bf16) {
     FwdArgs A;
     A.q = (const uint16_t*)t.q;
@@ -729,6 +719,10 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.k_mean = t.k_mean;
     A.o = (uint16_t*)t.o;
     A.lse = t.lse;
+    // with the backward workspace (bf16, FP8 Q.K^T, d = 128) the forward keeps O_s, O_l, 1/den
+    A.os = bw != nullptr ? bw->os : nullptr;
+    A.ol = bw != nullptr ? bw->ol : nullptr;
+    A.inv_den = bw != nullptr ? bw->inv_den : nullptr;
     A.N = g.N;
     A.T = g.T;
     A.H = g.H;

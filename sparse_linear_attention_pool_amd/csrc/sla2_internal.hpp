@@ -40,18 +40,27 @@ struct Workspace {
 
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);
 
-// Views into the caller's backward workspace (layout fixed by bwd_workspace_layout()).
+// Views into the caller's backward workspace (layout fixed by bwd_workspace_layout()).  The
+// first three are written by the forward pass when it is given the backward workspace.
 struct BwdWorkspace {
+  uint16_t* os;         // [BH, N, D] O_s of the forward (bf16)
+  uint16_t* ol;         // [BH, N, D] O_l of the forward (bf16)
+  float* inv_den;       // [BH, 64T] 1 / (phi(q).Z_i + eps) of the forward (0 with every block routed)
   uint16_t* dos;        // [BH, 64T, D] alpha * dO in bf16 (rows past N zero)
-  uint16_t* dot;        // [BH, T, D, 64] dos transposed per block
-  uint16_t* qt;         // [BH, T, D, 64] dequantised e4m3 Q, transposed per block
-  uint16_t* kt;         // [BH, T, D, 64] dequantised e4m3 K~, transposed per block
+  uint16_t* dot;        // [BH, T, D, 64] dO transposed per block, tokens in the V^T tile order
+  uint16_t* q8t;        // [BH, T, D, 64] e4m3 values of the Q codes, transposed likewise
+  uint16_t* phqdt;      // [BH, T, D, 64] phi(q) / den, transposed likewise
+  uint16_t* k8t;        // [BH, T, D, 64] e4m3 values of the K~ codes, transposed likewise
+  uint16_t* phkt;       // [BH, T, D, 64] phi(K~), transposed likewise (pad tokens 0)
+  uint16_t* htimg;      // [BH, D, D] bf16 h_sum transposed (rows a), in its LDS layout
+  float* qrec;          // [BH, T, 256] per query block: lse[64], D_q[64], zeros
+  float* dden;          // [BH, 64T]
   int32_t* inv;         // [BH, T, T] per key block: the query blocks routing to it, ascending
   int32_t* inv_cnt;     // [BH, T]
-  float* dsum;          // [BH, 64T] rowsum(dO_s * O_s)
-  float* dH;            // [BH, T, D, D] dH_i
-  float* dZ;            // [BH, T, D]
-  float* dH_tot;        // [BH, D, D]
+  float* dZ;            // [BH, T, D] dZ_i
+  float* gpart;         // [BH, ceil(T/16), D, D] partials of G_tot
+  float* zpart;         // [BH, ceil(T/16), D] partials of dZ_tot
+  float* g_tot;         // [BH, D, D] sum over tokens of (phi(q)/den)^T dO
   float* dZ_tot;        // [BH, D]
   float* dalpha_part;   // [BH, T, D]
   float* dkt;           // [BH, 64T, D] dK~ in fp32, before the key-smoothing correction
@@ -65,7 +74,8 @@ hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspac
 hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
                              float* soft_mask, float* lambda, hipStream_t s);
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
-hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);
+hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const BwdWorkspace* bw,
+                      hipStream_t s);
 hipError_t launch_sum_parts(const float* parts, const float* zparts, int P, int D, int BH, float* out,
                             float* zout, hipStream_t s);
 hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const BwdWorkspace& bw,

@@ -32,7 +32,7 @@ def _run(w, inp):
     say(f"[gpu] backward {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} topk={w.topk} seed={w.seed}")
     p = params_for(w)
     dev = to_device(w, inp)
-    bufs = Bn.allocate(p, "cuda", with_lse=True, per_block_stats=True, with_bwd=True)
+    bufs = Bn.allocate(p, "cuda", with_lse=True, per_block_stats=False, with_bwd=True)   # h, z not needed
     Bn.forward(p, dev, bufs)
     dout = torch.from_numpy(inp["dout"]).to(torch.bfloat16).cuda()
     g = Bn.backward(p, dev, bufs, dout)

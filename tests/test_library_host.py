@@ -117,8 +117,9 @@ def test_backward_needs_the_forward_buffers(B):
     assert sz["workspace_bwd"] > 0
     fake = 256 * 1024          # aligned, never dereferenced: every call fails before a launch
     have = {"workspace": fake}
+    # h and z (the per-block statistics) are not needed: the backward never forms H_i per block
     for name in ("q", "k", "v", "alpha", "k_mean", "lut", "mask", "q8", "q_scale", "k8", "k_scale",
-                 "h", "z", "h_sum", "z_sum", "lse", "workspace_bwd"):
+                 "h_sum", "z_sum", "lse", "workspace_bwd"):
         with pytest.raises(B.SLA2Error) as e:
             B.sla2_attention_bwd(p, have, fake, fake, fake, fake, fake, stream=0)
         assert e.value.status == B.SLA2_ERR_INVALID_ARG and f"'{name}'" in str(e.value), (name, str(e.value))
@@ -126,3 +127,15 @@ def test_backward_needs_the_forward_buffers(B):
     with pytest.raises(B.SLA2Error) as e:
         B.sla2_attention_bwd(p, have, None, fake, fake, fake, fake, stream=0)
     assert "'dout'" in str(e.value)
+
+
+def test_training_forward_rejects_a_misaligned_backward_workspace(B):
+    # given the backward workspace, the forward also stores O_s, O_l and 1/den there
+    p = B.make_params(1, 12, 32760, 128, 15, "bf16", "fp8")
+    fake = 256 * 1024
+    have = {name: fake for name in ("workspace", "q", "k", "v", "alpha", "lut", "h_sum", "z_sum", "o",
+                                    "k_mean", "q8", "k8", "q_scale", "k_scale")}
+    have["workspace_bwd"] = fake + 16
+    with pytest.raises(B.SLA2Error) as e:
+        B.sla2_attention_fwd(p, have, stream=0)
+    assert e.value.status == B.SLA2_ERR_INVALID_ARG and "workspace_bwd" in str(e.value)
