@@ -46,6 +46,8 @@ constexpr int kNT = 256;
 constexpr int kTTile = kD * kBlock * 2;   // bytes of one transposed bf16 tile: 128 rows x 64
 constexpr int kRec = 256;                 // floats per query block in the key side's record
 constexpr int kGChunk = 16;               // query blocks per partial of G_tot
+constexpr int kQReadAhead = 1;            // feature tiles whose LDS operands are read ahead (query side)
+constexpr int kKReadAhead = 2;            // the same on the key side
 
 // Row-major LDS tile of RB-byte rows whose 16-byte chunks are XOR-swizzled by the row index:
 // 16 lanes reading one chunk column of 16 consecutive rows hit distinct banks.
@@ -391,12 +393,16 @@ __device__ __forceinline__ int list_entry(bool in_reg, int regv, const int32_t* 
 }
 
 // ---------------------------------------------------------------------------------------
-// Query side.  One workgroup of four waves per (head, query block i); wave w owns queries
-// 16w..16w+15, one per lane column (l % 16).  Products are computed transposed so that each
-// lane holds one query and the pair's keys 16mt + 4g + r: S^T = K8 Q8^T, dP^T = V dO_s^T,
-// U^T = V dnum^T, then dQ'^T += K8^T dS^T and C^T += phi(K)^T U^T with dS^T and U^T packed
-// straight into B operands (keys at vt_pos, the order of the transposed tiles).
+// Query side.  One workgroup of eight waves per (head, query block i), in two roles over the
+// same staged key tiles; wave w owns queries 16(w % 4)..+15, one per lane column (l % 16).
+// Products are computed transposed so that each lane holds one query and the pair's keys
+// 16mt + 4g + r, and their results pack straight into B operands (keys at vt_pos, the order of
+// the transposed tiles):
+//   sparse waves (w < 4): S^T = K8 Q8^T, dP^T = V dO_s^T, dS^T, then dQ'^T += K8^T dS^T;
+//   linear waves (w >= 4): U^T = V dnum^T, then C^T += phi(K)^T U^T.
 // ---------------------------------------------------------------------------------------
+constexpr int kNT2 = 512;   // threads of the two-role kernels
+
 namespace qlds {
 constexpr int K8 = 0;                 // e4m3 rows of key block j       64 x 128 B
 constexpr int V = K8 + 8192;          // V rows                          64 x 256 B
@@ -404,58 +410,54 @@ constexpr int KT = V + 16384;         // K8 values^T                     128 x 1
 constexpr int PT = KT + 16384;        // phi(K~)^T                       128 x 128 B
 constexpr int STAGE = PT + 16384;
 static_assert(STAGE >= 2 * kD * kD, "the H_tot image fits in a stage");
+static_assert(STAGE >= 4 * kBlock * kD, "the linear part of dQ (fp32) fits in a stage");
 }  // namespace qlds
 
 struct QSrc {
   __amdgpu_buffer_rsrc_t k8, v, kt, pt, him;
 };
 
-// key block j's tiles into a stage: 14 16-byte copies per thread
+// key block j's tiles into a stage: 7 16-byte copies per thread
 __device__ __forceinline__ void q_dma(const QSrc& s, int j, int N, int tid, uint8_t* st) {
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
+  {
+    const int row = tid >> 3, pc = tid & 7;
+    lds_dma(s.k8, st + qlds::K8 + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * 8192);
+  }
   static_for<2>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
-    lds_dma(s.k8, st + qlds::K8 + 4096 * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * 8192);
-  });
-  static_for<4>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 4, pc = qd & 15;
+    const int qd = tid + kNT2 * P, row = qd >> 4, pc = qd & 15;
     const int tok = min(kBlock * j + row, N - 1);   // rows past N: a finite row, masked later
-    lds_dma(s.v, st + qlds::V + 4096 * P + wofs, tok * 256 + 16 * (pc ^ (row & 15)), 0);
+    lds_dma(s.v, st + qlds::V + 8192 * P + wofs, tok * 256 + 16 * (pc ^ (row & 15)), 0);
   });
-  static_for<4>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+  static_for<2>([&](auto P) {
+    const int qd = tid + kNT2 * P, row = qd >> 3, pc = qd & 7;
     const int vo = row * 128 + 16 * (pc ^ (row & 7));
-    lds_dma(s.kt, st + qlds::KT + 4096 * P + wofs, vo, j * kTTile);
-    lds_dma(s.pt, st + qlds::PT + 4096 * P + wofs, vo, j * kTTile);
+    lds_dma(s.kt, st + qlds::KT + 8192 * P + wofs, vo, j * kTTile);
+    lds_dma(s.pt, st + qlds::PT + 8192 * P + wofs, vo, j * kTTile);
   });
 }
 
 // the 32 KB image of H_tot (rows a) into a stage
 __device__ __forceinline__ void q_dma_himage(const QSrc& s, int tid, uint8_t* st) {
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
-  static_for<8>([&](auto P) { lds_dma(s.him, st + 4096 * P + wofs, 16 * (tid + kNT * P), 0); });
+  static_for<4>([&](auto P) { lds_dma(s.him, st + 8192 * P + wofs, 16 * (tid + kNT2 * P), 0); });
 }
 
-struct QState {
-  f32x4 dqa[8];   // dQ'^T: features 16ct + 4g + r of this lane's query (scales folded in)
-  f32x4 cra[8];   // C^T = sum over routed pairs of phi(K)^T U^T, same layout
-};
-
 struct QOps {
-  i32x8 q8;       // e4m3 codes of features 32g..32g+31
-  bf16x8 dso[4];  // alpha dO, features 32s + 8g + e
-  bf16x8 dno[4];  // dnum = (1 - alpha) dO / den, same features
-  float lse_l;    // lse * log2(e)
-  float dq_l;     // D_q
+  i32x8 q8;       // sparse waves: e4m3 codes of features 32g..32g+31
+  bf16x8 b[4];    // features 32s + 8g + e: alpha dO (sparse waves) or dnum (linear waves)
+  float lse_l;    // sparse waves: lse * log2(e)
+  float dq_l;     // sparse waves: D_q
 };
 
 // One routed pair: key block j = LUT entry r in stage STG, K scale ksc.  The next block's tiles
-// (after the last, the H_tot image) are copied into the other stage meanwhile.
+// (after the last, the H_tot image) are copied into the other stage meanwhile.  acc: dQ'^T
+// (sparse waves, scales folded in) or C^T (linear waves), features 16ct + 4g + r.
 template <int STG>
-__device__ __forceinline__ void q_iteration(const BwdArgs& A, QState& st, uint8_t* smem0, uint8_t* smem1,
+__device__ __forceinline__ void q_iteration(const BwdArgs& A, f32x4 (&acc)[8], uint8_t* smem0, uint8_t* smem1,
                                             const QSrc& src, bool lut_reg, int lutv, const int32_t* lutG,
                                             int r, int topk, int bh, float sq, float& ksc, const QOps& qo,
-                                            int nvalid, int l16, int g, int tid) {
+                                            bool sparse, int nvalid, int l16, int g, int tid) {
   const uint8_t* stg = STG == 0 ? smem0 : smem1;
   uint8_t* next = STG == 0 ? smem1 : smem0;
   float ksc_next = 1.f;
@@ -468,64 +470,113 @@ __device__ __forceinline__ void q_iteration(const BwdArgs& A, QState& st, uint8_
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
-  f32x4 S[4], dP[4], U[4];
-  static_for<4>([&](auto mt) {
-    S[mt] = mfma_fp8(lds_fp8_row(stg + qlds::K8, 16 * mt + l16, g), qo.q8, f32x4{0.f, 0.f, 0.f, 0.f});
-    dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (sparse) {
+    const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
+    // P^T and dS^T (times k_scale / sqrt(d), the factor of dQ' = dS K' / sqrt(d)) of key half s
+    // (tiles 2s, 2s+1) as B operands
+    const float cj = kLog2e * inv_sqrt_d * sq * ksc, fs = ksc * inv_sqrt_d;
+    f32x4 S[4], dP[4];
+    bf16x8 dso_[2];
+    auto half_ops = [&](int s) {
+      float dv8[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a = op256(stg + qlds::V, 16 * mt + l16, s, g);
-      dP[mt] = mfma_bf16(a, qo.dso[s], dP[mt]);
-      U[mt] = mfma_bf16(a, qo.dno[s], U[mt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  });
-
-  // P^T and dS^T (times k_scale / sqrt(d), the factor of dQ' = dS K' / sqrt(d)) as B operands
-  const float cj = kLog2e * inv_sqrt_d * sq * ksc, fs = ksc * inv_sqrt_d;
-  bf16x8 dso_[2], uo[2];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float dv8[8], uv8[8];
+        for (int rr = 0; rr < 4; ++rr) {
+          const int mt = 2 * s + h, key = 16 * mt + 4 * g + rr;
+          float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
+          if (key >= nvalid) p = 0.f;
+          dv8[4 * h + rr] = p * (dP[mt][rr] - qo.dq_l) * fs;
+        }
+      dso_[s] = pack8(dv8);
+    };
+    // operand reads run one key tile ahead of the products that use them
+    i32x8 kr[4];
+    bf16x8 va[4][4];
+    auto read_keys = [&](auto mt) {
+      kr[mt] = lds_fp8_row(stg + qlds::K8, 16 * mt + l16, g);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int s = 0; s < 4; ++s) va[mt][s] = op256(stg + qlds::V, 16 * mt + l16, s, g);
+    };
+    read_keys(std::integral_constant<int, 0>{});
+    static_for<4>([&](auto mt) {
+      if constexpr (mt + 1 < 4) read_keys(std::integral_constant<int, mt + 1>{});
+      S[mt] = mfma_fp8(kr[mt], qo.q8, f32x4{0.f, 0.f, 0.f, 0.f});
+      dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int mt = 2 * s + h, key = 16 * mt + 4 * g + rr;
-        float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
-        if (key >= nvalid) p = 0.f;
-        dv8[4 * h + rr] = p * (dP[mt][rr] - qo.dq_l) * fs;
-        uv8[4 * h + rr] = U[mt][rr];
-      }
-    dso_[s] = pack8(dv8);
-    uo[s] = pack8(uv8);
-  }
-
-  static_for<8>([&](auto ct) {
+      for (int s = 0; s < 4; ++s) dP[mt] = mfma_bf16(va[mt][s], qo.b[s], dP[mt]);
+      if constexpr (mt == 2) half_ops(0);   // while tile 2's products run
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    half_ops(1);
+    bf16x8 ka[8][2];
+    auto read_feat = [&](auto ct) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) ka[ct][s] = op128(stg + qlds::KT, 16 * ct + l16, s, g);
+    };
+    static_for<kQReadAhead>([&](auto ct) { read_feat(ct); });
+    static_for<8>([&](auto ct) {
+      if constexpr (ct + kQReadAhead < 8) read_feat(std::integral_constant<int, ct + kQReadAhead>{});
+#pragma unroll
+      for (int s = 0; s < 2; ++s) acc[ct] = mfma_bf16(ka[ct][s], dso_[s], acc[ct]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    // U^T = V dnum^T, packed as the B operand of C^T += phi(K)^T U^T
+    f32x4 U[4];
+    bf16x8 va[4][4];
+    auto read_keys = [&](auto mt) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) va[mt][s] = op256(stg + qlds::V, 16 * mt + l16, s, g);
+    };
+    read_keys(std::integral_constant<int, 0>{});
+    static_for<4>([&](auto mt) {
+      if constexpr (mt + 1 < 4) read_keys(std::integral_constant<int, mt + 1>{});
+      U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) U[mt] = mfma_bf16(va[mt][s], qo.b[s], U[mt]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    bf16x8 uo[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      st.dqa[ct] = mfma_bf16(op128(stg + qlds::KT, 16 * ct + l16, s, g), dso_[s], st.dqa[ct]);
-      st.cra[ct] = mfma_bf16(op128(stg + qlds::PT, 16 * ct + l16, s, g), uo[s], st.cra[ct]);
+      float uv8[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) uv8[4 * h + rr] = U[2 * s + h][rr];
+      uo[s] = pack8(uv8);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  });
+    bf16x8 pa[8][2];
+    auto read_feat = [&](auto ct) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) pa[ct][s] = op128(stg + qlds::PT, 16 * ct + l16, s, g);
+    };
+    static_for<kQReadAhead>([&](auto ct) { read_feat(ct); });
+    static_for<8>([&](auto ct) {
+      if constexpr (ct + kQReadAhead < 8) read_feat(std::integral_constant<int, ct + kQReadAhead>{});
+#pragma unroll
+      for (int s = 0; s < 2; ++s) acc[ct] = mfma_bf16(pa[ct][s], uo[s], acc[ct]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
 
   wait_dma();
   lds_barrier();
   ksc = ksc_next;
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
+__global__ __launch_bounds__(512, 1) void bwd_query_kernel(BwdArgs A) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[qlds::STAGE];   // stage of even LUT entries
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[qlds::STAGE];   // stage of odd LUT entries
   __shared__ float zS[kD];                                                // Z_i
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
   const int bh = __builtin_amdgcn_readfirstlane(lid / A.T), i = __builtin_amdgcn_readfirstlane(lid % A.T);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4, wq = w & 3;
+  const bool sparse = w < 4;
   const int hidx = bh % A.H, T = A.T, N = A.N, topk = A.topk;
-  const int qq = kBlock * i + 16 * w + l16;   // this lane's query
+  const int qq = kBlock * i + 16 * wq + l16;   // this lane's query
   const bool qok = qq < N;
   const int32_t* lutG = A.lut + ((size_t)bh * T + i) * topk;
   const bool lut_reg = topk <= 64;
@@ -542,12 +593,9 @@ __global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
   q_dma(src, j0, N, tid, smem0);
 
   QOps qo;
-  {
-    const uint8_t* s8 = A.q8 + ((size_t)bh * T * kBlock + qq) * kD + 32 * g;   // pad rows: code 0
-    const u32x4 a = *reinterpret_cast<const u32x4*>(s8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
-    qo.q8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
+  qo.q8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  qo.lse_l = 0.f;
+  qo.dq_l = 0.f;
   const float invd = qok ? A.inv_den[(size_t)bh * T * kBlock + qq] : 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -557,20 +605,22 @@ __global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
     const f32x4 a1 = *reinterpret_cast<const f32x4*>(A.alpha + (size_t)hidx * kD + c + 4);
     const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-    float d8[8], n8[8];
+    float b8[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf16_lo(rw[e]), hi = bf16_hi(rw[e]);
-      d8[2 * e] = av[2 * e] * lo;
-      d8[2 * e + 1] = av[2 * e + 1] * hi;
-      n8[2 * e] = (1.f - av[2 * e]) * lo * invd;
-      n8[2 * e + 1] = (1.f - av[2 * e + 1]) * hi * invd;
+    for (int e = 0; e < 8; ++e) {
+      const float d = (e & 1) ? bf16_hi(rw[e >> 1]) : bf16_lo(rw[e >> 1]);
+      b8[e] = sparse ? av[e] * d : (1.f - av[e]) * d * invd;   // alpha dO or dnum
     }
-    qo.dso[s] = pack8(d8);
-    qo.dno[s] = pack8(n8);
+    qo.b[s] = pack8(b8);
   }
-  qo.lse_l = qok ? A.lse[(size_t)bh * N + qq] * kLog2e : 0.f;
-  qo.dq_l = A.qrec[((size_t)bh * T + i) * kRec + kBlock + 16 * w + l16];
+  if (sparse) {
+    const uint8_t* s8 = A.q8 + ((size_t)bh * T * kBlock + qq) * kD + 32 * g;   // pad rows: code 0
+    const u32x4 a = *reinterpret_cast<const u32x4*>(s8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
+    qo.q8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    qo.lse_l = qok ? A.lse[(size_t)bh * N + qq] * kLog2e : 0.f;
+    qo.dq_l = A.qrec[((size_t)bh * T + i) * kRec + kBlock + 16 * wq + l16];
+  }
   const float dden_l = A.dden[(size_t)bh * T * kBlock + qq];
   const float sq = A.q_scale[(size_t)bh * T + i];
   if (tid < kD) zS[tid] = A.z_sum[(size_t)bh * kD + tid] - A.zrout[((size_t)bh * T + i) * kD + tid];
@@ -578,75 +628,86 @@ __global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
   const int nlast = N - kBlock * (T - 1);
   const bool last_partial = list_entry(lut_reg, lutv, lutG, topk - 1) == T - 1 && nlast < kBlock;
 
-  QState st;
+  f32x4 acc[8];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    st.dqa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.cra[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   wait_dma();
   lds_barrier();
 
-  for (int r = 0; r < topk; r += 2) {
-    q_iteration<0>(A, st, smem0, smem1, src, lut_reg, lutv, lutG, r, topk, bh, sq, ksc, qo,
-                   (last_partial && r == topk - 1) ? nlast : kBlock, l16, g, tid);
-    if (r + 1 < topk)
-      q_iteration<1>(A, st, smem0, smem1, src, lut_reg, lutv, lutG, r + 1, topk, bh, sq, ksc, qo,
-                     (last_partial && r + 1 == topk - 1) ? nlast : kBlock, l16, g, tid);
+  // pairs of LUT entries, then the odd last one: the loop body has no branch on the count, so
+  // its registers need no reshuffling at a join
+  int r = 0;
+  for (; r + 1 < topk; r += 2) {
+    q_iteration<0>(A, acc, smem0, smem1, src, lut_reg, lutv, lutG, r, topk, bh, sq, ksc, qo, sparse, kBlock, l16, g,
+                   tid);
+    q_iteration<1>(A, acc, smem0, smem1, src, lut_reg, lutv, lutG, r + 1, topk, bh, sq, ksc, qo, sparse,
+                   (last_partial && r + 1 == topk - 1) ? nlast : kBlock, l16, g, tid);
   }
+  if (r < topk)
+    q_iteration<0>(A, acc, smem0, smem1, src, lut_reg, lutv, lutG, r, topk, bh, sq, ksc, qo, sparse,
+                   last_partial ? nlast : kBlock, l16, g, tid);
 
-  // ---------------- epilogue: the H_tot image is in the stage after the last tile's
+  // ---------------- epilogue: the H_tot image is in the stage after the last tile's; the
+  // other stage carries the linear part of dQ from the linear waves to the sparse waves
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
-  // phi(q) at features a = 16at + 4g + r (the layout of the accumulators)
-  float ph[8][4];
-  {
-    const uint16_t* qr = A.q + ((size_t)bh * N + min(qq, N - 1)) * kD + 4 * g;
-    float mx = -INFINITY;
+  float* X = reinterpret_cast<float*>((topk & 1) ? smem0 : smem1);
+  if (!sparse) {
+    // phi(q) at features a = 16at + 4g + r (the layout of the accumulators)
+    float ph[8][4];
+    {
+      const uint16_t* qr = A.q + ((size_t)bh * N + min(qq, N - 1)) * kD + 4 * g;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int at = 0; at < 8; ++at) {
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(qr + 16 * at);
+        ph[at][0] = bf16_lo(wv.x);
+        ph[at][1] = bf16_hi(wv.x);
+        ph[at][2] = bf16_lo(wv.y);
+        ph[at][3] = bf16_hi(wv.y);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, ph[at][rr]);
+      }
+      mx = rows4_max(mx);
+      float sm = 0.f;
+#pragma unroll
+      for (int at = 0; at < 8; ++at)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          ph[at][rr] = __expf(ph[at][rr] - mx);
+          sm += ph[at][rr];
+        }
+      const float is = 1.f / rows4_sum(sm);
+#pragma unroll
+      for (int at = 0; at < 8; ++at)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ph[at][rr] *= is;
+    }
+    // dphi(q)^T = H_tot dnum^T - C^T + Z_i dden, then the softmax backward
+    float dphi[8][4], dotp = 0.f;
 #pragma unroll
     for (int at = 0; at < 8; ++at) {
-      const u32x2 wv = *reinterpret_cast<const u32x2*>(qr + 16 * at);
-      ph[at][0] = bf16_lo(wv.x);
-      ph[at][1] = bf16_hi(wv.x);
-      ph[at][2] = bf16_lo(wv.y);
-      ph[at][3] = bf16_hi(wv.y);
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, ph[at][r]);
-    }
-    mx = rows4_max(mx);
-    float sm = 0.f;
+      for (int s = 0; s < 4; ++s) t = mfma_bf16(op256(Hs, 16 * at + l16, s, g), qo.b[s], t);
 #pragma unroll
-    for (int at = 0; at < 8; ++at)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ph[at][r] = __expf(ph[at][r] - mx);
-        sm += ph[at][r];
+      for (int rr = 0; rr < 4; ++rr) {
+        dphi[at][rr] = t[rr] - acc[at][rr] + zS[16 * at + 4 * g + rr] * dden_l;
+        dotp = fmaf(ph[at][rr], dphi[at][rr], dotp);
       }
-    const float is = 1.f / rows4_sum(sm);
+    }
+    dotp = rows4_sum(dotp);
 #pragma unroll
     for (int at = 0; at < 8; ++at)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ph[at][r] *= is;
+      for (int rr = 0; rr < 4; ++rr) X[((wq * 8 + at) * 4 + rr) * 64 + lane] = ph[at][rr] * (dphi[at][rr] - dotp);
   }
-  // dphi(q)^T = H_tot dnum^T - C^T + Z_i dden, then the softmax backward
-  float dphi[8][4], dotp = 0.f;
-#pragma unroll
-  for (int at = 0; at < 8; ++at) {
-    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) t = mfma_bf16(op256(Hs, 16 * at + l16, s, g), qo.dno[s], t);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dphi[at][r] = t[r] - st.cra[at][r] + zS[16 * at + 4 * g + r] * dden_l;
-      dotp = fmaf(ph[at][r], dphi[at][r], dotp);
-    }
-  }
-  dotp = rows4_sum(dotp);
-  if (qok) {
+  __syncthreads();
+  if (sparse && qok) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       float o[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = st.dqa[ct][r] + ph[ct][r] * (dphi[ct][r] - dotp);
+      for (int rr = 0; rr < 4; ++rr) o[rr] = acc[ct][rr] + X[((wq * 8 + ct) * 4 + rr) * 64 + lane];
       u32x2 sv;
       sv.x = pack_bf16x2(o[0], o[1]);
       sv.y = pack_bf16x2(o[2], o[3]);
@@ -656,10 +717,11 @@ __global__ __launch_bounds__(256, 1) void bwd_query_kernel(BwdArgs A) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Key side.  One workgroup of four waves per (head, key block j); wave w owns keys
-// 16w..16w+15, one per lane column.  Per routing query block i: S = Q8 K8^T, dP = dO_s V^T,
-// dV^T += dO^T P, dK'^T += Q8^T dS (queries at vt_pos), and C[a][c] += (phi(q)/den)^T dO over
-// the wave's rows a = 32w..32w+31, sharing the dO^T operands of the dV product.
+// Key side.  One workgroup of eight waves per (head, key block j), in two roles over the same
+// staged query tiles.  Per routing query block i:
+//   sparse waves (w < 4, keys 16w..16w+15, one per lane column): S = Q8 K8^T, dP = dO_s V^T,
+//     then dV^T += dO^T P and dK'^T += Q8^T dS (queries at vt_pos);
+//   correction waves (w >= 4): C[a][c] += (phi(q)/den)^T dO over rows a = 32(w - 4)..+31.
 // ---------------------------------------------------------------------------------------
 namespace klds {
 constexpr int Q8 = 0;                 // e4m3 rows of query block i      64 x 128 B
@@ -676,48 +738,46 @@ struct KSrc {
   __amdgpu_buffer_rsrc_t q8, dos, dot, qt, pt, rec;
 };
 
-// query block i's tiles into a stage: 18 16-byte copies per thread (19 in wave 0)
+// query block i's tiles into a stage: 9 16-byte copies per thread (10 in wave 0)
 __device__ __forceinline__ void k_dma(const KSrc& s, int i, int tid, uint8_t* st) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wofs = 1024 * w;
+  {
+    const int row = tid >> 3, pc = tid & 7;
+    lds_dma(s.q8, st + klds::Q8 + wofs, row * 128 + 16 * (pc ^ (row & 7)), i * 8192);
+  }
   static_for<2>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
-    lds_dma(s.q8, st + klds::Q8 + 4096 * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), i * 8192);
+    const int qd = tid + kNT2 * P, row = qd >> 4, pc = qd & 15;
+    lds_dma(s.dos, st + klds::DOS + 8192 * P + wofs, row * 256 + 16 * (pc ^ (row & 15)), i * 16384);
   });
-  static_for<4>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 4, pc = qd & 15;
-    lds_dma(s.dos, st + klds::DOS + 4096 * P + wofs, row * 256 + 16 * (pc ^ (row & 15)), i * 16384);
-  });
-  static_for<4>([&](auto P) {
-    const int qd = tid + kNT * P, row = qd >> 3, pc = qd & 7;
+  static_for<2>([&](auto P) {
+    const int qd = tid + kNT2 * P, row = qd >> 3, pc = qd & 7;
     const int vo = row * 128 + 16 * (pc ^ (row & 7));
-    lds_dma(s.dot, st + klds::DOT + 4096 * P + wofs, vo, i * kTTile);
-    lds_dma(s.qt, st + klds::QT + 4096 * P + wofs, vo, i * kTTile);
-    lds_dma(s.pt, st + klds::PT + 4096 * P + wofs, vo, i * kTTile);
+    lds_dma(s.dot, st + klds::DOT + 8192 * P + wofs, vo, i * kTTile);
+    lds_dma(s.qt, st + klds::QT + 8192 * P + wofs, vo, i * kTTile);
+    lds_dma(s.pt, st + klds::PT + 8192 * P + wofs, vo, i * kTTile);
   });
   if (w == 0) lds_dma(s.rec, st + klds::REC, 16 * (tid & 63), i * (kRec * 4));
 }
 
-struct KState {
-  f32x4 dva[8];      // dV^T: features 16ct + 4g + r of this lane's key (alpha applied after)
-  f32x4 dka[8];      // dK'^T (scales folded in)
-  f32x4 cra[2][8];   // C[a][c], a = 32w + 16at + 4g + r, c = 16ct + l%16
-  float dz;          // threads < 128: sum of dZ_i over the routing query blocks, feature tid
-};
-
 struct KOps {
-  i32x8 k8;          // e4m3 codes of features 32g..32g+31 of this lane's key
-  bf16x8 v[4];       // V of this lane's key, features 32s + 8g + e
+  i32x8 k8;          // sparse waves: e4m3 codes of features 32g..32g+31 of this lane's key
+  bf16x8 v[4];       // sparse waves: V of this lane's key, features 32s + 8g + e
 };
 
+// acc: sparse waves: [0..7] dV^T, [8..15] dK'^T (features 16ct + 4g + r of this lane's key);
+// correction waves: C[a][c] at [8at + ct], a = 32(w - 4) + 16at + 4g + r, c = 16ct + l%16
 template <int STG>
-__device__ __forceinline__ void k_iteration(const BwdArgs& A, KState& st, uint8_t* smem0, uint8_t* smem1,
-                                            const KSrc& src, bool inv_reg, int invv, const int32_t* invG,
-                                            int x, int cnt, int bh, float ksc, int& i, float& sq,
-                                            const KOps& ko, bool kok, int w, int l16, int g, int tid) {
+__device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], float& dz, uint8_t* smem0,
+                                            uint8_t* smem1, const KSrc& src, bool inv_reg, int invv,
+                                            const int32_t* invG, int x, int cnt, int bh, float ksc, int& i,
+                                            float& sq, const KOps& ko, bool sparse, bool kok, int wc, int l16,
+                                            int g, int tid) {
   const uint8_t* stg = STG == 0 ? smem0 : smem1;
   uint8_t* next = STG == 0 ? smem1 : smem0;
-  // dZ_i is loaded before the copies are issued: waiting for it then never waits for them
-  const float dzi = tid < kD ? A.dZ[((size_t)bh * A.T + i) * kD + tid] : 0.f;
+  // dZ_i (correction waves, one feature per thread) is loaded before the copies are issued:
+  // waiting for it then never waits for them
+  const int zt = tid - 4 * 64;
+  const float dzi = (!sparse && zt < kD) ? A.dZ[((size_t)bh * A.T + i) * kD + zt] : 0.f;
   __builtin_amdgcn_sched_barrier(0);
   int i_next = 0;
   float sq_next = 1.f;
@@ -728,74 +788,121 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, KState& st, uint8_
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
-  const int nq = min(kBlock, A.N - kBlock * i);
-  f32x4 S[4], dP[4];
-  static_for<4>([&](auto mt) {
-    S[mt] = mfma_fp8(lds_fp8_row(stg + klds::Q8, 16 * mt + l16, g), ko.k8, f32x4{0.f, 0.f, 0.f, 0.f});
-    dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (sparse) {
+    const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
+    const int nq = min(kBlock, A.N - kBlock * i);
+    // P and dS (times q_scale / sqrt(d), the factor of dK' = dS^T Q' / sqrt(d)) of query half s
+    // (tiles 2s, 2s+1) as B operands, with the pair's lse and D_q at rows 16mt + 4g .. +3
+    const float* rec = reinterpret_cast<const float*>(stg + klds::REC);
+    const float cij = kLog2e * inv_sqrt_d * sq * ksc, fk = sq * inv_sqrt_d;
+    f32x4 S[4], dP[4], l4[2], d4[2];
+    bf16x8 po[2], dso_[2];
+    auto read_rec = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dP[mt] = mfma_bf16(op256(stg + klds::DOS, 16 * mt + l16, s, g), ko.v[s], dP[mt]);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-
-  // P and dS (times q_scale / sqrt(d), the factor of dK' = dS^T Q' / sqrt(d)) as B operands
-  const float cij = kLog2e * inv_sqrt_d * sq * ksc, fk = sq * inv_sqrt_d;
-  const float* rec = reinterpret_cast<const float*>(stg + klds::REC);
-  bf16x8 po[2], dso_[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float p8[8], d8[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q0 = 16 * (2 * s + h) + 4 * g;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(rec + q0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(rec + kBlock + q0);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float p = __builtin_amdgcn_exp2f(fmaf(S[2 * s + h][rr], cij, -l4[rr] * kLog2e));
-        if (q0 + rr >= nq || !kok) p = 0.f;
-        p8[4 * h + rr] = p;
-        d8[4 * h + rr] = p * (dP[2 * s + h][rr] - d4[rr]) * fk;
+      for (int h = 0; h < 2; ++h) {
+        l4[h] = *reinterpret_cast<const f32x4*>(rec + 16 * (2 * s + h) + 4 * g);
+        d4[h] = *reinterpret_cast<const f32x4*>(rec + kBlock + 16 * (2 * s + h) + 4 * g);
       }
-    }
-    po[s] = pack8(p8);
-    dso_[s] = pack8(d8);
+    };
+    auto half_ops = [&](int s) {
+      float p8[8], d8[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int mt = 2 * s + h, q0 = 16 * mt + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cij, -l4[h][rr] * kLog2e));
+          if (q0 + rr >= nq || !kok) p = 0.f;
+          p8[4 * h + rr] = p;
+          d8[4 * h + rr] = p * (dP[mt][rr] - d4[h][rr]) * fk;
+        }
+      }
+      po[s] = pack8(p8);
+      dso_[s] = pack8(d8);
+    };
+    // operand reads run one query tile ahead of the products that use them
+    i32x8 qr[4];
+    bf16x8 da[4][4];
+    auto read_queries = [&](auto mt) {
+      qr[mt] = lds_fp8_row(stg + klds::Q8, 16 * mt + l16, g);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) da[mt][s] = op256(stg + klds::DOS, 16 * mt + l16, s, g);
+    };
+    read_rec(0);
+    read_queries(std::integral_constant<int, 0>{});
+    static_for<4>([&](auto mt) {
+      if constexpr (mt + 1 < 4) read_queries(std::integral_constant<int, mt + 1>{});
+      S[mt] = mfma_fp8(qr[mt], ko.k8, f32x4{0.f, 0.f, 0.f, 0.f});
+      dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dP[mt] = mfma_bf16(da[mt][s], ko.v[s], dP[mt]);
+      if constexpr (mt == 2) {   // the first half's operands, while tile 2's products run
+        half_ops(0);
+        read_rec(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    half_ops(1);
+    bf16x8 fo[8][2], fq[8][2];
+    auto read_feat = [&](auto ct) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        fo[ct][s] = op128(stg + klds::DOT, 16 * ct + l16, s, g);
+        fq[ct][s] = op128(stg + klds::QT, 16 * ct + l16, s, g);
+      }
+    };
+    static_for<kKReadAhead>([&](auto ct) { read_feat(ct); });
+    static_for<8>([&](auto ct) {
+      if constexpr (ct + kKReadAhead < 8) read_feat(std::integral_constant<int, ct + kKReadAhead>{});
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        acc[ct] = mfma_bf16(fo[ct][s], po[s], acc[ct]);
+        acc[8 + ct] = mfma_bf16(fq[ct][s], dso_[s], acc[8 + ct]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    bf16x8 fa[2][2];
+#pragma unroll
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) fa[at][s] = op128(stg + klds::PT, 32 * wc + 16 * at + l16, s, g);
+    bf16x8 fo[8][2];
+    auto read_feat = [&](auto ct) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) fo[ct][s] = op128(stg + klds::DOT, 16 * ct + l16, s, g);
+    };
+    static_for<kKReadAhead>([&](auto ct) { read_feat(ct); });
+    static_for<8>([&](auto ct) {
+      if constexpr (ct + kKReadAhead < 8) read_feat(std::integral_constant<int, ct + kKReadAhead>{});
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        acc[ct] = mfma_bf16(fa[0][s], fo[ct][s], acc[ct]);
+        acc[8 + ct] = mfma_bf16(fa[1][s], fo[ct][s], acc[8 + ct]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
-  bf16x8 fa[2][2];
-#pragma unroll
-  for (int at = 0; at < 2; ++at)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) fa[at][s] = op128(stg + klds::PT, 32 * w + 16 * at + l16, s, g);
-  static_for<8>([&](auto ct) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 fo = op128(stg + klds::DOT, 16 * ct + l16, s, g);
-      st.dva[ct] = mfma_bf16(fo, po[s], st.dva[ct]);
-      st.dka[ct] = mfma_bf16(op128(stg + klds::QT, 16 * ct + l16, s, g), dso_[s], st.dka[ct]);
-      st.cra[0][ct] = mfma_bf16(fa[0][s], fo, st.cra[0][ct]);
-      st.cra[1][ct] = mfma_bf16(fa[1][s], fo, st.cra[1][ct]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  });
-
-  st.dz += dzi;
+  dz += dzi;
   wait_dma();
   lds_barrier();
   i = i_next;
   sq = sq_next;
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
+__global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[klds::STAGE];   // stage of even list entries
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[klds::STAGE];   // stage of odd list entries
   __shared__ float dzS[kD], alS[kD];
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
   const int bh = __builtin_amdgcn_readfirstlane(lid / A.T), j = __builtin_amdgcn_readfirstlane(lid % A.T);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  const bool sparse = w < 4;
+  const int wc = w & 3;
   const int hidx = bh % A.H, T = A.T, N = A.N;
-  const int kk = kBlock * j + 16 * w + l16;   // this lane's key
+  const int kk = kBlock * j + 16 * wc + l16;   // sparse waves: this lane's key
   const bool kok = kk < N;
   const int cnt = __builtin_amdgcn_readfirstlane(A.inv_cnt[(size_t)bh * T + j]);
   const int32_t* invG = A.inv + ((size_t)bh * T + j) * T;
@@ -818,57 +925,63 @@ __global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
   }
 
   KOps ko;
-  {
+  ko.k8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) ko.v[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  if (sparse) {
     const uint8_t* s8 = A.k8 + ((size_t)bh * T * kBlock + kk) * kD + 32 * g;   // pad rows: code 0
     const u32x4 a = *reinterpret_cast<const u32x4*>(s8);
     const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
     ko.k8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    ko.v[s] = __builtin_bit_cast(bf16x8, kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + 32 * s + 8 * g)
-                                             : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < 4; ++s)
+      ko.v[s] = __builtin_bit_cast(bf16x8, kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + 32 * s + 8 * g)
+                                               : u32x4{0, 0, 0, 0});
+  }
   const float ksc = A.k_scale[(size_t)bh * T + j];
   if (tid < kD) alS[tid] = A.alpha[(size_t)hidx * kD + tid];
 
-  KState st;
+  f32x4 acc[16];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    st.dva[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.dka[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.cra[0][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.cra[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  st.dz = 0.f;
+  for (int e = 0; e < 16; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dz = 0.f;
   wait_dma();
   lds_barrier();
 
-  for (int x = 0; x < cnt; x += 2) {
-    k_iteration<0>(A, st, smem0, smem1, src, inv_reg, invv, invG, x, cnt, bh, ksc, i, sq, ko, kok, w, l16, g, tid);
-    if (x + 1 < cnt)
-      k_iteration<1>(A, st, smem0, smem1, src, inv_reg, invv, invG, x + 1, cnt, bh, ksc, i, sq, ko, kok, w, l16, g,
-                     tid);
+  // pairs of list entries, then the odd last one (a loop body without a branch on the count)
+  int x = 0;
+  for (; x + 1 < cnt; x += 2) {
+    k_iteration<0>(A, acc, dz, smem0, smem1, src, inv_reg, invv, invG, x, cnt, bh, ksc, i, sq, ko, sparse, kok, wc,
+                   l16, g, tid);
+    k_iteration<1>(A, acc, dz, smem0, smem1, src, inv_reg, invv, invG, x + 1, cnt, bh, ksc, i, sq, ko, sparse, kok,
+                   wc, l16, g, tid);
   }
+  if (x < cnt)
+    k_iteration<0>(A, acc, dz, smem0, smem1, src, inv_reg, invv, invG, x, cnt, bh, ksc, i, sq, ko, sparse, kok, wc,
+                   l16, g, tid);
 
   // ---------------- epilogue
-  // dh_j = (G_tot - C) diag(1 - alpha) as bf16 images with rows a and rows c; dz_j
-  if (tid < kD) dzS[tid] = A.dZ_tot[(size_t)bh * kD + tid] - st.dz;
+  // correction waves: dh_j = (G_tot - C) diag(1 - alpha) as bf16 images with rows a and rows c,
+  // and dz_j
   const LTile<256> DH{smem0}, DHT{smem0 + 2 * kD * kD};
-  {
+  if (!sparse) {
+    const int zt = tid - 4 * 64;
+    if (zt < kD) dzS[zt] = A.dZ_tot[(size_t)bh * kD + zt] - dz;
     const float* gt = A.g_tot + (size_t)bh * kD * kD;
 #pragma unroll
     for (int at = 0; at < 2; ++at)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a = 32 * w + 16 * at + 4 * g + r, c = 16 * ct + l16;
-          const uint16_t bv = f32_to_bf16((gt[a * kD + c] - st.cra[at][ct][r]) * (1.f - alS[c]));
+        for (int rr = 0; rr < 4; ++rr) {
+          const int a = 32 * wc + 16 * at + 4 * g + rr, c = 16 * ct + l16;
+          const uint16_t bv = f32_to_bf16((gt[a * kD + c] - acc[8 * at + ct][rr]) * (1.f - alS[c]));
           *DH.el16(a, c) = bv;
           *DHT.el16(c, a) = bv;
         }
   }
   __syncthreads();
+  if (!sparse) return;
 
   // phi(k~) of this lane's key: as B operand (features 32s + 8g + e) and at the accumulator
   // features 16at + 4g + r
@@ -913,7 +1026,7 @@ __global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
       const u32x2 wv = *reinterpret_cast<const u32x2*>(kr + 16 * at + 4 * g);
       const float raw[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pk[at][r] = __expf(raw[r] - mu[16 * at + 4 * g + r] - mx) * is;
+      for (int rr = 0; rr < 4; ++rr) pk[at][rr] = __expf(raw[rr] - mu[16 * at + 4 * g + rr] - mx) * is;
     }
   }
   // dphi(k)^T = dh_j V^T + dz_j; dV^T = alpha dV_sparse^T + dh_j^T phi(k)^T
@@ -924,29 +1037,29 @@ __global__ __launch_bounds__(256, 1) void bwd_key_kernel(BwdArgs A) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), ko.v[s], t);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dphi[at][r] = t[r] + dzS[16 * at + 4 * g + r];
-      dotp = fmaf(pk[at][r], dphi[at][r], dotp);
+    for (int rr = 0; rr < 4; ++rr) {
+      dphi[at][rr] = t[rr] + dzS[16 * at + 4 * g + rr];
+      dotp = fmaf(pk[at][rr], dphi[at][rr], dotp);
     }
   }
   dotp = rows4_sum(dotp);
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st.dva[ct][r] *= alS[16 * ct + 4 * g + r];
+    for (int rr = 0; rr < 4; ++rr) acc[ct][rr] *= alS[16 * ct + 4 * g + rr];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) st.dva[ct] = mfma_bf16(DHT.op(16 * ct + l16, 32 * s + 8 * g), pko[s], st.dva[ct]);
+    for (int s = 0; s < 4; ++s) acc[ct] = mfma_bf16(DHT.op(16 * ct + l16, 32 * s + 8 * g), pko[s], acc[ct]);
   }
   if (kok) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = st.dka[ct][r] + pk[ct][r] * (dphi[ct][r] - dotp);
+      for (int rr = 0; rr < 4; ++rr) o[rr] = acc[8 + ct][rr] + pk[ct][rr] * (dphi[ct][rr] - dotp);
       *reinterpret_cast<f32x4*>(A.dkt + ((size_t)bh * T * kBlock + kk) * kD + 16 * ct + 4 * g) = o;
       u32x2 sv;
-      sv.x = pack_bf16x2(st.dva[ct][0], st.dva[ct][1]);
-      sv.y = pack_bf16x2(st.dva[ct][2], st.dva[ct][3]);
+      sv.x = pack_bf16x2(acc[ct][0], acc[ct][1]);
+      sv.y = pack_bf16x2(acc[ct][2], acc[ct][3]);
       *reinterpret_cast<u32x2*>(A.dv + ((size_t)bh * N + kk) * kD + 16 * ct + 4 * g) = sv;
     }
   }
@@ -1110,8 +1223,8 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   hipLaunchKernelGGL(bwd_gtot_kernel, dim3(A.pg, g.BH), dim3(256), 0, s, A);
   hipError_t e = launch_sum_parts(bw.gpart, bw.zpart, A.pg, g.D, g.BH, bw.g_tot, bw.dZ_tot, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_query_kernel, dim3(A.nblocks), dim3(256), 0, s, A);
-  hipLaunchKernelGGL(bwd_key_kernel, dim3(A.nblocks), dim3(256), 0, s, A);
+  hipLaunchKernelGGL(bwd_query_kernel, dim3(A.nblocks), dim3(kNT2), 0, s, A);
+  hipLaunchKernelGGL(bwd_key_kernel, dim3(A.nblocks), dim3(kNT2), 0, s, A);
   hipLaunchKernelGGL(bwd_colsum_kernel, dim3(A.nch, g.BH), dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_mean_kernel, dim3(g.BH), dim3(128), 0, s, A);
   hipLaunchKernelGGL(bwd_dk_kernel, dim3((g.N * 16 + 255) / 256, g.BH), dim3(256), 0, s, A);
