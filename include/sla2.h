@@ -135,9 +135,12 @@ int sla2_route(const sla2_params *p, const sla2_tensors *t, void *stream);
  * then, from the same fp64 scores:
  *   P_ij = softmax_j(s_ij) (the compressed attention of SLA page, section 2 Q2 step 1),
  *   soft_mask[b,h,i,j] = sigmoid((P_ij - lambda_i) / tau),  lambda[b,h,i] = lambda_i,
- * with lambda_i from 60 halvings of [min_j P_ij - tau (ln T + 2), max_j P_ij + tau (ln T + 2)]
- * that keep the half where sum_j sigmoid((P_ij - lambda)/tau) crosses k_sel (fp64; each row
- * then sums to k_sel up to rounding).  k_sel = T gives soft_mask = 1 and lambda = -inf.
+ * with lambda_i the root of sum_j sigmoid((P_ij - lambda)/tau) = k_sel in [min_j P_ij -
+ * tau (ln T + 2), max_j P_ij + tau (ln T + 2)], the value a binary search over that bracket
+ * converges to (fp64; each row then sums to k_sel up to rounding).  The search keeps the
+ * bracket and steps to the Newton point of the row sum when it lies inside, else to the
+ * midpoint, until a Newton step is below 2^-30 of lambda (at most 60 steps).  k_sel = T gives
+ * soft_mask = 1 and lambda = -inf.
  * soft_mask: device float[B,H,T,T]; lambda: device float[B,H,T]; both caller-owned.
  * tau must be positive and finite (else SLA2_ERR_INVALID_ARG). */
 int sla2_route_soft(const sla2_params *p, const sla2_tensors *t, float tau, float *soft_mask,

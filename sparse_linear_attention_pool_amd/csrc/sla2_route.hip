@@ -458,11 +458,17 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
 // by SoftTop-k, which keeps its row sum; section 6: a sigmoid with temperature tau and a
 // per-row offset lambda_i found by binary search so that each row sums to the Top-k count).
 // Input: P_c = softmax over the row of the router scores s_ij (SLA page, section 2 Q2 step 1),
-// the scores the hard Top-k ranks.  M_ij = sigmoid((P_ij - lambda_i) / tau).  The search
-// starts from [min P - tau (ln T + 2), max P + tau (ln T + 2)] (row sum above T - 1 at the
-// lower end, below 1 at the upper end) and halves it kSoftSteps times, keeping the half in
-// which the row sum crosses k_sel; lambda_i is the last midpoint.  k_sel = T gives M = 1 and
-// lambda = -inf.  One wave per query-block row, lane l holding the columns j = l + 64 m;
+// the scores the hard Top-k ranks.  M_ij = sigmoid((P_ij - lambda_i) / tau).  lambda_i is the
+// root of sum_j sigmoid((P_ij - lambda) / tau) = k_sel in [min P - tau (ln T + 2), max P +
+// tau (ln T + 2)] (row sum above T - 1 at the lower end, below 1 at the upper end).  The
+// bracket is kept as in a binary search, halved on the side where the row sum crosses
+// k_sel; each step tries the Newton point of the (strictly decreasing) row sum and takes it
+// when it falls inside the bracket, else the midpoint.  It stops after a Newton step below
+// 2^-30 of lambda (the point it lands on is then within about 2^-60), when the bracket is at
+// the rounding level, or after kSoftSteps steps: the root that kSoftSteps plain halvings reach
+// (to 2^-kSoftSteps of the bracket), in a few steps.  The fp64 search starts from the point
+// the same search finds in fp32, which is cheap and close.
+// k_sel = T gives M = 1 and lambda = -inf.  Lane l holds the columns j = l + 64 m of a row;
 // fp64 throughout, like the hard router.
 // ---------------------------------------------------------------------------------------
 constexpr int kSoftSteps = 60;
@@ -490,23 +496,10 @@ __device__ __forceinline__ double sigmoid_f64(double x) {
   return e / (1.0 + e);
 }
 
-template <int MAXS, int D>
-__global__ __launch_bounds__(64) void softtopk_kernel(const double* __restrict__ qhat,
-                                                      const double* __restrict__ khatT, int T, int topk,
-                                                      double inv_sqrt_d, double tau, float* __restrict__ soft_mask,
-                                                      float* __restrict__ lambda) {
-  const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
-  const double* qrow = qhat + ((size_t)bh * T + i) * D;
-  const double* kb = khatT + (size_t)bh * D * T;
-  double p[MAXS];
-  static_for<MAXS>([&](auto m) { p[m] = 0.0; });
-  for (int c = 0; c < D; ++c) {
-    const double qc = qrow[c];
-    static_for<MAXS>([&](auto m) {
-      const int j = 64 * m + lane;
-      if (j < T) p[m] = fma(qc, kb[(size_t)c * T + j], p[m]);
-    });
-  }
+// One row of the soft mask from its scores p[] (fp64, lane l holds columns l + 64 m).
+template <int MAXS>
+__device__ __forceinline__ void soft_row(double (&p)[MAXS], int T, int topk, double inv_sqrt_d, double tau,
+                                         float* __restrict__ mrow, float* __restrict__ lam_out, int lane) {
   // P_c: softmax over the row's T columns
   double mx = -INFINITY;
   static_for<MAXS>([&](auto m) {
@@ -533,44 +526,128 @@ __global__ __launch_bounds__(64) void softtopk_kernel(const double* __restrict__
 
   double lam = -INFINITY;
   if (topk < T) {
-    const double pad = tau * (log((double)T) + 2.0);
-    double lo = pmin - pad, hi = pmax + pad;
-    for (int it = 0; it < kSoftSteps; ++it) {
-      const double mid = 0.5 * (lo + hi);
-      double f = 0.0;
-      static_for<MAXS>([&](auto m) {
-        if (64 * m + lane < T) f += sigmoid_f64((p[m] - mid) / tau);
-      });
-      f = wave_sum_f64(f);
-      if (f > (double)topk) lo = mid;   // row sum too large: the offset must grow
-      else hi = mid;
+    const double pad = tau * (log((double)T) + 2.0), itau = 1.0 / tau, k = (double)topk;
+    double lo = pmin - pad, hi = pmax + pad, x = 0.5 * (lo + hi);
+    {
+      // a start near the root from the same search in fp32 (about 1e-7 relative)
+      const float itf = (float)itau, kf = (float)topk;
+      float lof = (float)lo, hif = (float)hi, xf = (float)x;
+      float pf[MAXS];
+      static_for<MAXS>([&](auto m) { pf[m] = (float)p[m]; });
+      for (int it = 0; it < kSoftSteps; ++it) {
+        float f = 0.f, df = 0.f;
+        static_for<MAXS>([&](auto m) {
+          if (64 * m + lane < T) {
+            const float sg = 1.f / (1.f + __expf((xf - pf[m]) * itf));
+            f += sg;
+            df += sg - sg * sg;
+          }
+        });
+        f = __shfl(wave_sum(f), 0);   // lane 0's value everywhere: the steps below are uniform
+        df = __shfl(wave_sum(df), 0) * itf;
+        if (f > kf) lof = xf;
+        else hif = xf;
+        if (f == kf) break;
+        float xn = xf + (f - kf) / df;
+        if (!(df > 0.f) || !(xn > lof && xn < hif)) xn = 0.5f * (lof + hif);
+        const bool done = fabsf(xn - xf) <= 0x1p-18f * fabsf(xn) || hif - lof <= 0x1p-21f * fmaxf(fabsf(lof), fabsf(hif));
+        xf = xn;
+        if (done) break;
+      }
+      if ((double)xf > lo && (double)xf < hi) x = (double)xf;
     }
-    lam = 0.5 * (lo + hi);
+    for (int it = 0; it < kSoftSteps; ++it) {
+      // row sum f(x) and its slope -f'(x) = sum sigma (1 - sigma) / tau
+      double f = 0.0, df = 0.0;
+      static_for<MAXS>([&](auto m) {
+        if (64 * m + lane < T) {
+          const double sg = sigmoid_f64((p[m] - x) * itau);
+          f += sg;
+          df += sg - sg * sg;
+        }
+      });
+      f = wave_sum_f64(f);   // identical on every lane: the steps below are uniform
+      df = wave_sum_f64(df) * itau;
+      if (f > k) lo = x;     // row sum too large: the offset must grow
+      else hi = x;
+      if (f == k) break;
+      double xn = x + (f - k) / df;
+      if (!(df > 0.0) || !(xn > lo && xn < hi)) xn = 0.5 * (lo + hi);
+      // a Newton step this small leaves an error about its square (the row sum's own rounding
+      // keeps later steps near 1e-16 relative, so a test at the rounding level would not stop)
+      const bool done = fabs(xn - x) <= 0x1p-30 * fabs(xn) || hi - lo <= 0x1p-52 * fmax(fabs(lo), fabs(hi));
+      x = xn;
+      if (done) break;
+    }
+    lam = x;
   }
-  float* mrow = soft_mask + ((size_t)bh * T + i) * T;
   static_for<MAXS>([&](auto m) {
     const int j = 64 * m + lane;
     if (j < T) mrow[j] = topk < T ? (float)sigmoid_f64((p[m] - lam) / tau) : 1.f;
   });
-  if (lane == 0) lambda[(size_t)bh * T + i] = (float)lam;
+  if (lane == 0) *lam_out = (float)lam;
+}
+
+// Four waves per workgroup, ROWS rows per wave.  The projected keys pass through LDS in
+// chunks of kSoftChunk features (at most 64 KB of fp64), loaded by the whole workgroup and
+// read by every row.
+template <int MAXS, int D>
+constexpr int kSoftChunk = 8192 / (64 * MAXS) < D ? 8192 / (64 * MAXS) : D;
+
+template <int MAXS, int D, int ROWS>
+__global__ __launch_bounds__(256) void softtopk_kernel(const double* __restrict__ qhat,
+                                                       const double* __restrict__ khatT, int T, int topk,
+                                                       double inv_sqrt_d, double tau, float* __restrict__ soft_mask,
+                                                       float* __restrict__ lambda) {
+  constexpr int CH = kSoftChunk<MAXS, D>, TP = 64 * MAXS;   // chunk features, padded row length
+  static_assert(D % CH == 0, "chunks tile the features");
+  __shared__ double kt[CH * TP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = (blockIdx.x * 4 + w) * ROWS, bh = blockIdx.y;
+  const double* kb = khatT + (size_t)bh * D * T;
+  double p[ROWS][MAXS];
+  static_for<ROWS>([&](auto r) { static_for<MAXS>([&](auto m) { p[r][m] = 0.0; }); });
+  for (int c0 = 0; c0 < D; c0 += CH) {
+    __syncthreads();   // the previous chunk is consumed
+    for (int e = tid; e < CH * TP; e += 256) {
+      const int c = e / TP, j = e % TP;
+      kt[e] = j < T ? kb[(size_t)(c0 + c) * T + j] : 0.0;
+    }
+    __syncthreads();
+    for (int c = 0; c < CH; ++c) {
+      double kv[MAXS];
+      static_for<MAXS>([&](auto m) { kv[m] = kt[c * TP + 64 * m + lane]; });
+      static_for<ROWS>([&](auto r) {
+        const double qc = qhat[((size_t)bh * T + min(i0 + (int)r, T - 1)) * D + c0 + c];
+        static_for<MAXS>([&](auto m) { p[r][m] = fma(qc, kv[m], p[r][m]); });
+      });
+    }
+  }
+  static_for<ROWS>([&](auto r) {
+    const int i = i0 + r;
+    if (i < T)
+      soft_row<MAXS>(p[r], T, topk, inv_sqrt_d, tau, soft_mask + ((size_t)bh * T + i) * T, lambda + (size_t)bh * T + i,
+                     lane);
+  });
 }
 
 template <int D>
 static void launch_softtopk(const Geometry& g, const Workspace& ws, double tau, float* soft_mask, float* lambda,
                             hipStream_t s) {
-  const dim3 grid(g.T, g.BH);
   const int S = (g.T + 63) / 64;
   const double isd = 1.0 / sqrt((double)g.D);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(64), 0, s, ws.qhat, ws.khatT, g.T, g.topk, isd, tau, soft_mask, lambda);
+  auto go = [&](auto kern, int rows) {   // four waves of `rows` rows per workgroup
+    hipLaunchKernelGGL(kern, dim3((g.T + 4 * rows - 1) / (4 * rows), g.BH), dim3(256), 0, s, ws.qhat, ws.khatT, g.T,
+                       g.topk, isd, tau, soft_mask, lambda);
   };
-  if (S <= 1) go(softtopk_kernel<1, D>);
-  else if (S <= 2) go(softtopk_kernel<2, D>);
-  else if (S <= 4) go(softtopk_kernel<4, D>);
-  else if (S <= 8) go(softtopk_kernel<8, D>);
-  else if (S <= 16) go(softtopk_kernel<16, D>);
-  else if (S <= 32) go(softtopk_kernel<32, D>);
-  else go(softtopk_kernel<64, D>);
+  // up to 32 scores per lane across the rows of a wave
+  if (S <= 1) go(softtopk_kernel<1, D, 4>, 4);
+  else if (S <= 2) go(softtopk_kernel<2, D, 4>, 4);
+  else if (S <= 4) go(softtopk_kernel<4, D, 4>, 4);
+  else if (S <= 8) go(softtopk_kernel<8, D, 4>, 4);
+  else if (S <= 16) go(softtopk_kernel<16, D, 2>, 2);
+  else if (S <= 32) go(softtopk_kernel<32, D, 1>, 1);
+  else go(softtopk_kernel<64, D, 1>, 1);
 }
 
 hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
