@@ -28,8 +28,8 @@
 // operand is the tile the sparse branch's dV product reads.
 //
 // Kernels: bwd_prep_kernel (per-token terms and the transposed operand tiles), the column sums
-// G_tot and dZ_tot, bwd_query_kernel (dQ), bwd_key_kernel (dK~, dV), then the key-smoothing
-// mean and dalpha.  Both main kernels copy each pair's tiles into LDS with direct-to-LDS loads
+// G_tot and dZ_tot, bwd_query_kernel (dQ), bwd_key_kernel (dK~ with its column sums per key
+// block, dV), then the key-smoothing mean, dK and dalpha.  Both main kernels copy each pair's tiles into LDS with direct-to-LDS loads
 // while the previous pair is processed (two stages), and run the products on the bf16
 // 16x16x32 matrix cores (the scores on the e4m3 16x16x128 ones, as the forward computed them).
 #include <math.h>
@@ -45,7 +45,7 @@ constexpr int kD = 128;
 constexpr int kNT = 256;
 constexpr int kTTile = kD * kBlock * 2;   // bytes of one transposed bf16 tile: 128 rows x 64
 constexpr int kRec = 256;                 // floats per query block in the key side's record
-constexpr int kGChunk = 16;               // query blocks per partial of G_tot
+constexpr int kGChunk = 8;                // query blocks per partial of G_tot
 constexpr int kQReadAhead = 1;            // feature tiles whose LDS operands are read ahead (query side)
 constexpr int kKReadAhead = 2;            // the same on the key side
 
@@ -163,14 +163,14 @@ struct BwdArgs {
   float* dZ_tot;           // [BH, D]
   float* dalpha_part;      // [BH, T, D]
   float* dkt;              // [BH, 64T, D] dK~ (fp32)
-  float* colsum_part;      // [BH, NCH, D]
+  float* colsum_part;      // [BH, T, D] column sums of dK~ over each key block
   float* dk_mean;          // [BH, D]
   // outputs
   uint16_t* dq;            // bf16 [BH, N, D]
   uint16_t* dk;
   uint16_t* dv;
   float* dalpha;           // [H, D]
-  int B, H, N, T, topk, nch, pg, nblocks;
+  int B, H, N, T, topk, pg, nblocks;
   int smooth_k;
 };
 
@@ -981,110 +981,115 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
         }
   }
   __syncthreads();
-  if (!sparse) return;
-
-  // phi(k~) of this lane's key: as B operand (features 32s + 8g + e) and at the accumulator
-  // features 16at + 4g + r
-  bf16x8 pko[4];
-  float pk[8][4];
-  {
-    const uint16_t* kr = A.k + ((size_t)bh * N + min(kk, N - 1)) * kD;
-    const float* mu = A.k_mean + (size_t)bh * kD;
-    float fb[4][8];
-    float mx = -INFINITY;
+  __shared__ float csum[4][kD];   // per sparse wave: column sums of dK~ over its 16 keys
+  if (sparse) {
+    // phi(k~) of this lane's key: as B operand (features 32s + 8g + e) and at the accumulator
+    // features 16at + 4g + r
+    bf16x8 pko[4];
+    float pk[8][4];
+    {
+      const uint16_t* kr = A.k + ((size_t)bh * N + min(kk, N - 1)) * kD;
+      const float* mu = A.k_mean + (size_t)bh * kD;
+      float fb[4][8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * g);
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fb[s][2 * e] = bf16_lo(ww[e]) - mu[32 * s + 8 * g + 2 * e];
-        fb[s][2 * e + 1] = bf16_hi(ww[e]) - mu[32 * s + 8 * g + 2 * e + 1];
+        for (int e = 0; e < 4; ++e) {
+          fb[s][2 * e] = bf16_lo(ww[e]) - mu[32 * s + 8 * g + 2 * e];
+          fb[s][2 * e + 1] = bf16_hi(ww[e]) - mu[32 * s + 8 * g + 2 * e + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fb[s][e]);
+      }
+      mx = rows4_max(mx);
+      float sm = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          fb[s][e] = __expf(fb[s][e] - mx);
+          sm += fb[s][e];
+        }
+      const float rsum = 1.f / rows4_sum(sm);
+      const float is = kok ? rsum : 0.f;   // pad keys: phi(k) = 0
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fb[s][e] *= is;
+        pko[s] = pack8(fb[s]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fb[s][e]);
-    }
-    mx = rows4_max(mx);
-    float sm = 0.f;
+      for (int at = 0; at < 8; ++at) {
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(kr + 16 * at + 4 * g);
+        const float raw[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        fb[s][e] = __expf(fb[s][e] - mx);
-        sm += fb[s][e];
+        for (int rr = 0; rr < 4; ++rr) pk[at][rr] = __expf(raw[rr] - mu[16 * at + 4 * g + rr] - mx) * is;
       }
-    const float rsum = 1.f / rows4_sum(sm);
-    const float is = kok ? rsum : 0.f;   // pad keys: phi(k) = 0
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fb[s][e] *= is;
-      pko[s] = pack8(fb[s]);
     }
+    // dphi(k)^T = dh_j V^T + dz_j; dV^T = alpha dV_sparse^T + dh_j^T phi(k)^T
+    float dphi[8][4], dotp = 0.f;
 #pragma unroll
     for (int at = 0; at < 8; ++at) {
-      const u32x2 wv = *reinterpret_cast<const u32x2*>(kr + 16 * at + 4 * g);
-      const float raw[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) pk[at][rr] = __expf(raw[rr] - mu[16 * at + 4 * g + rr] - mx) * is;
+      for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), ko.v[s], t);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        dphi[at][rr] = t[rr] + dzS[16 * at + 4 * g + rr];
+        dotp = fmaf(pk[at][rr], dphi[at][rr], dotp);
+      }
     }
-  }
-  // dphi(k)^T = dh_j V^T + dz_j; dV^T = alpha dV_sparse^T + dh_j^T phi(k)^T
-  float dphi[8][4], dotp = 0.f;
+    dotp = rows4_sum(dotp);
 #pragma unroll
-  for (int at = 0; at < 8; ++at) {
-    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 8; ++ct) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), ko.v[s], t);
+      for (int rr = 0; rr < 4; ++rr) acc[ct][rr] *= alS[16 * ct + 4 * g + rr];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      dphi[at][rr] = t[rr] + dzS[16 * at + 4 * g + rr];
-      dotp = fmaf(pk[at][rr], dphi[at][rr], dotp);
+      for (int s = 0; s < 4; ++s) acc[ct] = mfma_bf16(DHT.op(16 * ct + l16, 32 * s + 8 * g), pko[s], acc[ct]);
     }
-  }
-  dotp = rows4_sum(dotp);
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) acc[ct][rr] *= alS[16 * ct + 4 * g + rr];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[ct] = mfma_bf16(DHT.op(16 * ct + l16, 32 * s + 8 * g), pko[s], acc[ct]);
-  }
-  if (kok) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       f32x4 o;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) o[rr] = acc[8 + ct][rr] + pk[ct][rr] * (dphi[ct][rr] - dotp);
-      *reinterpret_cast<f32x4*>(A.dkt + ((size_t)bh * T * kBlock + kk) * kD + 16 * ct + 4 * g) = o;
-      u32x2 sv;
-      sv.x = pack_bf16x2(acc[ct][0], acc[ct][1]);
-      sv.y = pack_bf16x2(acc[ct][2], acc[ct][3]);
-      *reinterpret_cast<u32x2*>(A.dv + ((size_t)bh * N + kk) * kD + 16 * ct + 4 * g) = sv;
+      for (int rr = 0; rr < 4; ++rr) o[rr] = kok ? acc[8 + ct][rr] + pk[ct][rr] * (dphi[ct][rr] - dotp) : 0.f;
+      if (kok) {
+        *reinterpret_cast<f32x4*>(A.dkt + ((size_t)bh * T * kBlock + kk) * kD + 16 * ct + 4 * g) = o;
+        u32x2 sv;
+        sv.x = pack_bf16x2(acc[ct][0], acc[ct][1]);
+        sv.y = pack_bf16x2(acc[ct][2], acc[ct][3]);
+        *reinterpret_cast<u32x2*>(A.dv + ((size_t)bh * N + kk) * kD + 16 * ct + 4 * g) = sv;
+      }
+      // sums over this wave's 16 keys (the lanes of a 16-lane row) for the key-smoothing mean
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float cs = row16_sum(o[rr]);
+        if (l16 == 0) csum[wc][16 * ct + 4 * g + rr] = cs;
+      }
     }
   }
-}
-
-// Column sums of dK~ over chunks of 256 tokens, then per head: mean over the N tokens.
-__global__ __launch_bounds__(256) void bwd_colsum_kernel(BwdArgs A) {
-  __shared__ float red[2][kD];
-  const int ch = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int c = tid & (kD - 1), half = tid >> 7;
-  float s = 0.f;
-  const int r0 = 256 * ch, r1 = min(A.N, r0 + 256);
-  for (int r = r0 + half; r < r1; r += 2) s += A.dkt[((size_t)bh * A.T * 64 + r) * kD + c];
-  red[half][c] = s;
   __syncthreads();
-  if (tid < kD) A.colsum_part[((size_t)bh * A.nch + ch) * kD + tid] = red[0][tid] + red[1][tid];
+  if (tid < kD)
+    A.colsum_part[((size_t)bh * T + j) * kD + tid] = (csum[0][tid] + csum[1][tid]) + (csum[2][tid] + csum[3][tid]);
 }
 
-// mean over the N tokens of dK~ (zero without key smoothing), from the chunk sums in fixed order
-__global__ __launch_bounds__(128) void bwd_mean_kernel(BwdArgs A) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+// mean over the N tokens of dK~ (zero without key smoothing) from the key blocks' column sums:
+// 8 partial sums per feature over interleaved blocks, combined in fixed order
+__global__ __launch_bounds__(1024) void bwd_mean_kernel(BwdArgs A) {
+  __shared__ float red[8][kD];
+  const int bh = blockIdx.x, c = threadIdx.x & (kD - 1), u = threadIdx.x >> 7;
   float s = 0.f;
-  if (A.smooth_k)
-    for (int ch = 0; ch < A.nch; ++ch) s += A.colsum_part[((size_t)bh * A.nch + ch) * kD + c];
-  A.dk_mean[(size_t)bh * kD + c] = A.smooth_k ? s / (float)A.N : 0.f;
+#pragma unroll 8
+  for (int j = u; j < A.T; j += 8) s += A.colsum_part[((size_t)bh * A.T + j) * kD + c];
+  red[u][c] = s;
+  __syncthreads();
+  if (u == 0) {
+    float t = 0.f;
+    for (int k = 0; k < 8; ++k) t += red[k][c];
+    A.dk_mean[(size_t)bh * kD + c] = A.smooth_k ? t / (float)A.N : 0.f;
+  }
 }
 
 // dK = dK~ - mean: 16 bytes of a row per thread
@@ -1111,6 +1116,7 @@ __global__ __launch_bounds__(1024) void bwd_dalpha_kernel(BwdArgs A) {
   float s = 0.f;
   for (int b = 0; b < A.B; ++b) {
     const int bh = b * A.H + hidx;
+#pragma unroll 8
     for (int i = u; i < A.T; i += 8) s += A.dalpha_part[((size_t)bh * A.T + i) * kD + c];
   }
   red[u][c] = s;
@@ -1126,7 +1132,6 @@ __global__ __launch_bounds__(1024) void bwd_dalpha_kernel(BwdArgs A) {
 
 size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
   const size_t BH = g.BH, T = g.T, D = g.D, N = g.N;
-  const size_t nch = (g.N + 255) / 256;
   const size_t pg = (g.T + kGChunk - 1) / kGChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1156,7 +1161,7 @@ size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
   w.dZ_tot = (float*)take(BH * D * 4);
   w.dalpha_part = (float*)take(BH * T * D * 4);
   w.dkt = (float*)take(BH * T * 64 * D * 4);
-  w.colsum_part = (float*)take(BH * nch * D * 4);
+  w.colsum_part = (float*)take(BH * T * D * 4);
   w.dk_mean = (float*)take(BH * D * 4);
   if (ws) *ws = w;
   return off;
@@ -1213,7 +1218,6 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   A.N = g.N;
   A.T = g.T;
   A.topk = g.topk;
-  A.nch = (g.N + 255) / 256;
   A.pg = (g.T + kGChunk - 1) / kGChunk;
   A.nblocks = g.BH * g.T;
   A.smooth_k = g.smooth_k ? 1 : 0;
@@ -1225,8 +1229,7 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_query_kernel, dim3(A.nblocks), dim3(kNT2), 0, s, A);
   hipLaunchKernelGGL(bwd_key_kernel, dim3(A.nblocks), dim3(kNT2), 0, s, A);
-  hipLaunchKernelGGL(bwd_colsum_kernel, dim3(A.nch, g.BH), dim3(256), 0, s, A);
-  hipLaunchKernelGGL(bwd_mean_kernel, dim3(g.BH), dim3(128), 0, s, A);
+  hipLaunchKernelGGL(bwd_mean_kernel, dim3(g.BH), dim3(1024), 0, s, A);
   hipLaunchKernelGGL(bwd_dk_kernel, dim3((g.N * 16 + 255) / 256, g.BH), dim3(256), 0, s, A);
   hipLaunchKernelGGL(bwd_dalpha_kernel, dim3(g.H), dim3(1024), 0, s, A);
   return hipGetLastError();

@@ -58,13 +58,13 @@ struct BwdWorkspace {
   int32_t* inv;         // [BH, T, T] per key block: the query blocks routing to it, ascending
   int32_t* inv_cnt;     // [BH, T]
   float* dZ;            // [BH, T, D] dZ_i
-  float* gpart;         // [BH, ceil(T/16), D, D] partials of G_tot
-  float* zpart;         // [BH, ceil(T/16), D] partials of dZ_tot
+  float* gpart;         // [BH, ceil(T/8), D, D] partials of G_tot
+  float* zpart;         // [BH, ceil(T/8), D] partials of dZ_tot
   float* g_tot;         // [BH, D, D] sum over tokens of (phi(q)/den)^T dO
   float* dZ_tot;        // [BH, D]
   float* dalpha_part;   // [BH, T, D]
   float* dkt;           // [BH, 64T, D] dK~ in fp32, before the key-smoothing correction
-  float* colsum_part;   // [BH, ceil(N/256), D]
+  float* colsum_part;   // [BH, T, D] column sums of dK~ over each key block
   float* dk_mean;       // [BH, D]
 };
 
