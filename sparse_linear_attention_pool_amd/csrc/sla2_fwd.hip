@@ -730,8 +730,9 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.nblocks = g.BH * g.T;
     A.eps = g.eps;
     const bool lut_reg = g.topk <= kLutReg;
-    // FP8: two query tiles per wave, two waves per workgroup; native bf16 Q.K: one tile per
-    // wave, four waves (its 16 KB key tiles leave no LDS for a second tile set).
+    // One query tile per wave, four waves per workgroup (two workgroups per CU in FP8 mode).
+    // Two tiles per wave (QT = 2: every LDS operand read serving both) measured 30% slower at
+    // C2: half the waves per CU leave too little to overlap the copies and the barriers.
     if (g.fp8) {
       if (lut_reg) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
       else hipLaunchKernelGGL((fwd_mfma_kernel<true, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
