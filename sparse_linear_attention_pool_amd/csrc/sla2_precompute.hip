@@ -26,12 +26,33 @@ namespace sla2 {
 // Thread (c = tid % 16, r0 = tid / 16) holds columns 8c..8c+7 of rows r0 + 16p, p = 0..3
 // (a 16-lane row of a wave holds one token); the next block's K and V are loaded while the
 // current one is processed.
-// phi and V go to LDS row-major (row stride 65 words, conflict-free 16-bit column gathers);
-// wave w computes the 4 x 4 tiles (a-tiles 4*(w/2).., c-tiles 4*(w%2)..) of
-// D[a][c] = sum_t phi[t][a] V[t][c] with v_mfma_f32_16x16x32_bf16 over 64 tokens.  phi is
+// phi and V go to LDS row-major (row stride 68 words); the operands whose contraction index
+// runs down those rows (tokens) are read with the transposing LDS reads.  Wave w computes the
+// 4 x 4 tiles (a-tiles 4*(w/2).., c-tiles 4*(w%2)..) of D[a][c] = sum_t phi[t][a] V[t][c] with
+// v_mfma_f32_16x16x32_bf16 over 64 tokens.  phi is
 // split into bf16 hi + lo parts (phi - hi rounded again), so the product carries phi to about
 // 2^-16 relative although the matrix cores take bf16; V is bf16 already.
 // ---------------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, the four
+// 16-bit values that source lane i loads from its address, M[i][0..3], reach lane j as
+// M[4k + j / 4][j % 4], k = 0..3.  With lane i of the group addressing X[r0 + i / 4][c0 + 4 (i %
+// 4)] of a row-major 16-bit matrix X (row stride `ld` elements, 8-byte aligned rows), lane j
+// receives X[r0 + k][c0 + j], k = 0..3: four consecutive rows of column c0 + j, the k-run of a
+// matrix-core operand whose contraction index runs down the rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(x + (r0 + (i >> 2)) * ld + c0 + 4 * (i & 3)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// the 8-element operand of rows r0 .. r0 + 7 at column c0 + j (two transposing reads)
+__device__ __forceinline__ bf16x8 lds_op_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
+  const u32x2 a = lds_read_tr16(x, ld, r0, c0, i), b = lds_read_tr16(x, ld, r0 + 4, c0, i);
+  return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 template <bool FP8, bool STORE>
 __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
@@ -39,7 +60,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
     float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8, float* __restrict__ zblk) {
   constexpr int D = 128;
-  constexpr int SW = 65;  // LDS row stride in 32-bit words
+  constexpr int SW = 68;  // LDS row stride in 32-bit words (8-byte aligned rows for the transposing reads)
   __shared__ uint32_t phiS[64 * SW];
   __shared__ uint32_t phiLoS[64 * SW];
   __shared__ uint32_t vS[64 * SW];
@@ -198,26 +219,15 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // operands of tokens t0 .. t0 + 7 (the contraction index, down the LDS rows)
       const int t0 = 32 * ks + 8 * g;
       bf16x8 Bv[4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int cc = 16 * (nbase + ni) + l16;
-        uint16_t e16[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e16[e] = v16[(t0 + e) * 2 * SW + cc];
-        Bv[ni] = __builtin_bit_cast(bf16x8, e16);
-      }
+      for (int ni = 0; ni < 4; ++ni) Bv[ni] = lds_op_tr16(v16, 2 * SW, t0, 16 * (nbase + ni), l16);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const int a = 16 * (mbase + mi) + l16;
-        uint16_t e16[8], l16v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          e16[e] = phi16[(t0 + e) * 2 * SW + a];
-          l16v[e] = philo16[(t0 + e) * 2 * SW + a];
-        }
-        const bf16x8 Ah = __builtin_bit_cast(bf16x8, e16), Al = __builtin_bit_cast(bf16x8, l16v);
+        const bf16x8 Ah = lds_op_tr16(phi16, 2 * SW, t0, 16 * (mbase + mi), l16);
+        const bf16x8 Al = lds_op_tr16(philo16, 2 * SW, t0, 16 * (mbase + mi), l16);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           f32x4& dst = STORE ? acc[mi][ni] : hs[mi][ni];
@@ -245,18 +255,16 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     }
 
     // V of this block, transposed: vt[j][c][32s + 8gg + e] = V[key][c] with
-    // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4)
+    // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4).  Each 16-lane group
+    // takes 16 columns of one (s, gg); the four groups of a wave take gg = 0..3 of the same
+    // columns, so each column receives 64 contiguous bytes per store.
     uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
     static_for<4>([&](auto pp) {
-      const int qd = tid + 256 * pp;
-      const int cc = qd >> 3, s = (qd >> 2) & 1, gg = qd & 3;
-      uint16_t e16[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 32 * s + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
-        e16[e] = v16[key * 2 * SW + cc];
-      }
-      *reinterpret_cast<u32x4*>(vtj + (size_t)cc * kBlock + 32 * s + 8 * gg) = __builtin_bit_cast(u32x4, e16);
+      const int ct = 2 * pp + (w >> 1), s = w & 1, gg = g;
+      const u32x2 lo4 = lds_read_tr16(v16, 2 * SW, 32 * s + 4 * gg, 16 * ct, l16);
+      const u32x2 hi4 = lds_read_tr16(v16, 2 * SW, 32 * s + 16 + 4 * gg, 16 * ct, l16);
+      *reinterpret_cast<u32x4*>(vtj + (size_t)(16 * ct + l16) * kBlock + 32 * s + 8 * gg) =
+          u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
     });
     __syncthreads();
   }
