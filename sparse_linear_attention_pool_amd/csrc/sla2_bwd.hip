@@ -36,6 +36,7 @@
 
 #include "sla2_device.hpp"
 #include "sla2_internal.hpp"
+#include "sla2_lds.hpp"
 
 namespace sla2 {
 
@@ -112,6 +113,16 @@ __device__ __forceinline__ int vt_pos(int x) {
   return 32 * s + 8 * gg + 4 * h + e;
 }
 
+// The operand with rows c = c0 + l%16 of dO^T and the k-run of query half s in the packed order
+// (queries 32s + 4g + 0..3, then 32s + 16 + 4g + 0..3), read from the staged dO rows (256-byte
+// rows, swizzled) with transposing reads: the A operand of dV^T = dO^T P and, identically laid
+// out, the B operand of the dh_j correction (phi(q)/den)^T dO.
+__device__ __forceinline__ bf16x8 dot_op(const uint8_t* dorows, int s, int c0, int l16, int g) {
+  const u32x2 a = lds_read_tr16_sw256(dorows, 32 * s + 4 * g, c0, l16);
+  const u32x2 b = lds_read_tr16_sw256(dorows, 32 * s + 16 + 4 * g, c0, l16);
+  return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 // 8 bf16 values as the B operand: v[4h + rr] from output tile 2s + h, row 4g + rr
 __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
   const uint32_t w[4] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
@@ -145,8 +156,6 @@ struct BwdArgs {
   const uint16_t* ol;      // [BH, N, D] O_l (bf16)
   const float* inv_den;    // [BH, 64T] 1 / den (0 when every block is routed)
   // backward workspace
-  uint16_t* dos;           // [BH, 64T, D] alpha * dO rows (pad rows 0)
-  uint16_t* dot;           // [BH, T, D, 64] dO^T per block, tokens at vt_pos
   uint16_t* q8t;           // [BH, T, D, 64] e4m3 values of Q8 (unscaled) transposed, vt_pos
   uint16_t* phqdt;         // [BH, T, D, 64] (phi(q) / den)^T, vt_pos
   uint16_t* k8t;           // [BH, T, D, 64] e4m3 values of K8 transposed, vt_pos
@@ -176,8 +185,8 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------------------------------
 // Per (head, 64-token block b), four threads per token (32 features each).  As a query block:
-// D_q, dden, the dalpha and dZ_i column sums, alpha dO rows, and the transposed tiles dO^T,
-// (phi(q)/den)^T and Q8^T.  As a key block: K8^T and phi(K~)^T.  Block 0 also writes the bf16
+// D_q, dden, the dalpha and dZ_i column sums, and the transposed tiles (phi(q)/den)^T and
+// Q8^T.  As a key block: K8^T and phi(K~)^T.  Block 0 also writes the bf16
 // image of H_tot with rows a.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
@@ -262,20 +271,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
   const float dden = -dd * inv_den;
   colsum(A.dalpha_part + ((size_t)bh * A.T + b) * kD);
 
-  // alpha dO rows and dO^T
-  {
-    uint16_t out[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      out[e] = f32_to_bf16(al[e] * dO[e]);
-      tr[(c0 + e) * kBlock + px] = f32_to_bf16(dO[e]);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      reinterpret_cast<u32x4*>(A.dos + prow * kD + c0)[u] = reinterpret_cast<const u32x4*>(out)[u];
-  }
-  flush(A.dot);
-
   // phi(q) / den and the column sums dZ_i = sum_q dden phi(q)
   {
     float f[32];
@@ -352,7 +347,8 @@ __global__ __launch_bounds__(64) void bwd_invlut_kernel(BwdArgs A) {
 // and of dZ_tot.  Wave w: rows a = 32w..32w+31.
 __global__ __launch_bounds__(256) void bwd_gtot_kernel(BwdArgs A) {
   __shared__ __attribute__((aligned(1024))) uint8_t sm[2 * kTTile];
-  const LTile<128> PT{sm}, OT{sm + kTTile};
+  const LTile<128> PT{sm};
+  const LTile<256> DO{sm + kTTile};   // dO rows of the block (rows past N: row N-1, times phi 0)
   const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   f32x4 acc[2][8];
@@ -365,12 +361,22 @@ __global__ __launch_bounds__(256) void bwd_gtot_kernel(BwdArgs A) {
     __syncthreads();
     const size_t tile = ((size_t)bh * A.T + b) * kD * kBlock;
     stage<128>(PT, reinterpret_cast<const uint8_t*>(A.phqdt + tile), 128, kD, tid);
-    stage<128>(OT, reinterpret_cast<const uint8_t*>(A.dot + tile), 128, kD, tid);
+    for (int x = tid; x < kBlock * 16; x += kNT) {
+      const int r = x >> 4, c = x & 15, tok = min(kBlock * b + r, A.N - 1);
+      *reinterpret_cast<u32x4*>(DO.chunk(r, c)) =
+          *reinterpret_cast<const u32x4*>(A.dout + ((size_t)bh * A.N + tok) * kD + 8 * c);
+    }
     __syncthreads();
 #pragma unroll
-    for (int at = 0; at < 2; ++at)
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 fa0 = PT.op(32 * w + l16, 32 * s + 8 * g), fa1 = PT.op(32 * w + 16 + l16, 32 * s + 8 * g);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc[at][ct] = mm<64>(PT, 32 * w + 16 * at, OT, 16 * ct, l16, g, acc[at][ct]);
+      for (int ct = 0; ct < 8; ++ct) {
+        const bf16x8 fo = dot_op(DO.p, s, 16 * ct, l16, g);
+        acc[0][ct] = mfma_bf16(fa0, fo, acc[0][ct]);
+        acc[1][ct] = mfma_bf16(fa1, fo, acc[1][ct]);
+      }
+    }
   }
   float* out = A.gpart + ((size_t)bh * A.pg + p) * kD * kD;
 #pragma unroll
@@ -719,27 +725,28 @@ __global__ __launch_bounds__(512, 1) void bwd_query_kernel(BwdArgs A) {
 // ---------------------------------------------------------------------------------------
 // Key side.  One workgroup of eight waves per (head, key block j), in two roles over the same
 // staged query tiles.  Per routing query block i:
-//   sparse waves (w < 4, keys 16w..16w+15, one per lane column): S = Q8 K8^T, dP = dO_s V^T,
-//     then dV^T += dO^T P and dK'^T += Q8^T dS (queries at vt_pos);
+//   sparse waves (w < 4, keys 16w..16w+15, one per lane column): S = Q8 K8^T, dP = dO (alpha
+//     V)^T, then dV^T += dO^T P and dK'^T += Q8^T dS (queries in the packed vt_pos order);
 //   correction waves (w >= 4): C[a][c] += (phi(q)/den)^T dO over rows a = 32(w - 4)..+31.
+// dO is staged once, as rows copied from the input; the dO^T operands come from the same tile
+// through transposing reads.
 // ---------------------------------------------------------------------------------------
 namespace klds {
 constexpr int Q8 = 0;                 // e4m3 rows of query block i      64 x 128 B
-constexpr int DOS = Q8 + 8192;        // alpha dO rows                    64 x 256 B
-constexpr int DOT = DOS + 16384;      // dO^T                             128 x 128 B
-constexpr int QT = DOT + 16384;       // Q8 values^T                      128 x 128 B
+constexpr int DO = Q8 + 8192;         // dO rows (the input)              64 x 256 B
+constexpr int QT = DO + 16384;        // Q8 values^T                      128 x 128 B
 constexpr int PT = QT + 16384;        // (phi(q)/den)^T                   128 x 128 B
 constexpr int REC = PT + 16384;       // lse[64], D_q[64], zeros          1 KB
 constexpr int STAGE = REC + 1024;
-static_assert(STAGE >= 2 * 2 * kD * kD, "the two dh_j images fit in a stage");
+static_assert(STAGE >= 2 * kD * kD, "a dh_j image fits in a stage");
 }  // namespace klds
 
 struct KSrc {
-  __amdgpu_buffer_rsrc_t q8, dos, dot, qt, pt, rec;
+  __amdgpu_buffer_rsrc_t q8, dout, qt, pt, rec;
 };
 
-// query block i's tiles into a stage: 9 16-byte copies per thread (10 in wave 0)
-__device__ __forceinline__ void k_dma(const KSrc& s, int i, int tid, uint8_t* st) {
+// query block i's tiles into a stage: 7 16-byte copies per thread (8 in wave 0)
+__device__ __forceinline__ void k_dma(const KSrc& s, int i, int N, int tid, uint8_t* st) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wofs = 1024 * w;
   {
     const int row = tid >> 3, pc = tid & 7;
@@ -747,12 +754,12 @@ __device__ __forceinline__ void k_dma(const KSrc& s, int i, int tid, uint8_t* st
   }
   static_for<2>([&](auto P) {
     const int qd = tid + kNT2 * P, row = qd >> 4, pc = qd & 15;
-    lds_dma(s.dos, st + klds::DOS + 8192 * P + wofs, row * 256 + 16 * (pc ^ (row & 15)), i * 16384);
+    const int tok = min(kBlock * i + row, N - 1);   // rows past N: a finite row, masked by P
+    lds_dma(s.dout, st + klds::DO + 8192 * P + wofs, tok * 256 + 16 * (pc ^ (row & 15)), 0);
   });
   static_for<2>([&](auto P) {
     const int qd = tid + kNT2 * P, row = qd >> 3, pc = qd & 7;
     const int vo = row * 128 + 16 * (pc ^ (row & 7));
-    lds_dma(s.dot, st + klds::DOT + 8192 * P + wofs, vo, i * kTTile);
     lds_dma(s.qt, st + klds::QT + 8192 * P + wofs, vo, i * kTTile);
     lds_dma(s.pt, st + klds::PT + 8192 * P + wofs, vo, i * kTTile);
   });
@@ -761,7 +768,7 @@ __device__ __forceinline__ void k_dma(const KSrc& s, int i, int tid, uint8_t* st
 
 struct KOps {
   i32x8 k8;          // sparse waves: e4m3 codes of features 32g..32g+31 of this lane's key
-  bf16x8 v[4];       // sparse waves: V of this lane's key, features 32s + 8g + e
+  bf16x8 v[4];       // sparse waves: alpha V of this lane's key, features 32s + 8g + e
 };
 
 // acc: sparse waves: [0..7] dV^T, [8..15] dK'^T (features 16ct + 4g + r of this lane's key);
@@ -784,7 +791,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
   if (x + 1 < cnt) {
     i_next = list_entry(inv_reg, invv, invG, x + 1);
     sq_next = A.q_scale[(size_t)bh * A.T + i_next];
-    k_dma(src, i_next, tid, next);
+    k_dma(src, i_next, A.N, tid, next);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -826,7 +833,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
     auto read_queries = [&](auto mt) {
       qr[mt] = lds_fp8_row(stg + klds::Q8, 16 * mt + l16, g);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) da[mt][s] = op256(stg + klds::DOS, 16 * mt + l16, s, g);
+      for (int s = 0; s < 4; ++s) da[mt][s] = op256(stg + klds::DO, 16 * mt + l16, s, g);
     };
     read_rec(0);
     read_queries(std::integral_constant<int, 0>{});
@@ -847,7 +854,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
     auto read_feat = [&](auto ct) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        fo[ct][s] = op128(stg + klds::DOT, 16 * ct + l16, s, g);
+        fo[ct][s] = dot_op(stg + klds::DO, s, 16 * ct, l16, g);
         fq[ct][s] = op128(stg + klds::QT, 16 * ct + l16, s, g);
       }
     };
@@ -870,7 +877,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
     bf16x8 fo[8][2];
     auto read_feat = [&](auto ct) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) fo[ct][s] = op128(stg + klds::DOT, 16 * ct + l16, s, g);
+      for (int s = 0; s < 2; ++s) fo[ct][s] = dot_op(stg + klds::DO, s, 16 * ct, l16, g);
     };
     static_for<kKReadAhead>([&](auto ct) { read_feat(ct); });
     static_for<8>([&](auto ct) {
@@ -911,8 +918,7 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
 
   KSrc src;
   src.q8 = rsrc(A.q8 + (size_t)bh * T * kBlock * kD, (size_t)T * kBlock * kD);
-  src.dos = rsrc(A.dos + (size_t)bh * T * kBlock * kD, (size_t)T * kBlock * kD * 2);
-  src.dot = rsrc(A.dot + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
+  src.dout = rsrc(A.dout + (size_t)bh * N * kD, (size_t)N * kD * 2);
   src.qt = rsrc(A.q8t + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
   src.pt = rsrc(A.phqdt + (size_t)bh * T * kD * kBlock, (size_t)T * kTTile);
   src.rec = rsrc(A.qrec + (size_t)bh * T * kRec, (size_t)T * kRec * 4);
@@ -921,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
   if (cnt > 0) {
     i = list_entry(inv_reg, invv, invG, 0);
     sq = A.q_scale[(size_t)bh * T + i];
-    k_dma(src, i, tid, smem0);
+    k_dma(src, i, N, tid, smem0);
   }
 
   KOps ko;
@@ -934,9 +940,18 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
     const u32x4 b = *reinterpret_cast<const u32x4*>(s8 + 16);
     ko.k8 = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      ko.v[s] = __builtin_bit_cast(bf16x8, kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + 32 * s + 8 * g)
-                                               : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < 4; ++s) {
+      const int c = 32 * s + 8 * g;
+      const u32x4 raw = kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + c) : u32x4{0, 0, 0, 0};
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(A.alpha + (size_t)hidx * kD + c);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(A.alpha + (size_t)hidx * kD + c + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = av[e] * ((e & 1) ? bf16_hi(rw[e >> 1]) : bf16_lo(rw[e >> 1]));
+      ko.v[s] = pack8(v8);   // dP = dO_s V^T = dO (alpha V)^T
+    }
   }
   const float ksc = A.k_scale[(size_t)bh * T + j];
   if (tid < kD) alS[tid] = A.alpha[(size_t)hidx * kD + tid];
@@ -963,7 +978,7 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
   // ---------------- epilogue
   // correction waves: dh_j = (G_tot - C) diag(1 - alpha) as bf16 images with rows a and rows c,
   // and dz_j
-  const LTile<256> DH{smem0}, DHT{smem0 + 2 * kD * kD};
+  const LTile<256> DH{smem0}, DHT{smem1};
   if (!sparse) {
     const int zt = tid - 4 * 64;
     if (zt < kD) dzS[zt] = A.dZ_tot[(size_t)bh * kD + zt] - dz;
@@ -1029,13 +1044,19 @@ __global__ __launch_bounds__(512, 1) void bwd_key_kernel(BwdArgs A) {
         for (int rr = 0; rr < 4; ++rr) pk[at][rr] = __expf(raw[rr] - mu[16 * at + 4 * g + rr] - mx) * is;
       }
     }
-    // dphi(k)^T = dh_j V^T + dz_j; dV^T = alpha dV_sparse^T + dh_j^T phi(k)^T
+    // dphi(k)^T = dh_j V^T + dz_j (V of this lane's key, unscaled); dV^T = alpha dV_sparse^T +
+    // dh_j^T phi(k)^T
+    bf16x8 vk[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      vk[s] = __builtin_bit_cast(bf16x8, kok ? *reinterpret_cast<const u32x4*>(A.v + ((size_t)bh * N + kk) * kD + 32 * s + 8 * g)
+                                             : u32x4{0, 0, 0, 0});
     float dphi[8][4], dotp = 0.f;
 #pragma unroll
     for (int at = 0; at < 8; ++at) {
       f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), ko.v[s], t);
+      for (int s = 0; s < 4; ++s) t = mfma_bf16(DH.op(16 * at + l16, 32 * s + 8 * g), vk[s], t);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         dphi[at][rr] = t[rr] + dzS[16 * at + 4 * g + rr];
@@ -1143,8 +1164,6 @@ size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
   w.os = (uint16_t*)take(BH * N * D * 2);
   w.ol = (uint16_t*)take(BH * N * D * 2);
   w.inv_den = (float*)take(BH * T * 64 * 4);
-  w.dos = (uint16_t*)take(BH * T * 64 * D * 2);
-  w.dot = (uint16_t*)take(BH * T * D * 64 * 2);
   w.q8t = (uint16_t*)take(BH * T * D * 64 * 2);
   w.phqdt = (uint16_t*)take(BH * T * D * 64 * 2);
   w.k8t = (uint16_t*)take(BH * T * D * 64 * 2);
@@ -1189,8 +1208,6 @@ hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   A.os = bw.os;
   A.ol = bw.ol;
   A.inv_den = bw.inv_den;
-  A.dos = bw.dos;
-  A.dot = bw.dot;
   A.q8t = bw.q8t;
   A.phqdt = bw.phqdt;
   A.k8t = bw.k8t;

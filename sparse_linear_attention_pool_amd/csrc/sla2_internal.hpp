@@ -46,8 +46,6 @@ struct BwdWorkspace {
   uint16_t* os;         // [BH, N, D] O_s of the forward (bf16)
   uint16_t* ol;         // [BH, N, D] O_l of the forward (bf16)
   float* inv_den;       // [BH, 64T] 1 / (phi(q).Z_i + eps) of the forward (0 with every block routed)
-  uint16_t* dos;        // [BH, 64T, D] alpha * dO in bf16 (rows past N zero)
-  uint16_t* dot;        // [BH, T, D, 64] dO transposed per block, tokens in the V^T tile order
   uint16_t* q8t;        // [BH, T, D, 64] e4m3 values of the Q codes, transposed likewise
   uint16_t* phqdt;      // [BH, T, D, 64] phi(q) / den, transposed likewise
   uint16_t* k8t;        // [BH, T, D, 64] e4m3 values of the K~ codes, transposed likewise

@@ -1,0 +1,33 @@
+// Transposing LDS reads (gfx950 ds_read_b64_tr_b16) for matrix-core operands whose
+// contraction index runs down the rows of a row-major 16-bit tile in LDS.
+//
+// Within each group of 16 lanes, the four 16-bit values that source lane i loads from its own
+// address, M[i][0..3], reach lane j as M[4k + j / 4][j % 4], k = 0..3 (pinned on the GPU with
+// an in-bounds probe).  So with lane i of a group addressing X[r0 + i / 4][c0 + 4 (i % 4)],
+// lane j receives X[r0 + k][c0 + j], k = 0..3: four consecutive rows of column c0 + j, which is
+// half of the eight-element k-run a 16x16x32 bf16 operand lane holds.
+#pragma once
+#include "sla2_device.hpp"
+
+namespace sla2 {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Unswizzled tile, row stride `ld` elements (8-byte aligned rows): rows r0..r0+3, column c0 + j.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
+  return lds_tr16(x + (r0 + (i >> 2)) * ld + c0 + 4 * (i & 3));
+}
+
+// The same on a tile of 256-byte rows (128 elements) whose 16-byte chunk k of row r sits at
+// chunk k ^ (r % 16).
+__device__ __forceinline__ u32x2 lds_read_tr16_sw256(const uint8_t* tile, int r0, int c0, int i) {
+  const int row = r0 + (i >> 2), col = c0 + 4 * (i & 3);
+  return lds_tr16(tile + row * 256 + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7));
+}
+
+}  // namespace sla2

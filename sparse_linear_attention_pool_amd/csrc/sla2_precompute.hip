@@ -18,6 +18,7 @@
 
 #include "sla2_device.hpp"
 #include "sla2_internal.hpp"
+#include "sla2_lds.hpp"
 
 namespace sla2 {
 
@@ -33,20 +34,6 @@ namespace sla2 {
 // split into bf16 hi + lo parts (phi - hi rounded again), so the product carries phi to about
 // 2^-16 relative although the matrix cores take bf16; V is bf16 already.
 // ---------------------------------------------------------------------------------------
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, the four
-// 16-bit values that source lane i loads from its address, M[i][0..3], reach lane j as
-// M[4k + j / 4][j % 4], k = 0..3.  With lane i of the group addressing X[r0 + i / 4][c0 + 4 (i %
-// 4)] of a row-major 16-bit matrix X (row stride `ld` elements, 8-byte aligned rows), lane j
-// receives X[r0 + k][c0 + j], k = 0..3: four consecutive rows of column c0 + j, the k-run of a
-// matrix-core operand whose contraction index runs down the rows.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(x + (r0 + (i >> 2)) * ld + c0 + 4 * (i & 3)));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // the 8-element operand of rows r0 .. r0 + 7 at column c0 + j (two transposing reads)
 __device__ __forceinline__ bf16x8 lds_op_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
   const u32x2 a = lds_read_tr16(x, ld, r0, c0, i), b = lds_read_tr16(x, ld, r0 + 4, c0, i);
