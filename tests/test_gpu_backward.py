@@ -87,3 +87,27 @@ def test_backward_full_size_c4_sampled():
     inp = I.generate(w, with_dout=True)
     out = _run(w, inp)
     _check(w, inp, out, [(0, 0), (0, 7)])
+
+
+def test_backward_is_deterministic_and_training_forward_keeps_o():
+    """Two backward calls on the same inputs give the same bits (fixed reduction order, no
+    atomics), and a forward given the backward workspace (which also stores O_s, O_l, 1/den)
+    writes the same O, bit for bit, as one without it."""
+    import torch
+    from sparse_linear_attention_pool_amd import binding as Bn
+    w = I.make_workload("C4", grid=(4, 16, 64), H=2, seed=45, sparse_frac=0.25, name="determinism")
+    inp = I.generate(w, with_dout=True)
+    p = params_for(w)
+    dev = to_device(w, inp)
+    plain = Bn.allocate(p, "cuda", with_lse=True, per_block_stats=False)
+    Bn.forward(p, dev, plain)
+    bufs = Bn.allocate(p, "cuda", with_lse=True, per_block_stats=False, with_bwd=True)
+    Bn.forward(p, dev, bufs)
+    torch.cuda.synchronize()
+    assert torch.equal(plain["o"], bufs["o"]) and torch.equal(plain["lse"], bufs["lse"])
+    dout = torch.from_numpy(inp["dout"]).to(torch.bfloat16).cuda()
+    g1 = Bn.backward(p, dev, bufs, dout)
+    g2 = Bn.backward(p, dev, bufs, dout)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dalpha"):
+        assert torch.equal(g1[key], g2[key]), key
