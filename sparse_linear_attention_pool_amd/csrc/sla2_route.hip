@@ -224,6 +224,141 @@ __global__ __launch_bounds__(256) void project_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// SoftTop-k router mask (SLA2 page, section 4: for training the row's hard Top-k is replaced
+// by SoftTop-k, which keeps its row sum; section 6: a sigmoid with temperature tau and a
+// per-row offset lambda_i found by binary search so that each row sums to the Top-k count).
+// Input: P_c = softmax over the row of the router scores s_ij (SLA page, section 2 Q2 step 1),
+// the scores the hard Top-k ranks.  M_ij = sigmoid((P_ij - lambda_i) / tau).  lambda_i is the
+// root of sum_j sigmoid((P_ij - lambda) / tau) = k_sel in [min P - tau (ln T + 2), max P +
+// tau (ln T + 2)] (row sum above T - 1 at the lower end, below 1 at the upper end).  The
+// bracket is kept as in a binary search, halved on the side where the row sum crosses
+// k_sel; each step tries the Newton point of the (strictly decreasing) row sum and takes it
+// when it falls inside the bracket, else the midpoint.  It stops after a Newton step below
+// 2^-30 of lambda (the point it lands on is then within about 2^-60), when the bracket is at
+// the rounding level, or after kSoftSteps steps: the root that kSoftSteps plain halvings reach
+// (to 2^-kSoftSteps of the bracket), in a few steps.  The fp64 search starts from the point
+// the same search finds in fp32, which is cheap and close.
+// k_sel = T gives M = 1 and lambda = -inf.  Lane l holds the columns j = l + 64 m of a row;
+// fp64 throughout, like the hard router.
+// ---------------------------------------------------------------------------------------
+constexpr int kSoftSteps = 60;
+
+// Sum over the wave, then lane 0's value on every lane: a branch on the result is then
+// uniform even though the butterfly adds in a different order on each lane.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return __shfl(v, 0);
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;   // exact, so every lane holds the same value
+}
+__device__ __forceinline__ double wave_min_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmin(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double sigmoid_f64(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+// One row of the soft mask from its scores p[] (fp64, lane l holds columns l + 64 m).
+template <int MAXS>
+__device__ __forceinline__ void soft_row(double (&p)[MAXS], int T, int topk, double inv_sqrt_d, double tau,
+                                         float* __restrict__ mrow, float* __restrict__ lam_out, int lane) {
+  // P_c: softmax over the row's T columns
+  double mx = -INFINITY;
+  static_for<MAXS>([&](auto m) {
+    p[m] *= inv_sqrt_d;
+    if (64 * m + lane < T) mx = fmax(mx, p[m]);
+  });
+  mx = wave_max_f64(mx);
+  double z = 0.0;
+  static_for<MAXS>([&](auto m) {
+    p[m] = 64 * m + lane < T ? exp(p[m] - mx) : 0.0;
+    z += p[m];
+  });
+  z = wave_sum_f64(z);
+  double pmin = INFINITY, pmax = -INFINITY;
+  static_for<MAXS>([&](auto m) {
+    p[m] /= z;
+    if (64 * m + lane < T) {
+      pmin = fmin(pmin, p[m]);
+      pmax = fmax(pmax, p[m]);
+    }
+  });
+  pmin = wave_min_f64(pmin);
+  pmax = wave_max_f64(pmax);
+
+  double lam = -INFINITY;
+  if (topk < T) {
+    const double pad = tau * (log((double)T) + 2.0), itau = 1.0 / tau, k = (double)topk;
+    double lo = pmin - pad, hi = pmax + pad, x = 0.5 * (lo + hi);
+    {
+      // a start near the root from the same search in fp32 (about 1e-7 relative)
+      const float itf = (float)itau, kf = (float)topk;
+      float lof = (float)lo, hif = (float)hi, xf = (float)x;
+      float pf[MAXS];
+      static_for<MAXS>([&](auto m) { pf[m] = (float)p[m]; });
+      for (int it = 0; it < kSoftSteps; ++it) {
+        float f = 0.f, df = 0.f;
+        static_for<MAXS>([&](auto m) {
+          if (64 * m + lane < T) {
+            const float sg = 1.f / (1.f + __expf((xf - pf[m]) * itf));
+            f += sg;
+            df += sg - sg * sg;
+          }
+        });
+        f = __shfl(wave_sum(f), 0);   // lane 0's value everywhere: the steps below are uniform
+        df = __shfl(wave_sum(df), 0) * itf;
+        if (f > kf) lof = xf;
+        else hif = xf;
+        if (f == kf) break;
+        float xn = xf + (f - kf) / df;
+        if (!(df > 0.f) || !(xn > lof && xn < hif)) xn = 0.5f * (lof + hif);
+        const bool done = fabsf(xn - xf) <= 0x1p-18f * fabsf(xn) || hif - lof <= 0x1p-21f * fmaxf(fabsf(lof), fabsf(hif));
+        xf = xn;
+        if (done) break;
+      }
+      if ((double)xf > lo && (double)xf < hi) x = (double)xf;
+    }
+    for (int it = 0; it < kSoftSteps; ++it) {
+      // row sum f(x) and its slope -f'(x) = sum sigma (1 - sigma) / tau
+      double f = 0.0, df = 0.0;
+      static_for<MAXS>([&](auto m) {
+        if (64 * m + lane < T) {
+          const double sg = sigmoid_f64((p[m] - x) * itau);
+          f += sg;
+          df += sg - sg * sg;
+        }
+      });
+      f = wave_sum_f64(f);   // identical on every lane: the steps below are uniform
+      df = wave_sum_f64(df) * itau;
+      if (f > k) lo = x;     // row sum too large: the offset must grow
+      else hi = x;
+      if (f == k) break;
+      double xn = x + (f - k) / df;
+      if (!(df > 0.0) || !(xn > lo && xn < hi)) xn = 0.5 * (lo + hi);
+      // a Newton step this small leaves an error about its square (the row sum's own rounding
+      // keeps later steps near 1e-16 relative, so a test at the rounding level would not stop)
+      const bool done = fabs(xn - x) <= 0x1p-30 * fabs(xn) || hi - lo <= 0x1p-52 * fmax(fabs(lo), fabs(hi));
+      x = xn;
+      if (done) break;
+    }
+    lam = x;
+  }
+  static_for<MAXS>([&](auto m) {
+    const int j = 64 * m + lane;
+    if (j < T) mrow[j] = topk < T ? (float)sigmoid_f64((p[m] - lam) / tau) : 1.f;
+  });
+  if (lane == 0) *lam_out = (float)lam;
+}
+
+// ---------------------------------------------------------------------------------------
 // Scores + Top-k: one workgroup per (R query blocks, head), 256 threads.
 //
 // Phase 1: scores q_hat k_hat^T / sqrt(d) in fp64 on the matrix cores.  The A operand is the
@@ -238,6 +373,9 @@ __global__ __launch_bounds__(256) void project_kernel(
 // Keys equal to the final threshold are taken in increasing j until topk are chosen, which
 // gives the lower block index on ties.  The mask row and the ascending LUT row follow by
 // ballot compaction.
+//
+// Phase 3 (SOFT, for sla2_route_soft): one wave per row, the SoftTop-k mask and lambda of the
+// row (soft_row above) from the same fp64 scores, read back from LDS.
 // ---------------------------------------------------------------------------------------
 
 // Order-preserving map of a double to an unsigned key (-0.0 is taken as +0.0).
@@ -251,11 +389,18 @@ __device__ __forceinline__ int ballot_count(bool p) {
   return __popcll(__builtin_amdgcn_ballot_w64(p));
 }
 
-template <int R, int MAXS, int D>
+// The score a key was made from (score_key is a bijection onto its range).
+__device__ __forceinline__ double key_score(uint64_t key) {
+  const uint64_t u = (key >> 63) ? (key & 0x7fffffffffffffffull) : ~key;
+  return __longlong_as_double((long long)u);
+}
+
+template <int R, int MAXS, int D, bool SOFT>
 __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__ qhat,
                                                       const double* __restrict__ khatT, int T, int topk,
                                                       double inv_sqrt_d, int32_t* __restrict__ lut,
-                                                      uint8_t* __restrict__ mask) {
+                                                      uint8_t* __restrict__ mask, double tau,
+                                                      float* __restrict__ soft_mask, float* __restrict__ lambda) {
   constexpr int KS = D / 4;    // matrix-core steps over the channels
   constexpr int HS = KS / 2;   // steps per half tile
   extern __shared__ uint64_t keys_s[];   // [R][T]
@@ -395,40 +540,69 @@ __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__
       }
     });
   }
+
+  if constexpr (SOFT) {
+    for (int r = w; r < R; r += 4) {
+      if (i0 + r >= T) break;
+      double p[MAXS];
+      static_for<MAXS>([&](auto s) {
+        const int j = 64 * s + lane;
+        p[s] = j < T ? key_score(keys_s[r * T + j]) : 0.0;   // already divided by sqrt(d)
+      });
+      const size_t row = (size_t)bh * T + i0 + r;
+      soft_row<MAXS>(p, T, topk, 1.0, tau, soft_mask + row * T, lambda + row, lane);
+    }
+  }
 }
 
 // LDS for the score keys of one workgroup: R rows of T keys.
 constexpr size_t kTopkLdsBudget = 160 * 1024;
 
-template <int R, int MAXS, int D>
-static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+// Soft-mask arguments of the fused SoftTop-k phase (unused by the plain router).
+struct SoftOut {
+  double tau;
+  float* mask;
+  float* lambda;
+};
+
+template <int R, int MAXS, int D, bool SOFT>
+static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
+                          hipStream_t s) {
   const size_t lds = (size_t)R * g.T * sizeof(uint64_t);
   static bool attr_set = false;   // dynamic LDS above the 64 KB default
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D, SOFT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)kTopkLdsBudget);
     attr_set = true;
   }
   dim3 grid((g.T + R - 1) / R, g.BH);
-  hipLaunchKernelGGL((topk_kernel<R, MAXS, D>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
-                     1.0 / sqrt((double)g.D), t.lut, t.mask);
+  hipLaunchKernelGGL((topk_kernel<R, MAXS, D, SOFT>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
+                     1.0 / sqrt((double)g.D), t.lut, t.mask, so.tau, so.mask, so.lambda);
 }
 
 // Rows per workgroup R: 16 (one matrix-core tile) when the keys fit in the LDS budget, else
-// 8 or 4.  Candidate slots per lane MAXS: the smallest power of two >= ceil(T / 64).  T <= 4096
-// leaves the pairs below.
-template <int D>
-static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+// 8 or 4.  Candidate slots per lane MAXS: the smallest of 4, 8, 16, 24, 32, 64 that is at
+// least ceil(T / 64).  T <= 4096 leaves the pairs below.
+template <int D, bool SOFT>
+static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
+                        hipStream_t s) {
   int R = 16;
   while (R > 4 && (size_t)R * g.T * sizeof(uint64_t) > kTopkLdsBudget) R >>= 1;
   const int S = (g.T + 63) / 64;
-  if (R == 16 && S <= 4) launch_topk_s<16, 4, D>(g, t, ws, s);
-  else if (R == 16 && S <= 8) launch_topk_s<16, 8, D>(g, t, ws, s);
-  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D>(g, t, ws, s);
-  else if (R == 16) launch_topk_s<16, 32, D>(g, t, ws, s);
-  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D>(g, t, ws, s);
-  else if (R == 8) launch_topk_s<8, 64, D>(g, t, ws, s);
-  else launch_topk_s<4, 64, D>(g, t, ws, s);
+  // the soft phase runs long fp64 chains per row: above 8 slots per lane, 8 rows per workgroup
+  // leave room for two workgroups per CU
+  if (SOFT && S > 8 && R > 8) R = 8;
+  if (R == 16 && S <= 4) launch_topk_s<16, 4, D, SOFT>(g, t, ws, so, s);
+  else if (R == 16 && S <= 8) launch_topk_s<16, 8, D, SOFT>(g, t, ws, so, s);
+  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D, SOFT>(g, t, ws, so, s);
+  else if (R == 16 && S <= 24) launch_topk_s<16, 24, D, SOFT>(g, t, ws, so, s);
+  else if (R == 16) launch_topk_s<16, 32, D, SOFT>(g, t, ws, so, s);
+  else if (R == 8 && S <= 16) launch_topk_s<8, 16, D, SOFT>(g, t, ws, so, s);
+  else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT>(g, t, ws, so, s);
+  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT>(g, t, ws, so, s);
+  else if constexpr (SOFT) launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);   // 8 rows would spill
+  else if (R == 8) launch_topk_s<8, 64, D, SOFT>(g, t, ws, so, s);
+  else launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);
 }
 
 template <typename Tin, int D>
@@ -453,222 +627,28 @@ static void launch_route_typed(const Geometry& g, const sla2_tensors& t, const W
                      t.k_mean, mu_final, ws.qhat, ws.khatT);
 }
 
-// ---------------------------------------------------------------------------------------
-// SoftTop-k router mask (SLA2 page, section 4: for training the row's hard Top-k is replaced
-// by SoftTop-k, which keeps its row sum; section 6: a sigmoid with temperature tau and a
-// per-row offset lambda_i found by binary search so that each row sums to the Top-k count).
-// Input: P_c = softmax over the row of the router scores s_ij (SLA page, section 2 Q2 step 1),
-// the scores the hard Top-k ranks.  M_ij = sigmoid((P_ij - lambda_i) / tau).  lambda_i is the
-// root of sum_j sigmoid((P_ij - lambda) / tau) = k_sel in [min P - tau (ln T + 2), max P +
-// tau (ln T + 2)] (row sum above T - 1 at the lower end, below 1 at the upper end).  The
-// bracket is kept as in a binary search, halved on the side where the row sum crosses
-// k_sel; each step tries the Newton point of the (strictly decreasing) row sum and takes it
-// when it falls inside the bracket, else the midpoint.  It stops after a Newton step below
-// 2^-30 of lambda (the point it lands on is then within about 2^-60), when the bracket is at
-// the rounding level, or after kSoftSteps steps: the root that kSoftSteps plain halvings reach
-// (to 2^-kSoftSteps of the bracket), in a few steps.  The fp64 search starts from the point
-// the same search finds in fp32, which is cheap and close.
-// k_sel = T gives M = 1 and lambda = -inf.  Lane l holds the columns j = l + 64 m of a row;
-// fp64 throughout, like the hard router.
-// ---------------------------------------------------------------------------------------
-constexpr int kSoftSteps = 60;
-
-// Sum over the wave, then lane 0's value on every lane: a branch on the result is then
-// uniform even though the butterfly adds in a different order on each lane.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return __shfl(v, 0);
-}
-__device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;   // exact, so every lane holds the same value
-}
-__device__ __forceinline__ double wave_min_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmin(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ double sigmoid_f64(double x) {
-  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
-  const double e = exp(x);
-  return e / (1.0 + e);
-}
-
-// One row of the soft mask from its scores p[] (fp64, lane l holds columns l + 64 m).
-template <int MAXS>
-__device__ __forceinline__ void soft_row(double (&p)[MAXS], int T, int topk, double inv_sqrt_d, double tau,
-                                         float* __restrict__ mrow, float* __restrict__ lam_out, int lane) {
-  // P_c: softmax over the row's T columns
-  double mx = -INFINITY;
-  static_for<MAXS>([&](auto m) {
-    p[m] *= inv_sqrt_d;
-    if (64 * m + lane < T) mx = fmax(mx, p[m]);
-  });
-  mx = wave_max_f64(mx);
-  double z = 0.0;
-  static_for<MAXS>([&](auto m) {
-    p[m] = 64 * m + lane < T ? exp(p[m] - mx) : 0.0;
-    z += p[m];
-  });
-  z = wave_sum_f64(z);
-  double pmin = INFINITY, pmax = -INFINITY;
-  static_for<MAXS>([&](auto m) {
-    p[m] /= z;
-    if (64 * m + lane < T) {
-      pmin = fmin(pmin, p[m]);
-      pmax = fmax(pmax, p[m]);
-    }
-  });
-  pmin = wave_min_f64(pmin);
-  pmax = wave_max_f64(pmax);
-
-  double lam = -INFINITY;
-  if (topk < T) {
-    const double pad = tau * (log((double)T) + 2.0), itau = 1.0 / tau, k = (double)topk;
-    double lo = pmin - pad, hi = pmax + pad, x = 0.5 * (lo + hi);
-    {
-      // a start near the root from the same search in fp32 (about 1e-7 relative)
-      const float itf = (float)itau, kf = (float)topk;
-      float lof = (float)lo, hif = (float)hi, xf = (float)x;
-      float pf[MAXS];
-      static_for<MAXS>([&](auto m) { pf[m] = (float)p[m]; });
-      for (int it = 0; it < kSoftSteps; ++it) {
-        float f = 0.f, df = 0.f;
-        static_for<MAXS>([&](auto m) {
-          if (64 * m + lane < T) {
-            const float sg = 1.f / (1.f + __expf((xf - pf[m]) * itf));
-            f += sg;
-            df += sg - sg * sg;
-          }
-        });
-        f = __shfl(wave_sum(f), 0);   // lane 0's value everywhere: the steps below are uniform
-        df = __shfl(wave_sum(df), 0) * itf;
-        if (f > kf) lof = xf;
-        else hif = xf;
-        if (f == kf) break;
-        float xn = xf + (f - kf) / df;
-        if (!(df > 0.f) || !(xn > lof && xn < hif)) xn = 0.5f * (lof + hif);
-        const bool done = fabsf(xn - xf) <= 0x1p-18f * fabsf(xn) || hif - lof <= 0x1p-21f * fmaxf(fabsf(lof), fabsf(hif));
-        xf = xn;
-        if (done) break;
-      }
-      if ((double)xf > lo && (double)xf < hi) x = (double)xf;
-    }
-    for (int it = 0; it < kSoftSteps; ++it) {
-      // row sum f(x) and its slope -f'(x) = sum sigma (1 - sigma) / tau
-      double f = 0.0, df = 0.0;
-      static_for<MAXS>([&](auto m) {
-        if (64 * m + lane < T) {
-          const double sg = sigmoid_f64((p[m] - x) * itau);
-          f += sg;
-          df += sg - sg * sg;
-        }
-      });
-      f = wave_sum_f64(f);   // identical on every lane: the steps below are uniform
-      df = wave_sum_f64(df) * itau;
-      if (f > k) lo = x;     // row sum too large: the offset must grow
-      else hi = x;
-      if (f == k) break;
-      double xn = x + (f - k) / df;
-      if (!(df > 0.0) || !(xn > lo && xn < hi)) xn = 0.5 * (lo + hi);
-      // a Newton step this small leaves an error about its square (the row sum's own rounding
-      // keeps later steps near 1e-16 relative, so a test at the rounding level would not stop)
-      const bool done = fabs(xn - x) <= 0x1p-30 * fabs(xn) || hi - lo <= 0x1p-52 * fmax(fabs(lo), fabs(hi));
-      x = xn;
-      if (done) break;
-    }
-    lam = x;
-  }
-  static_for<MAXS>([&](auto m) {
-    const int j = 64 * m + lane;
-    if (j < T) mrow[j] = topk < T ? (float)sigmoid_f64((p[m] - lam) / tau) : 1.f;
-  });
-  if (lane == 0) *lam_out = (float)lam;
-}
-
-// Four waves per workgroup, ROWS rows per wave.  The projected keys pass through LDS in
-// chunks of kSoftChunk features (at most 64 KB of fp64), loaded by the whole workgroup and
-// read by every row.
-template <int MAXS, int D>
-constexpr int kSoftChunk = 8192 / (64 * MAXS) < D ? 8192 / (64 * MAXS) : D;
-
-template <int MAXS, int D, int ROWS>
-__global__ __launch_bounds__(256) void softtopk_kernel(const double* __restrict__ qhat,
-                                                       const double* __restrict__ khatT, int T, int topk,
-                                                       double inv_sqrt_d, double tau, float* __restrict__ soft_mask,
-                                                       float* __restrict__ lambda) {
-  constexpr int CH = kSoftChunk<MAXS, D>, TP = 64 * MAXS;   // chunk features, padded row length
-  static_assert(D % CH == 0, "chunks tile the features");
-  __shared__ double kt[CH * TP];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int i0 = (blockIdx.x * 4 + w) * ROWS, bh = blockIdx.y;
-  const double* kb = khatT + (size_t)bh * D * T;
-  double p[ROWS][MAXS];
-  static_for<ROWS>([&](auto r) { static_for<MAXS>([&](auto m) { p[r][m] = 0.0; }); });
-  for (int c0 = 0; c0 < D; c0 += CH) {
-    __syncthreads();   // the previous chunk is consumed
-    for (int e = tid; e < CH * TP; e += 256) {
-      const int c = e / TP, j = e % TP;
-      kt[e] = j < T ? kb[(size_t)(c0 + c) * T + j] : 0.0;
-    }
-    __syncthreads();
-    for (int c = 0; c < CH; ++c) {
-      double kv[MAXS];
-      static_for<MAXS>([&](auto m) { kv[m] = kt[c * TP + 64 * m + lane]; });
-      static_for<ROWS>([&](auto r) {
-        const double qc = qhat[((size_t)bh * T + min(i0 + (int)r, T - 1)) * D + c0 + c];
-        static_for<MAXS>([&](auto m) { p[r][m] = fma(qc, kv[m], p[r][m]); });
-      });
-    }
-  }
-  static_for<ROWS>([&](auto r) {
-    const int i = i0 + r;
-    if (i < T)
-      soft_row<MAXS>(p[r], T, topk, inv_sqrt_d, tau, soft_mask + ((size_t)bh * T + i) * T, lambda + (size_t)bh * T + i,
-                     lane);
-  });
-}
-
-template <int D>
-static void launch_softtopk(const Geometry& g, const Workspace& ws, double tau, float* soft_mask, float* lambda,
-                            hipStream_t s) {
-  const int S = (g.T + 63) / 64;
-  const double isd = 1.0 / sqrt((double)g.D);
-  auto go = [&](auto kern, int rows) {   // four waves of `rows` rows per workgroup
-    hipLaunchKernelGGL(kern, dim3((g.T + 4 * rows - 1) / (4 * rows), g.BH), dim3(256), 0, s, ws.qhat, ws.khatT, g.T,
-                       g.topk, isd, tau, soft_mask, lambda);
-  };
-  // up to 32 scores per lane across the rows of a wave
-  if (S <= 1) go(softtopk_kernel<1, D, 4>, 4);
-  else if (S <= 2) go(softtopk_kernel<2, D, 4>, 4);
-  else if (S <= 4) go(softtopk_kernel<4, D, 4>, 4);
-  else if (S <= 8) go(softtopk_kernel<8, D, 4>, 4);
-  else if (S <= 16) go(softtopk_kernel<16, D, 2>, 2);
-  else if (S <= 32) go(softtopk_kernel<32, D, 1>, 1);
-  else go(softtopk_kernel<64, D, 1>, 1);
-}
-
-hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
-                             float* soft_mask, float* lambda, hipStream_t s) {
-  const hipError_t e = launch_route(g, t, ws, s);
-  if (e != hipSuccess) return e;
-  if (g.D == 128) launch_softtopk<128>(g, ws, tau, soft_mask, lambda, s);
-  else launch_softtopk<64>(g, ws, tau, soft_mask, lambda, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+// Pooling, projections, then the Top-k kernel (with the SoftTop-k phase when SOFT).
+template <bool SOFT>
+static hipError_t route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
+                        hipStream_t s) {
   if (g.bf16) {
     launch_route_typed<uint16_t, 128>(g, t, ws, s);   // bf16 inputs have d = 128
   } else {
     if (g.D == 128) launch_route_typed<float, 128>(g, t, ws, s);
     else launch_route_typed<float, 64>(g, t, ws, s);
   }
-  if (g.D == 128) launch_topk<128>(g, t, ws, s);
-  else launch_topk<64>(g, t, ws, s);
+  if (g.D == 128) launch_topk<128, SOFT>(g, t, ws, so, s);
+  else launch_topk<64, SOFT>(g, t, ws, so, s);
   return hipGetLastError();
+}
+
+hipError_t launch_route_soft(const Geometry& g, const sla2_tensors& t, const Workspace& ws, double tau,
+                             float* soft_mask, float* lambda, hipStream_t s) {
+  return route<true>(g, t, ws, SoftOut{tau, soft_mask, lambda}, s);
+}
+
+hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
+  return route<false>(g, t, ws, SoftOut{0.0, nullptr, nullptr}, s);
 }
 
 }  // namespace sla2
