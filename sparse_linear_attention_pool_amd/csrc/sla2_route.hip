@@ -20,6 +20,22 @@ namespace sla2 {
 // (exact for bf16 inputs); in FP8 mode also the block's absmax scale and the e4m3 codes of
 // Q.  Rows past N count as zero and receive code 0.
 // ---------------------------------------------------------------------------------------
+// fp64 sum over the lanes l, l ^ 32 (and l ^ 16, l ^ 48 when the rows are 16 lanes wide).
+template <int ROWLANES>
+__device__ __forceinline__ double rows_sum_f64(double v) {
+  u32x2 u = __builtin_bit_cast(u32x2, v);
+  auto a = __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+  v = __builtin_bit_cast(double, u32x2{a[0], b[0]}) + __builtin_bit_cast(double, u32x2{a[1], b[1]});
+  if constexpr (ROWLANES == 16) {
+    u = __builtin_bit_cast(u32x2, v);
+    a = __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false);
+    b = __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false);
+    v = __builtin_bit_cast(double, u32x2{a[0], b[0]}) + __builtin_bit_cast(double, u32x2{a[1], b[1]});
+  }
+  return v;
+}
+
 template <typename Tin, int D, bool FP8>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                    int N, int T, double* __restrict__ qsum,
@@ -30,7 +46,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
   constexpr int RPP = 256 / CPR;         // rows per pass
   constexpr int PASSES = kBlock / RPP;
   static_assert(!FP8 || VEC == 8, "FP8 quantisation needs bf16 input");
-  __shared__ double red[2][RPP * CPR * (VEC + 1)];
+  static_assert(CPR == 16 || CPR == 32, "a wave holds four rows of 16 chunks or two of 32");
+  __shared__ double red[2][4][D];   // per wave: column sums of its rows
   __shared__ float wmax[4];
 
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -79,22 +96,22 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // column sums: per-thread partials -> LDS (row stride padded to VEC + 1 per chunk, so the
-  // 8-byte writes of a 16-lane row hit distinct banks) -> one thread per column, fixed order
-  constexpr int RS = CPR * (VEC + 1);
+  // column sums: over the rows of each wave in registers, then over the four waves in LDS
+  // (sums of bf16 values in fp64 are exact, so the order does not matter for bf16 inputs)
   const size_t out = ((size_t)bh * T + i) * D;
+  const int w = tid >> 6;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    red[0][r0 * RS + c * (VEC + 1) + e] = qs[e];
-    red[1][r0 * RS + c * (VEC + 1) + e] = ks[e];
+    const double qw = rows_sum_f64<CPR>(qs[e]), kw = rows_sum_f64<CPR>(ks[e]);
+    if ((tid & 63) < CPR) {
+      red[0][w][c * VEC + e] = qw;
+      red[1][w][c * VEC + e] = kw;
+    }
   }
   __syncthreads();
   if (tid < 2 * D) {
     const int which = tid / D, col = tid % D;
-    const double* rd = red[which] + (col / VEC) * (VEC + 1) + col % VEC;
-    double sm = 0.0;
-#pragma unroll
-    for (int r = 0; r < RPP; ++r) sm += rd[r * RS];
+    const double sm = (red[which][0][col] + red[which][1][col]) + (red[which][2][col] + red[which][3][col]);
     (which ? ksum : qsum)[out + col] = sm;
   }
 
