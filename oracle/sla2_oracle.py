@@ -38,6 +38,16 @@ Precision of decisions: the FP8 codes are integers decided by floating point,
 so this oracle takes those decisions in the kernel's precision (float32):
 K_tilde32 = fl32(K - fl32(mu)), scale = fl32(absmax / 448),
 y = fl32(x / scale).  Everything else is fp64.
+
+Low-bit P.V (SLA2 page, section 5: the sparse branch also quantises P and V
+and dequantises their product).  The pages fix neither granularity nor scale
+form; the reading here: V gets one power-of-two scale per (64-token block,
+channel), the smallest 2**e with max|V| <= 448 * 2**e; P gets one
+power-of-two scale per (query, routed block), 2**(ceil(M) - 8) with M the
+largest log2-scaled score of that query in that block, so the block's
+largest P code lies in (128, 256].  The softmax normaliser sums the
+unquantised P.  Powers of two make the scaling exact, so only the e4m3
+rounding of P and V differs from the plain product.
 """
 from __future__ import annotations
 
@@ -139,6 +149,60 @@ def quantize_fp8_blocks(x32: np.ndarray, block: int = BLOCK):
 
 
 # --------------------------------------------------------------------------
+# low-bit P.V (SLA2 page, section 5): power-of-two scales, e4m3 codes
+# --------------------------------------------------------------------------
+E8M0_MIN = -127   # smallest power-of-two exponent a scale takes
+
+
+def v_channel_exponents(v_blk: np.ndarray) -> np.ndarray:
+    """Per channel c of one key block: the smallest integer e >= -127 with
+    max_t |V[t, c]| <= 448 * 2**e (-127 for an all-zero channel)."""
+    amax = np.max(np.abs(np.asarray(v_blk, np.float64)), axis=0)
+    e = np.full(amax.shape, E8M0_MIN, dtype=np.int64)
+    for c, a in enumerate(amax):
+        if a == 0.0:
+            continue
+        _, x = math.frexp(a)            # a = f * 2**x with 0.5 <= f < 1
+        ec = x - 10                     # 448 * 2**(x-10) < 0.5 * 2**x <= a
+        while math.ldexp(fp8_e4m3.FP8_E4M3_MAX, ec) < a:
+            ec += 1
+        e[c] = max(ec, E8M0_MIN)
+    return e
+
+
+def quantize_v_blocks(v: np.ndarray, block: int = BLOCK):
+    """V codes with per-(block, channel) power-of-two scales.
+
+    Returns (codes [N, d] uint8, exponents [T, d] int, dequantised [N, d] fp64
+    = decode(code) * 2**e)."""
+    v64 = np.asarray(v, np.float64)
+    N = v64.shape[0]
+    T = num_blocks(N, block)
+    codes = np.empty(v64.shape, dtype=np.uint8)
+    exps = np.empty((T, v64.shape[1]), dtype=np.int64)
+    deq = np.empty(v64.shape, dtype=np.float64)
+    for j in range(T):
+        r = block_rows(j, N, block)
+        e = v_channel_exponents(v64[r])
+        c = fp8_e4m3.encode(np.ldexp(v64[r], -e))   # exact scaling, then round to e4m3
+        codes[r], exps[j] = c, e
+        deq[r] = np.ldexp(fp8_e4m3.decode(c), e)
+    return codes, exps, deq
+
+
+def quantize_p_block(x: np.ndarray):
+    """P of one (query rows x routed block) tile from log2-scaled scores x.
+
+    Per row: c = ceil(max x) (an integer), codes = e4m3(2**(x - c + 8)), and
+    the dequantised P = decode(codes) * 2**(c - 8).  Returns (codes, c, deq)."""
+    x = np.asarray(x, np.float64)
+    c = np.ceil(x.max(axis=1, keepdims=True))
+    codes = fp8_e4m3.encode(np.exp2(x - c + 8.0))
+    deq = np.ldexp(fp8_e4m3.decode(codes), (c - 8.0).astype(np.int64))
+    return codes, c[:, 0].astype(np.int64), deq
+
+
+# --------------------------------------------------------------------------
 # linear branch (SLA page, sections 2-4; SLA2 page, section 3)
 # --------------------------------------------------------------------------
 def phi(x: np.ndarray) -> np.ndarray:
@@ -174,10 +238,13 @@ def route_head(q, k, wq, wk, topk, smooth_k=True, block=BLOCK):
 
 
 def forward_head(q, k, v, alpha_h, wq=None, wk=None, topk=1, smooth_k=True, qk_fp8=False,
-                 eps=EPS, block=BLOCK, lut=None, query_blocks: Optional[Sequence[int]] = None):
+                 eps=EPS, block=BLOCK, lut=None, query_blocks: Optional[Sequence[int]] = None,
+                 pv_fp8=False):
     """SLA2 forward of one (batch, head).
 
     q, k, v: [N, d] values (float32 holding the exact inputs); alpha_h: [d].
+    pv_fp8: the sparse branch's P.V with e4m3 P and V (quantize_p_block,
+    quantize_v_blocks); the softmax normaliser and the linear branch are exact.
     lut: use this routing instead of the router's (rows ascending).
     query_blocks: compute the outputs of these query blocks only (the router
     and the per-key-block statistics always cover every block).
@@ -214,6 +281,9 @@ def forward_head(q, k, v, alpha_h, wq=None, wk=None, topk=1, smooth_k=True, qk_f
         out.update(q8=q8, q_scale=sq, k8=k8, k_scale=sk)
     else:
         q_s, k_s = q64, kt64
+    if pv_fp8:
+        v8, v_exp, v_pv = quantize_v_blocks(v64, block)
+        out.update(v8=v8, v_exp=v_exp)
 
     # linear-branch statistics over every key block
     phi_k = phi(kt64)
@@ -235,7 +305,21 @@ def forward_head(q, k, v, alpha_h, wq=None, wk=None, topk=1, smooth_k=True, qk_f
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
         l = p.sum(axis=1, keepdims=True)
-        o_s[rows] = (p / l) @ v64[keys]
+        if pv_fp8:
+            # per routed block: e4m3 P (in units of 2**x, x = s / ln 2) times e4m3 V; the
+            # normaliser sum_t 2**x_t is exact.  An integer reference keeps the scaling exact.
+            x = s / math.log(2.0)
+            ref = np.ceil(x.max(axis=1, keepdims=True))
+            num = np.zeros((s.shape[0], d))
+            col = 0
+            for j in lut[i]:
+                n_j = block_rows(j, N, block).stop - block_rows(j, N, block).start
+                _, _, p_deq = quantize_p_block(x[:, col:col + n_j] - ref)
+                num += p_deq @ v_pv[keys[col:col + n_j]]
+                col += n_j
+            o_s[rows] = num / np.exp2(x - ref).sum(axis=1, keepdims=True)
+        else:
+            o_s[rows] = (p / l) @ v64[keys]
         lse[rows] = (m + np.log(l))[:, 0]
         # linear branch over the unrouted blocks
         H_i = np.tensordot(unrouted[i], h, axes=(0, 0))
@@ -249,7 +333,8 @@ def forward_head(q, k, v, alpha_h, wq=None, wk=None, topk=1, smooth_k=True, qk_f
 
 
 def forward(inputs: dict, topk: int, smooth_k: bool = True, qk_fp8: bool = False,
-            eps: float = EPS, block: int = BLOCK, luts=None, heads=None, query_blocks=None):
+            eps: float = EPS, block: int = BLOCK, luts=None, heads=None, query_blocks=None,
+            pv_fp8: bool = False):
     """SLA2 forward over [B, H, N, d] inputs (dict from the input generator).
 
     heads: optional list of (b, h) to compute; luts: optional {(b, h): lut}.
@@ -263,5 +348,6 @@ def forward(inputs: dict, topk: int, smooth_k: bool = True, qk_fp8: bool = False
         res[(b, hh)] = forward_head(
             q[b, hh], k[b, hh], v[b, hh], alpha[hh], inputs.get("wq"), inputs.get("wk"),
             topk=topk, smooth_k=smooth_k, qk_fp8=qk_fp8, eps=eps, block=block,
-            lut=None if luts is None else luts.get((b, hh)), query_blocks=query_blocks)
+            lut=None if luts is None else luts.get((b, hh)), query_blocks=query_blocks,
+            pv_fp8=pv_fp8)
     return res
