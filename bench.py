@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample (0 = skip)")
     ap.add_argument("--backward", action="store_true",
                     help="also time sla2_attention_bwd (default for the C4 fine-tuning workload)")
+    ap.add_argument("--pv-fp8", type=int, default=1,
+                    help="also time the low-bit P.V forward (e4m3 P and V) on FP8 workloads (0 = skip)")
     ap.add_argument("--soft-tau", type=float, default=0.001,
                     help="temperature of the separately timed SoftTop-k router leg (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -274,6 +276,39 @@ def main():
         passes["train_step_ms"] = round(float(ms_step + t_bwd), 5)
         log(f"[bench] sla2_attention_bwd: {t_bwd:.4f} ms ({passes['bwd_routed_TFLOPS']} TFLOP/s over the 4 routed "
             f"gradient products)")
+    if args.pv_fp8 and w.qk_mode == "fp8":
+        # the low-bit P.V forward (SLA2 page, section 5: P and V in e4m3 too) on the same inputs,
+        # in its own buffers, timed like the main step
+        p8 = Bn.make_params(w.B, w.H, w.N, w.d, w.topk, w.dtype, "fp8pv")
+        t8 = dict(Bn.allocate(p8, dev, per_block_stats=False))
+        t8.update(d_in)
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+        def step8(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            Bn.sla2_route(p8, t8, stream)
+            Bn.sla2_linear_precompute(p8, t8, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            Bn.sla2_attention_fwd(p8, t8, stream)
+            if ev is not None:
+                ev[2].record(stream)
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize(dev)
+        for k in range(args.steps):
+            step8(ev8[k])
+        torch.cuda.synchronize(dev)
+        t8_step = np.mean([e[0].elapsed_time(e[2]) for e in ev8])
+        t8_pre = np.mean([e[0].elapsed_time(e[1]) for e in ev8])
+        t8_fwd = np.mean([e[1].elapsed_time(e[2]) for e in ev8])
+        passes["pv_fp8_step_ms"] = round(float(t8_step), 5)
+        passes["pv_fp8_route_precompute_ms"] = round(float(t8_pre), 5)
+        passes["pv_fp8_fwd_ms"] = round(float(t8_fwd), 5)
+        passes["pv_fp8_fwd_routed_TFLOPS"] = round(f_sparse / (t8_fwd * 1e-3) / 1e12, 2)
+        log(f"[bench] low-bit P.V step: {t8_step:.4f} ms (route + precompute {t8_pre:.4f}, fwd {t8_fwd:.4f} ms, "
+            f"{passes['pv_fp8_fwd_routed_TFLOPS']} TFLOP/s routed-block)")
     if args.soft_tau > 0:
         # the training router (not part of the inference step): sla2_route_soft on the same
         # inputs, timed alone; its SoftTop-k kernel runs kSoftSteps fp64 sigmoid sums per row

@@ -60,7 +60,16 @@ typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
 /* Arithmetic of the sparse branch's Q.K^T (SLA2 page, section 5, low-bit attention). */
 typedef enum {
   SLA2_QK_NATIVE = 0,   /* Q.K^T in the input precision                                    */
-  SLA2_QK_FP8_E4M3 = 1  /* OCP e4m3 codes, one absmax/448 scale per 64-token block (bf16)  */
+  SLA2_QK_FP8_E4M3 = 1, /* OCP e4m3 codes, one absmax/448 scale per 64-token block (bf16)  */
+  /* Mode 1 plus the sparse branch's P.V in e4m3 (SLA2 page, section 5: P and V quantised, the
+   * product dequantised).  V: one power-of-two scale per (64-token block, channel), the
+   * smallest 2^e >= absmax/448 (e >= -127).  P: one power-of-two scale per (query, routed
+   * block), 2^(ceil(M) - 8) with M the block's largest score in log2 units, so the largest
+   * code lies in [128, 256].  The softmax normaliser sums the unquantised P.  The routed part
+   * of the linear branch (see sla2_attention_fwd) uses the same e4m3 V with the phi products
+   * as e4m3 codes of scale 2^10.  bf16, d = 128, forward only (the backward returns
+   * SLA2_ERR_UNSUPPORTED). */
+  SLA2_QK_PV_FP8_E4M3 = 2
 } sla2_qk_mode;
 
 typedef struct sla2_params {
@@ -69,7 +78,7 @@ typedef struct sla2_params {
   int32_t topk;         /* routed key blocks per query-block row, 1 <= topk <= T             */
   int32_t smooth_k;     /* 1: subtract the per-(b,h) token mean from K (SLA2 page, sec. 6)   */
   int32_t dtype;        /* sla2_dtype of q, k, v, o, h, vt                                   */
-  int32_t qk_mode;      /* sla2_qk_mode; FP8 needs dtype SLA2_BF16                           */
+  int32_t qk_mode;      /* sla2_qk_mode; modes 1 and 2 need dtype SLA2_BF16                  */
   float eps;            /* linear-branch denominator guard, 1e-5 (SLA page, section 4)       */
 } sla2_params;
 
@@ -164,6 +173,8 @@ int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *st
  * H by re-association, as the sum over the routed keys s of (phi(q).phi(K~_s)) V_s (SLA page,
  * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and takes
  * the routed part of Z from the precompute.
+ * SLA2_QK_PV_FP8_E4M3: the P.V products of both uses take e4m3 P (or phi-product codes) and
+ * e4m3 V from the precompute, with their power-of-two scales applied by the matrix cores.
  * Training forward: when t->workspace_bwd is non-NULL (and the backward supports the params:
  * SLA2_BF16, SLA2_QK_FP8_E4M3, d = 128) the call also stores in it, per query, the sparse
  * output O_s, the linear output O_l (both bf16) and 1/(phi(q).Z_i + eps), which the backward
@@ -176,7 +187,8 @@ int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream
  * the routing held fixed (no gradient reaches W_q, W_k or the pooling), the FP8 quantiser
  * passed straight through (dQ' -> dQ, dK' -> dK~), and key smoothing differentiated
  * (dK = dK~ - mean over tokens of dK~ when smooth_k).
- * Supported: dtype SLA2_BF16, qk_mode SLA2_QK_FP8_E4M3, d = 128 (else SLA2_ERR_UNSUPPORTED).
+ * Supported: dtype SLA2_BF16, qk_mode SLA2_QK_FP8_E4M3, d = 128 (else SLA2_ERR_UNSUPPORTED; the
+ * pages' backward is 16-bit, so a low-bit P.V forward has none here).
  * Reads what the three forward calls wrote for the same params and inputs: q, k, v, alpha,
  * k_mean, lut, mask, q8, q_scale, k8, k_scale, h_sum, z_sum, lse (so the forward must have
  * been given lse), the workspace, and the O_s, O_l and 1/den that a training forward (one given

@@ -52,7 +52,7 @@ class Workload:
     N: int
     d: int
     dtype: str              # "f32" or "bf16": element type of Q, K, V, O
-    qk_mode: str            # "native" or "fp8": Q.K^T arithmetic of the sparse branch
+    qk_mode: str            # "native", "fp8" (e4m3 Q.K^T) or "fp8pv" (e4m3 Q.K^T and P.V)
     sparse_frac: float      # share of key blocks routed to the sparse branch
     projections: bool       # seeded d x d router projections (else identity)
     seed: int

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla2.so
 
 SLA2_OK, SLA2_ERR_INVALID_ARG, SLA2_ERR_UNSUPPORTED, SLA2_ERR_HIP = 0, -1, -2, -3
 SLA2_F32, SLA2_BF16 = 0, 1
-SLA2_QK_NATIVE, SLA2_QK_FP8_E4M3 = 0, 1
+SLA2_QK_NATIVE, SLA2_QK_FP8_E4M3, SLA2_QK_PV_FP8_E4M3 = 0, 1, 2
 
 ENTRY_POINTS = ("sla2_buffer_sizes", "sla2_route", "sla2_linear_precompute", "sla2_attention_fwd",
                 "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_route_soft", "sla2_status_string",
@@ -91,7 +91,8 @@ def make_params(B: int, H: int, N: int, d: int, topk: int, dtype: str = "bf16", 
                 smooth_k: bool = True, eps: float = 1e-5) -> Params:
     return Params(B=B, H=H, N=N, d=d, block=64, topk=topk, smooth_k=int(bool(smooth_k)),
                   dtype={"f32": SLA2_F32, "bf16": SLA2_BF16}[dtype],
-                  qk_mode={"native": SLA2_QK_NATIVE, "fp8": SLA2_QK_FP8_E4M3}[qk_mode], eps=eps)
+                  qk_mode={"native": SLA2_QK_NATIVE, "fp8": SLA2_QK_FP8_E4M3,
+                           "fp8pv": SLA2_QK_PV_FP8_E4M3}[qk_mode], eps=eps)
 
 
 def sla2_buffer_sizes(params: Params) -> Dict[str, int]:
@@ -200,7 +201,7 @@ def allocate(params: Params, device="cuda", with_lse: bool = False, per_block_st
         "o": torch.empty((B, H, N, d), dtype=el, device=device),
         "workspace": torch.empty(max(sz["workspace"], 256), dtype=torch.uint8, device=device),
     }
-    if params.qk_mode == SLA2_QK_FP8_E4M3:
+    if params.qk_mode in (SLA2_QK_FP8_E4M3, SLA2_QK_PV_FP8_E4M3):
         out["q8"] = torch.empty((B, H, T * 64, d), dtype=torch.uint8, device=device)
         out["k8"] = torch.empty((B, H, T * 64, d), dtype=torch.uint8, device=device)
         out["q_scale"] = torch.empty((B, H, T), dtype=torch.float32, device=device)

@@ -36,7 +36,7 @@ int check_params(const sla2_params* p, Geometry* g) {
   if (p->d != 64 && p->d != 128) return fail(SLA2_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", p->d);
   if (p->block != 64) return fail(SLA2_ERR_INVALID_ARG, "block must be 64 (got %d)", p->block);
   if (p->dtype != SLA2_F32 && p->dtype != SLA2_BF16) return fail(SLA2_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-  if (p->qk_mode != SLA2_QK_NATIVE && p->qk_mode != SLA2_QK_FP8_E4M3)
+  if (p->qk_mode != SLA2_QK_NATIVE && p->qk_mode != SLA2_QK_FP8_E4M3 && p->qk_mode != SLA2_QK_PV_FP8_E4M3)
     return fail(SLA2_ERR_INVALID_ARG, "unknown qk_mode %d", p->qk_mode);
   if (p->smooth_k != 0 && p->smooth_k != 1) return fail(SLA2_ERR_INVALID_ARG, "smooth_k must be 0 or 1");
   if (!(p->eps >= 0.f) || p->eps > 1.f) return fail(SLA2_ERR_INVALID_ARG, "eps must be in [0, 1]");
@@ -44,7 +44,7 @@ int check_params(const sla2_params* p, Geometry* g) {
   if (T > 4096) return fail(SLA2_ERR_UNSUPPORTED, "at most 4096 blocks per sequence (N <= 262144)");
   if (p->topk < 1 || p->topk > T) return fail(SLA2_ERR_INVALID_ARG, "topk must be in [1, %lld] (got %d)", T, p->topk);
   if ((long long)p->B * p->H * T > 0x7fffffffLL) return fail(SLA2_ERR_INVALID_ARG, "B*H*T too large");
-  if (p->qk_mode == SLA2_QK_FP8_E4M3 && p->dtype != SLA2_BF16)
+  if (p->qk_mode != SLA2_QK_NATIVE && p->dtype != SLA2_BF16)
     return fail(SLA2_ERR_UNSUPPORTED, "FP8 Q.K^T needs bf16 inputs");
   if (p->dtype == SLA2_BF16 && p->d != 128) return fail(SLA2_ERR_UNSUPPORTED, "bf16 kernels need d = 128");
   g->B = p->B;
@@ -56,7 +56,8 @@ int check_params(const sla2_params* p, Geometry* g) {
   g->P = (g->T + kChunk - 1) / kChunk;
   g->BH = p->B * p->H;
   g->smooth_k = p->smooth_k != 0;
-  g->fp8 = p->qk_mode == SLA2_QK_FP8_E4M3;
+  g->fp8 = p->qk_mode != SLA2_QK_NATIVE;
+  g->pv8 = p->qk_mode == SLA2_QK_PV_FP8_E4M3;
   g->bf16 = p->dtype == SLA2_BF16;
   g->eps = p->eps;
   return SLA2_OK;
@@ -80,7 +81,8 @@ size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
   w.khatT = (double*)take(BH * D * T * sizeof(double));
   w.hpart = (float*)take(BH * P * D * D * sizeof(float));
   w.zpart = (float*)take(BH * P * D * sizeof(float));
-  w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * sizeof(uint16_t) : 0);
+  w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * (g.pv8 ? 1 : sizeof(uint16_t)) : 0);
+  w.vexp = (uint8_t*)take(g.pv8 ? BH * T * D : 0);
   w.phik8 = (uint8_t*)take(g.bf16 ? BH * T * 64 * D : 0);
   w.zblk = (float*)take(g.bf16 ? BH * T * D * sizeof(float) : 0);
   w.zrout = (float*)take(g.bf16 ? BH * T * D * sizeof(float) : 0);
@@ -117,7 +119,7 @@ int fill_sizes(const Geometry& g, sla2_sizes* s) {
   s->o = BH * N * D * es;
   s->lse = BH * N * 4;
   s->workspace = workspace_layout(g, nullptr, nullptr);
-  s->workspace_bwd = (g.bf16 && g.fp8 && g.D == 128) ? bwd_workspace_layout(g, nullptr, nullptr) : 0;
+  s->workspace_bwd = (g.bf16 && g.fp8 && !g.pv8 && g.D == 128) ? bwd_workspace_layout(g, nullptr, nullptr) : 0;
   return SLA2_OK;
 }
 
@@ -240,7 +242,7 @@ int sla2_attention_fwd(const sla2_params* p, const sla2_tensors* t, void* stream
   }
   // a backward workspace makes this a training forward: it also stores what the backward reads
   BwdWorkspace bw;
-  const bool keep = t->workspace_bwd != nullptr && g.bf16 && g.fp8 && g.D == 128;
+  const bool keep = t->workspace_bwd != nullptr && g.bf16 && g.fp8 && !g.pv8 && g.D == 128;
   if (keep) {
     if (((uintptr_t)t->workspace_bwd & 255) != 0)
       return fail(SLA2_ERR_INVALID_ARG, "%s: workspace_bwd must be 256-byte aligned", fn);
@@ -256,8 +258,8 @@ int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* 
   Workspace ws;
   int st = prepare(fn, p, t, &g, &ws);
   if (st != SLA2_OK) return st;
-  if (!g.bf16 || !g.fp8 || g.D != 128)
-    return fail(SLA2_ERR_UNSUPPORTED, "%s: implemented for bf16 inputs with FP8 Q.K^T and d = 128", fn);
+  if (!g.bf16 || !g.fp8 || g.pv8 || g.D != 128)
+    return fail(SLA2_ERR_UNSUPPORTED, "%s: implemented for bf16 inputs with FP8 Q.K^T (bf16 P.V) and d = 128", fn);
   REQUIRE(t->q, "q");
   REQUIRE(t->k, "k");
   REQUIRE(t->v, "v");

@@ -31,7 +31,8 @@ struct FwdArgs {
   const uint8_t* k8;
   const float* q_scale;   // [BH, T]
   const float* k_scale;
-  const uint16_t* vt;     // [BH, T, D, 64]
+  const uint16_t* vt;     // [BH, T, D, 64] bf16, or e4m3 bytes with low-bit P.V
+  const uint8_t* vexp;    // low-bit P.V: [BH, T, D] biased exponents of the V scales
   const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of 448 phi(K~), features permuted
   const int32_t* lut;     // [BH, T, topk]
   const uint16_t* hbf;    // [BH, D, D] bf16 LDS image of H^T = h_sum (see Workspace::hbf)
@@ -52,24 +53,28 @@ struct FwdArgs {
 // unpadded with the 16-byte chunks of each row permuted (physical chunk = logical chunk XOR
 // (row mod 8), mod 16 for 256-byte rows), so that the 16-byte operand reads of consecutive
 // lanes (consecutive rows, same logical chunk) hit distinct banks.
-template <bool FP8, int NT>
+template <bool FP8, int NT, bool PV8 = false>
 struct FwdLds {
   static constexpr int KROW = FP8 ? 128 : 256;    // one key row: 128 e4m3 codes or 128 bf16
   static constexpr int KTILE = 64 * KROW;
   static constexpr int PTILE = 64 * 128;          // e4m3 codes of phi(K~): 64 keys x 128
-  static constexpr int VTILE = 128 * 128;         // V^T: 128 rows (features) x 64 bf16 keys
-  static constexpr int POFF = KTILE, VOFF = KTILE + PTILE;
-  static constexpr int STAGE = KTILE + PTILE + VTILE;
-  static constexpr int BYTES = 2 * STAGE;         // the tile being read, the tile being written
+  // V^T: 128 rows (features) x 64 keys, bf16 (128-byte rows) or e4m3 (64-byte rows, physical
+  // chunk = logical chunk XOR ((row / 4) mod 4)), then the 128 exponent bytes of its scales
+  static constexpr int VROW = PV8 ? 64 : 128;
+  static constexpr int VTILE = 128 * VROW;
+  static constexpr int VEBYTES = PV8 ? 128 : 0;
+  static constexpr int POFF = KTILE, VOFF = KTILE + PTILE, VEOFF = VOFF + VTILE;
+  static constexpr int TILE = VEOFF + VEBYTES;
+  static constexpr int STAGE = TILE > 128 * 256 ? TILE : 128 * 256;   // also holds the epilogue's H^T
   static constexpr int KLOADS = KTILE / (16 * NT);   // 16-byte loads per thread per tile part
   static constexpr int PLOADS = PTILE / (16 * NT);
   static constexpr int VLOADS = VTILE / (16 * NT);
-  static_assert(128 * 256 <= BYTES, "epilogue H^T tile must fit in the staging buffers");
 };
 
 // This thread's share of one key block's tiles, in registers.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t k, phik8, vt, hbf;   // k: e4m3 codes of K~ (FP8) or bf16 K (native)
+  __amdgpu_buffer_rsrc_t vexp;                // low-bit P.V: exponents of the V scales
 };
 
 __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
@@ -80,15 +85,21 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   s.k = A.k8 != nullptr ? __builtin_amdgcn_make_buffer_rsrc((void*)(A.k8 + head), 0, bytes8, 0x00020000)
                         : __builtin_amdgcn_make_buffer_rsrc((void*)(A.k + (size_t)bh * A.N * D), 0, A.N * D * 2, 0x00020000);
   s.phik8 = __builtin_amdgcn_make_buffer_rsrc((void*)(A.phik8 + head), 0, bytes8, 0x00020000);
-  s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
+  if (A.vexp != nullptr) {   // e4m3 V^T tiles: one byte per element
+    s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)A.vt + head), 0, bytes8, 0x00020000);
+    s.vexp = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vexp + (size_t)bh * A.T * D), 0, A.T * D, 0x00020000);
+  } else {
+    s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
+    s.vexp = s.vt;
+  }
   s.hbf = __builtin_amdgcn_make_buffer_rsrc((void*)(A.hbf + (size_t)bh * D * D), 0, 2 * D * D, 0x00020000);
   return s;
 }
 
 // The tile of key block j (K, phi(K~) codes, V^T) into the LDS stage at `stage`.
-template <bool FP8, int NT>
+template <bool FP8, int NT, bool PV8>
 __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, int j, int tid, uint8_t* stage) {
-  using L = FwdLds<FP8, NT>;
+  using L = FwdLds<FP8, NT, PV8>;
   constexpr int D = 128;
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 1 KB of each group
   static_for<L::KLOADS>([&](auto P) {
@@ -107,10 +118,18 @@ __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, i
     const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
     lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
   });
-  static_for<L::VLOADS>([&](auto P) {
-    const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
-    lds_dma(src.vt, stage + L::VOFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (2 * kBlock * D));
-  });
+  if constexpr (PV8) {
+    static_for<L::VLOADS>([&](auto P) {
+      const int qd = tid + NT * P, row = qd >> 2, pc = qd & 3;
+      lds_dma(src.vt, stage + L::VOFF + 16 * NT * P + wofs, row * 64 + 16 * (pc ^ ((row >> 2) & 3)), j * (kBlock * D));
+    });
+    if (tid < L::VEBYTES / 16) lds_dma(src.vexp, stage + L::VEOFF, 16 * tid, j * D);   // wave 0, 8 lanes
+  } else {
+    static_for<L::VLOADS>([&](auto P) {
+      const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
+      lds_dma(src.vt, stage + L::VOFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (2 * kBlock * D));
+    });
+  }
 }
 
 // The 32 KB bf16 image of H^T, stored in memory already in its LDS layout, into `dst`.
@@ -155,13 +174,13 @@ struct QueryOps {
 // ksc.  The copy of the next tile (or, after the last, of the epilogue's H^T image) into the
 // other stage runs meanwhile.  mask: the block may be partial (only the last LUT entry can
 // be: LUT rows are ascending and only block T-1 is partial).
-template <bool FP8, bool LUT_REG, int QT, int STG>
+template <bool FP8, bool LUT_REG, int QT, int STG, bool PV8>
 __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem0, uint8_t* smem1, int lutv,
                                               float& ksc, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
                                               float cq, bool mask, const TileSrc& src) {
   constexpr int NT = 256 / QT;
-  using L = FwdLds<FP8, NT>;
+  using L = FwdLds<FP8, NT, PV8>;
   // the two stages are separate LDS objects and the stage roles are fixed per instantiation,
   // so the compiler can see that this block's reads never touch the copy in flight
   const uint8_t* stage = STG == 0 ? smem0 : smem1;
@@ -173,7 +192,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   if (r + 1 < topk) {
     const int jn = lut_entry<LUT_REG>(lutv, lutG, r + 1);
     if constexpr (FP8) ksc_next = A.k_scale[(size_t)bh * A.T + jn];
-    dma_tile<FP8, NT>(A, src, jn, tid, next);
+    dma_tile<FP8, NT, PV8>(A, src, jn, tid, next);
   } else {
     dma_himage<NT>(src, tid, next);
   }
@@ -236,7 +255,8 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
 
   // ---- online softmax, one query per lane and tile.  The running max is only raised when
   // the block max exceeds it by more than 8 (log2 units), so p <= 256; the rescale is skipped
-  // by the whole wave when no lane needs it.
+  // by the whole wave when no lane needs it.  With low-bit P.V the running max is raised to an
+  // integer (the ceiling of the block max), so every rescale and P scale is a power of two.
   float mx[QT];
   bool raise_any = false;
 #pragma unroll
@@ -252,7 +272,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   if (__builtin_amdgcn_ballot_w64(raise_any) != 0) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float mnew = mx[qt] > st.m_run[qt] + 8.f ? mx[qt] : st.m_run[qt];
+      const float mnew = mx[qt] > st.m_run[qt] + 8.f ? (PV8 ? ceilf(mx[qt]) : mx[qt]) : st.m_run[qt];
       const float f = __builtin_amdgcn_exp2f(st.m_run[qt] - mnew);
       st.l_run[qt] *= f;
 #pragma unroll
@@ -261,55 +281,111 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     }
   }
 
-  // P (probabilities) and A (448^2 phi(q).phi(k), the raw product of the codes) of key half s,
-  // keys 32s + 16h + 4g + rr, as the bf16 B operands of the products below
-  bf16x8 pop[QT][2], aop[QT][2];
-  auto make_ops = [&](int qt, int s) {
-    float pv[8], av[8], psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][2 * s + h][rr], cj, -st.m_run[qt]));
-        av[4 * h + rr] = Ph[qt][2 * s + h][rr];
-        psum += pv[4 * h + rr];
-      }
-    const uint32_t pw[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                            pack_bf16x2(pv[6], pv[7])};
-    const uint32_t aw[4] = {pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]), pack_bf16x2(av[4], av[5]),
-                            pack_bf16x2(av[6], av[7])};
-    pop[qt][s] = __builtin_bit_cast(bf16x8, pw);
-    aop[qt][s] = __builtin_bit_cast(bf16x8, aw);
-    st.l_run[qt] += psum;
-  };
-
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    make_ops(qt, 0);
-    make_ops(qt, 1);
-  }
-
-  // ---- O_s^T += V^T P^T and O_corr^T += V^T Ph^T, sharing each V^T operand read between the
-  // query tiles and the two products; reads run one feature tile ahead of the products
-  auto vread = [&](int dt, int s) {
-    const int row = 16 * dt + l16;
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
-                                                                     16 * ((4 * s + g) ^ (row & 7))));
-  };
-  // Steps k = 0..15 take key half s = k / 8 of feature tile dt = k % 8, so the two products
-  // that accumulate into the same registers are eight steps apart.
-  bf16x8 vq[16];
-  static_for<kVReadAhead>([&](auto k) { vq[k] = vread(k % 8, k / 8); });
-  static_for<16>([&](auto k) {
-    if constexpr (k + kVReadAhead < 16) vq[k + kVReadAhead] = vread((k + kVReadAhead) % 8, (k + kVReadAhead) / 8);
-    constexpr int dt = k % 8, sh = k / 8;
+  if constexpr (PV8) {
+    // ---- low-bit P.V (SLA2 page, section 5).  Per query, this block's P is coded as
+    // e4m3(2^(x - cb + 8)) with cb = ceil(block max), values up to 256; the normaliser takes
+    // the unquantised values.  A (the phi products) is coded with the fixed scale 2^-10.  Each
+    // lane's 16 keys fill 16 of the 32 k-positions of its lane group in a 16x16x128 e4m3
+    // product (the other 16 are zero), matching the V^T tile's byte order; the matrix cores
+    // apply 2^(cb - 8 - m_run) to P and the channel's 2^e to V.
+    i32x8 p8[QT], a8[QT];
+    int pexp[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      st.acc[qt][dt] = mfma_bf16(vq[k], pop[qt][sh], st.acc[qt][dt]);
-      st.accl[qt][dt] = mfma_bf16(vq[k], aop[qt][sh], st.accl[qt][dt]);
+      const float off = ceilf(mx[qt]) - 8.f;
+      float psum = 0.f;
+      uint32_t pw[4], aw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float pv[4], av[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pv[rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][mt][rr], cj, -off));
+          av[rr] = clamp_fp8(Ph[qt][mt][rr] * 0x1p-10f);
+          psum += pv[rr];
+        }
+        pw[mt] = pack_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+        aw[mt] = pack_fp8x4(av[0], av[1], av[2], av[3]);
+      }
+      p8[qt] = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
+      a8[qt] = i32x8{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], 0, 0, 0, 0};
+      const int rel = (int)(off - st.m_run[qt]);   // <= 0: m_run >= ceil(block max) - 8
+      st.l_run[qt] += __builtin_amdgcn_ldexpf(psum, rel);
+      pexp[qt] = rel + 127 > 0 ? rel + 127 : 0;    // E8M0 byte (2^-127 for negligible blocks)
     }
-    __builtin_amdgcn_sched_barrier(0);
-  });
+    // O_s^T += V^T P^T and O_corr^T += V^T A^T over the eight feature tiles; the scale byte of
+    // channel 16dt + l16 is byte dt of this lane's 8 exponent bytes
+    const u32x2 ve = *reinterpret_cast<const u32x2*>(stage + L::VEOFF + 8 * l16);
+    auto vread = [&](int dt) {
+      const int row = 16 * dt + l16;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 64 + 16 * (g ^ ((row >> 2) & 3)));
+      return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    };
+    i32x8 vq[8];
+    static_for<kVReadAhead>([&](auto dt) { vq[dt] = vread(dt); });
+    static_for<8>([&](auto dt) {
+      if constexpr (dt + kVReadAhead < 8) vq[dt + kVReadAhead] = vread(dt + kVReadAhead);
+      const int vs = dt < 4 ? (int)ve.x : (int)ve.y;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        st.acc[qt][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vq[dt], p8[qt], st.acc[qt][dt], 0, 0,
+                                                                          dt & 3, vs, 0, pexp[qt]);
+        st.accl[qt][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vq[dt], a8[qt], st.accl[qt][dt], 0, 0,
+                                                                           dt & 3, vs, 0, 127 + 10);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    // P (probabilities) and A (448^2 phi(q).phi(k), the raw product of the codes) of key half s,
+    // keys 32s + 16h + 4g + rr, as the bf16 B operands of the products below
+    bf16x8 pop[QT][2], aop[QT][2];
+    auto make_ops = [&](int qt, int s) {
+      float pv[8], av[8], psum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][2 * s + h][rr], cj, -st.m_run[qt]));
+          av[4 * h + rr] = Ph[qt][2 * s + h][rr];
+          psum += pv[4 * h + rr];
+        }
+      const uint32_t pw[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                              pack_bf16x2(pv[6], pv[7])};
+      const uint32_t aw[4] = {pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]), pack_bf16x2(av[4], av[5]),
+                              pack_bf16x2(av[6], av[7])};
+      pop[qt][s] = __builtin_bit_cast(bf16x8, pw);
+      aop[qt][s] = __builtin_bit_cast(bf16x8, aw);
+      st.l_run[qt] += psum;
+    };
+
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      make_ops(qt, 0);
+      make_ops(qt, 1);
+    }
+
+    // ---- O_s^T += V^T P^T and O_corr^T += V^T Ph^T, sharing each V^T operand read between the
+    // query tiles and the two products; reads run one feature tile ahead of the products
+    auto vread = [&](int dt, int s) {
+      const int row = 16 * dt + l16;
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
+                                                                       16 * ((4 * s + g) ^ (row & 7))));
+    };
+    // Steps k = 0..15 take key half s = k / 8 of feature tile dt = k % 8, so the two products
+    // that accumulate into the same registers are eight steps apart.
+    bf16x8 vq[16];
+    static_for<kVReadAhead>([&](auto k) { vq[k] = vread(k % 8, k / 8); });
+    static_for<16>([&](auto k) {
+      if constexpr (k + kVReadAhead < 16) vq[k + kVReadAhead] = vread((k + kVReadAhead) % 8, (k + kVReadAhead) / 8);
+      constexpr int dt = k % 8, sh = k / 8;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        st.acc[qt][dt] = mfma_bf16(vq[k], pop[qt][sh], st.acc[qt][dt]);
+        st.accl[qt][dt] = mfma_bf16(vq[k], aop[qt][sh], st.accl[qt][dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
 
   wait_dma();
   lds_barrier();
@@ -378,10 +454,10 @@ __device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
 // branch, with phi(K~) and phi(q) as e4m3 codes (phi(q) scaled per query).
 // Pipeline per routed block r: start copying the tile of block r+1 into the other LDS stage,
 // compute on the LDS tile of block r, wait for the copy, barrier.
-template <bool FP8, bool LUT_REG, int QT>
+template <bool FP8, bool LUT_REG, int QT, bool PV8 = false>
 __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   constexpr int NT = 256 / QT;
-  using L = FwdLds<FP8, NT>;
+  using L = FwdLds<FP8, NT, PV8>;
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[L::STAGE];   // stage of even LUT entries
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[L::STAGE];   // stage of odd LUT entries
@@ -412,7 +488,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   const TileSrc src = tile_src(A, bh);
   const int j0 = __builtin_amdgcn_readfirstlane(lutG[0]);
   float ksc = FP8 ? A.k_scale[(size_t)bh * A.T + j0] : 1.f;
-  dma_tile<FP8, NT>(A, src, j0, tid, smem0);
+  dma_tile<FP8, NT, PV8>(A, src, j0, tid, smem0);
 
   QueryOps<QT> qo;
   float cq = kLog2e / sqrtf((float)D);
@@ -468,10 +544,10 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   lds_barrier();
 
   for (int r = 0; r < topk; r += 2) {
-    fwd_iteration<FP8, LUT_REG, QT, 0>(A, st, smem0, smem1, lutv, ksc, lutG, r, topk, bh, l16, g, tid, qo, cq,
+    fwd_iteration<FP8, LUT_REG, QT, 0, PV8>(A, st, smem0, smem1, lutv, ksc, lutG, r, topk, bh, l16, g, tid, qo, cq,
                                        last_partial && r == topk - 1, src);
     if (r + 1 < topk)
-      fwd_iteration<FP8, LUT_REG, QT, 1>(A, st, smem0, smem1, lutv, ksc, lutG, r + 1, topk, bh, l16, g, tid, qo,
+      fwd_iteration<FP8, LUT_REG, QT, 1, PV8>(A, st, smem0, smem1, lutv, ksc, lutG, r + 1, topk, bh, l16, g, tid, qo,
                                          cq, last_partial && r + 1 == topk - 1, src);
   }
 
@@ -710,6 +786,7 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.q_scale = t.q_scale;
     A.k_scale = t.k_scale;
     A.vt = ws.vt;
+    A.vexp = g.pv8 ? ws.vexp : nullptr;
     A.phik8 = ws.phik8;
     A.zrout = ws.zrout;
     A.lut = t.lut;
@@ -733,7 +810,10 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     // One query tile per wave, four waves per workgroup (two workgroups per CU in FP8 mode).
     // Two tiles per wave (QT = 2: every LDS operand read serving both) measured 30% slower at
     // C2: half the waves per CU leave too little to overlap the copies and the barriers.
-    if (g.fp8) {
+    if (g.pv8) {
+      if (lut_reg) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1, true>), dim3(A.nblocks), dim3(256), 0, s, A);
+      else hipLaunchKernelGGL((fwd_mfma_kernel<true, false, 1, true>), dim3(A.nblocks), dim3(256), 0, s, A);
+    } else if (g.fp8) {
       if (lut_reg) hipLaunchKernelGGL((fwd_mfma_kernel<true, true, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
       else hipLaunchKernelGGL((fwd_mfma_kernel<true, false, 1>), dim3(A.nblocks), dim3(256), 0, s, A);
     } else {

@@ -17,6 +17,7 @@ struct Geometry {
   int B, H, N, D, T, topk, P;   // P = ceil(T / kChunk)
   int BH;
   bool smooth_k, fp8, bf16;
+  bool pv8;                     // P.V in e4m3 as well (implies fp8)
   float eps;
 };
 
@@ -29,7 +30,11 @@ struct Workspace {
   double* khatT;   // [BH, D, T]  projected pooled K~, transposed
   float* hpart;    // [BH, P, D, D] chunk partials of h_sum (transposed like h)
   float* zpart;    // [BH, P, D]
-  uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted
+  uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted;
+                   // with e4m3 P.V the same region holds [BH, T, D, 64] bytes: e4m3 codes of
+                   // V * 2^-e, row c (a channel) holding key 16mt + 4g + rr at byte 16g + 4mt + rr
+  uint8_t* vexp;   // e4m3 P.V only: [BH, T, D] the biased exponents e + 127 of the V scales,
+                   // channel c = 16dt + f at byte 8f + dt
   uint8_t* phik8;  // bf16 modes: [BH, T*64, D] e4m3 codes of 448 phi(K~) (pad rows 0); in each
                    // row, byte 32g + 8s + e holds feature 32s + 8g + e (g, s < 4, e < 8)
   float* zblk;     // bf16 modes: [BH, T, D] z_j of every key block

@@ -40,12 +40,23 @@ __device__ __forceinline__ bf16x8 lds_op_tr16(const uint16_t* x, int ld, int r0,
   return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
-template <bool FP8, bool STORE>
+// Exponent e of the power-of-two scale of one V channel of a key block (SLA2 page, section 5,
+// low-bit P.V): the smallest integer e >= -127 with amax <= 448 * 2^e; -127 for amax = 0.
+// The comparisons are exact (448 * 2^e is a float), so the choice has one answer.
+__device__ __forceinline__ int v_scale_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int e = __builtin_amdgcn_frexp_expf(amax) - 10;    // amax = f 2^x, 0.5 <= f < 1: 448 2^(x-10) < amax
+  while (__builtin_amdgcn_ldexpf(kFp8Max, e) < amax) ++e;   // at most three steps
+  return e > -127 ? e : -127;
+}
+
+template <bool FP8, bool STORE, bool PV8>
 __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ k_mean,
     int N, int T, int P, uint8_t* __restrict__ k8, float* __restrict__ k_scale,
     uint16_t* __restrict__ h, float* __restrict__ z, float* __restrict__ hpart,
-    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8, float* __restrict__ zblk) {
+    float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8, float* __restrict__ zblk,
+    uint8_t* __restrict__ vexp) {
   constexpr int D = 128;
   constexpr int SW = 68;  // LDS row stride in 32-bit words (8-byte aligned rows for the transposing reads)
   __shared__ uint32_t phiS[64 * SW];
@@ -241,18 +252,49 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         }
     }
 
-    // V of this block, transposed: vt[j][c][32s + 8gg + e] = V[key][c] with
-    // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4).  Each 16-lane group
-    // takes 16 columns of one (s, gg); the four groups of a wave take gg = 0..3 of the same
-    // columns, so each column receives 64 contiguous bytes per store.
-    uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
-    static_for<4>([&](auto pp) {
-      const int ct = 2 * pp + (w >> 1), s = w & 1, gg = g;
-      const u32x2 lo4 = lds_read_tr16(v16, 2 * SW, 32 * s + 4 * gg, 16 * ct, l16);
-      const u32x2 hi4 = lds_read_tr16(v16, 2 * SW, 32 * s + 16 + 4 * gg, 16 * ct, l16);
-      *reinterpret_cast<u32x4*>(vtj + (size_t)(16 * ct + l16) * kBlock + 32 * s + 8 * gg) =
-          u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
-    });
+    if constexpr (PV8) {
+      // e4m3 V of this block, transposed, one power-of-two scale per channel: row c of the tile
+      // holds key 16mt + 4g + rr at byte 16g + 4mt + rr (the keys lane group g of the forward
+      // holds).  Wave w, pass pp takes channels c = 16ct + l16 with ct = 4pp + w; lane group g
+      // reads keys 16mt + 4g .. + 3 of its channel with the transposing reads, so the 64 keys
+      // of a channel lie in the four lane groups of one wave and its absmax is a 4-row max.
+      uint8_t* v8j = reinterpret_cast<uint8_t*>(vt) + ((size_t)bh * T + j) * D * kBlock;
+      static_for<2>([&](auto pp) {
+        const int ct = 4 * pp + w, ch = 16 * ct + l16;
+        float x[16];
+        static_for<4>([&](auto mt) {
+          const u32x2 r4 = lds_read_tr16(v16, 2 * SW, 16 * mt + 4 * g, 16 * ct, l16);
+          x[4 * mt + 0] = bf16_lo(r4.x);
+          x[4 * mt + 1] = bf16_hi(r4.x);
+          x[4 * mt + 2] = bf16_lo(r4.y);
+          x[4 * mt + 3] = bf16_hi(r4.y);
+        });
+        float am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(x[e]));
+        const int ex = v_scale_exponent(rows4_max(am));
+        uint32_t wd[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)   // |x| 2^-ex <= 448: exact scaling, then round to e4m3
+          wd[mt] = pack_fp8x4(__builtin_amdgcn_ldexpf(x[4 * mt], -ex), __builtin_amdgcn_ldexpf(x[4 * mt + 1], -ex),
+                              __builtin_amdgcn_ldexpf(x[4 * mt + 2], -ex), __builtin_amdgcn_ldexpf(x[4 * mt + 3], -ex));
+        *reinterpret_cast<u32x4*>(v8j + (size_t)ch * kBlock + 16 * g) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        if (g == 0) vexp[((size_t)bh * T + j) * D + 8 * l16 + ct] = (uint8_t)(ex + 127);
+      });
+    } else {
+      // V of this block, transposed: vt[j][c][32s + 8gg + e] = V[key][c] with
+      // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4).  Each 16-lane group
+      // takes 16 columns of one (s, gg); the four groups of a wave take gg = 0..3 of the same
+      // columns, so each column receives 64 contiguous bytes per store.
+      uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
+      static_for<4>([&](auto pp) {
+        const int ct = 2 * pp + (w >> 1), s = w & 1, gg = g;
+        const u32x2 lo4 = lds_read_tr16(v16, 2 * SW, 32 * s + 4 * gg, 16 * ct, l16);
+        const u32x2 hi4 = lds_read_tr16(v16, 2 * SW, 32 * s + 16 + 4 * gg, 16 * ct, l16);
+        *reinterpret_cast<u32x4*>(vtj + (size_t)(16 * ct + l16) * kBlock + 32 * s + 8 * gg) =
+            u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
+      });
+    }
     __syncthreads();
   }
 
@@ -401,11 +443,11 @@ __global__ __launch_bounds__(128) void zroute_kernel(const float* __restrict__ z
   zrout[((size_t)bh * T + i) * 128 + c] = s;
 }
 
-template <bool FP8, bool STORE>
+template <bool FP8, bool STORE, bool PV8 = false>
 static void launch_precompute_bf16(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL((precompute_bf16_kernel<FP8, STORE>), dim3(g.P, g.BH), dim3(256), 0, s, (const uint16_t*)t.k,
-                     (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale, (uint16_t*)t.h, t.z, ws.hpart,
-                     ws.zpart, ws.vt, ws.phik8, ws.zblk);
+  hipLaunchKernelGGL((precompute_bf16_kernel<FP8, STORE, PV8>), dim3(g.P, g.BH), dim3(256), 0, s,
+                     (const uint16_t*)t.k, (const uint16_t*)t.v, t.k_mean, g.N, g.T, g.P, t.k8, t.k_scale,
+                     (uint16_t*)t.h, t.z, ws.hpart, ws.zpart, ws.vt, ws.phik8, ws.zblk, ws.vexp);
 }
 
 hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Workspace& ws,
@@ -414,7 +456,10 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
   if (g.bf16) {
     // h_j and z_j are stored only when both buffers are given
     const bool store = t.h != nullptr && t.z != nullptr;
-    if (g.fp8) {
+    if (g.pv8) {
+      if (store) launch_precompute_bf16<true, true, true>(g, t, ws, s);
+      else launch_precompute_bf16<true, false, true>(g, t, ws, s);
+    } else if (g.fp8) {
       if (store) launch_precompute_bf16<true, true>(g, t, ws, s);
       else launch_precompute_bf16<true, false>(g, t, ws, s);
     } else {

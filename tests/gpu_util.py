@@ -107,7 +107,10 @@ def check_lut(gpu_lut: np.ndarray, ref: dict, topk: int) -> np.ndarray:
     return ties
 
 
-def compare(got: np.ndarray, ref: np.ndarray, max_abs: float, mean_rel: float = None, what: str = ""):
+def compare(got: np.ndarray, ref: np.ndarray, max_abs: float, mean_rel: float = None, what: str = "",
+            allow: np.ndarray = None):
+    """max |got - ref| <= max_abs (+ allow, per element, where several roundings are correct)
+    and mean |got - ref| <= mean_rel * mean |ref|."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -115,18 +118,63 @@ def compare(got: np.ndarray, ref: np.ndarray, max_abs: float, mean_rel: float = 
     err = np.abs(got - ref)
     ma = float(err.max()) if err.size else 0.0
     mr = float(err.mean() / max(np.abs(ref).mean(), 1e-30)) if err.size else 0.0
-    say(f"    {what}: max_abs={ma:.3e} mean_rel={mr:.3e}")
-    assert ma <= max_abs, f"{what}: max abs error {ma} > {max_abs}"
+    extra = 0.0 if allow is None else allow
+    n_over = int(np.sum(err > max_abs)) if err.size else 0
+    say(f"    {what}: max_abs={ma:.3e} mean_rel={mr:.3e}" +
+        ("" if allow is None else f" (elements above {max_abs} inside their rounding allowance: {n_over})"))
+    assert np.all(err <= max_abs + extra), f"{what}: max abs error {ma} > {max_abs}" + \
+        ("" if allow is None else " plus the element's rounding allowance")
     if mean_rel is not None:
         assert mr <= mean_rel, f"{what}: mean rel error {mr} > {mean_rel}"
     return ma, mr
+
+
+PV8_DELTA = 3e-5   # relative gap between the kernel's fp32 scores / hardware exp2 and the oracle's fp64
+
+
+def pv8_flip_allowance(ref: dict, v: np.ndarray, lut: np.ndarray, d: int) -> np.ndarray:
+    """Per output element, what the low-bit P.V may differ by when a P code or a block's P
+    scale sits at a rounding boundary: the kernel forms the scores in fp32 and exp2 in hardware,
+    the oracle in fp64, so a P value within PV8_DELTA (relative) of an e4m3 rounding midpoint, or
+    a block max within PV8_DELTA of an integer, may be coded either way.  Each such key adds one
+    e4m3 step (2^-3 of its value) of p |V| / l.  Computed for the query blocks the oracle did."""
+    from oracle import fp8_e4m3 as F8
+    N = v.shape[0]
+    T = O.num_blocks(N)
+    allow = np.zeros((N, d))
+    va = np.abs(np.asarray(v, np.float64))
+    done = np.isfinite(ref["o"][:, 0])
+    for i in range(T):
+        rows = O.block_rows(i, N)
+        if not done[rows].all():
+            continue
+        blocks = lut[i]
+        keys = np.concatenate([np.arange(N)[O.block_rows(j, N)] for j in blocks])
+        qd = F8.decode(ref["q8"][rows]) * np.float64(ref["q_scale"][i])
+        kd = np.concatenate([F8.decode(ref["k8"][O.block_rows(j, N)]) * np.float64(ref["k_scale"][j]) for j in blocks])
+        x = (qd @ kd.T) / np.sqrt(d) / np.log(2.0)
+        flag = np.zeros(x.shape, dtype=bool)
+        col = 0
+        for j in blocks:
+            n_j = O.block_rows(j, N).stop - O.block_rows(j, N).start
+            xb = x[:, col:col + n_j]
+            M = xb.max(axis=1, keepdims=True)
+            y = np.exp2(xb - np.ceil(M) + 8.0)
+            flip = F8.encode(y * (1 - PV8_DELTA)) != F8.encode(y * (1 + PV8_DELTA))
+            scale_flip = np.ceil(M - PV8_DELTA * np.maximum(np.abs(M), 1)) != np.ceil(M + PV8_DELTA * np.maximum(np.abs(M), 1))
+            flag[:, col:col + n_j] = flip | scale_flip
+            col += n_j
+        p = np.exp2(x - x.max(axis=1, keepdims=True))
+        allow[rows] = 2.0 ** -3 * ((flag * p) @ va[keys]) / p.sum(axis=1, keepdims=True)
+    return allow
 
 
 def oracle_head(w: I.Workload, inp: dict, b: int, h: int, topk=None, smooth_k=True, lut=None,
                 query_blocks=None):
     return O.forward_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], inp["alpha"][h], inp["wq"],
                           inp["wk"], topk=w.topk if topk is None else topk, smooth_k=smooth_k,
-                          qk_fp8=(w.qk_mode == "fp8"), lut=lut, query_blocks=query_blocks)
+                          qk_fp8=(w.qk_mode in ("fp8", "fp8pv")), lut=lut, query_blocks=query_blocks,
+                          pv_fp8=(w.qk_mode == "fp8pv"))
 
 
 def check_head(w: I.Workload, inp: dict, out: dict, b: int, h: int, topk=None, smooth_k=True,
@@ -144,7 +192,7 @@ def check_head(w: I.Workload, inp: dict, out: dict, b: int, h: int, topk=None, s
     compare(out["q_pool"][b, h], ref["q_pool"], 1e-5 * max(1, np.abs(ref["q_pool"]).max()), what="q_pool")
     compare(out["k_pool"][b, h], ref["k_pool"], 1e-5 * max(1, np.abs(ref["k_pool"]).max()), what="k_pool")
     assert np.array_equal(out["k_mean"][b, h], ref["mu32"]), "k_mean differs from fp32(mean)"
-    if w.qk_mode == "fp8":
+    if w.qk_mode in ("fp8", "fp8pv"):
         N = w.N
         assert np.array_equal(out["q_scale"][b, h], ref["q_scale"]), "q_scale"
         assert np.array_equal(out["k_scale"][b, h], ref["k_scale"]), "k_scale"
@@ -177,7 +225,11 @@ def check_head(w: I.Workload, inp: dict, out: dict, b: int, h: int, topk=None, s
         compare(out["z_sum"][b, h], ref["z_sum"], 1e-4 * max(np.abs(ref["z_sum"]).max(), 1), what="z_sum")
     rows = np.isfinite(ref["o"][:, 0])
     tol = TOL_LOWP if w.dtype == "bf16" else TOL_F32
-    compare(out["o"][b, h][rows], ref["o"][rows], what="o", **tol)
+    if w.qk_mode == "fp8pv":
+        allow = pv8_flip_allowance(ref, inp["v"][b, h], out["lut"][b, h], w.d)
+        compare(out["o"][b, h][rows], ref["o"][rows], what="o", allow=allow[rows], **tol)
+    else:
+        compare(out["o"][b, h][rows], ref["o"][rows], what="o", **tol)
     lse_rows = rows & np.isfinite(ref["lse"])
     compare(out["lse"][b, h][lse_rows], ref["lse"][lse_rows], 1e-2 if w.dtype == "bf16" else 1e-4, what="lse")
     return ties

@@ -118,6 +118,10 @@ SMALL = [
     ("C2", dict(grid=(4, 16, 64), seed=31, name="C2-shaped fp8 N=4096")),
     ("C2", dict(grid=(5, 9, 41), H=3, seed=32, name="C2-shaped fp8 ragged N=1845")),
     ("C2", dict(N=2000, seed=33, name="C2 fp8 unstructured ragged", B=2, H=2)),
+    # low-bit P.V (e4m3 P and V with power-of-two scales) against the oracle's same mode
+    ("C2", dict(grid=(4, 16, 64), seed=34, qk_mode="fp8pv", name="C2-shaped fp8 P.V N=4096")),
+    ("C2", dict(grid=(5, 9, 41), H=3, seed=35, qk_mode="fp8pv", name="C2-shaped fp8 P.V ragged N=1845")),
+    ("C2", dict(N=2000, seed=36, qk_mode="fp8pv", name="fp8 P.V unstructured ragged", B=2, H=2)),
 ]
 
 
@@ -132,11 +136,11 @@ def test_small_workloads_match_oracle(base, kw):
             check_head(w, inp, out, b, h)
 
 
-@pytest.mark.parametrize("mode", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("mode", ["f32", "bf16", "fp8", "fp8pv"])
 def test_every_block_routed_is_softmax_attention(mode):
-    base = {"f32": "C0", "bf16": "C1", "fp8": "C2"}[mode]
+    base = {"f32": "C0", "bf16": "C1", "fp8": "C2", "fp8pv": "C2"}[mode]
     w = I.make_workload(base, grid=None, N=900, H=2, seed=40, d=(64 if mode == "f32" else 128),
-                        name=f"all routed {mode}")
+                        qk_mode=("fp8pv" if mode == "fp8pv" else None), name=f"all routed {mode}")
     inp = I.generate(w)
     inp["alpha"][:] = 1.0
     T = w.T
@@ -221,8 +225,8 @@ def test_fp8_encoder_on_every_bf16_value():
 
 
 # ----------------------------------------------------------------------------- full sizes
-def _sampled_full(base, heads, blocks_per_head=6):
-    w = I.CONFIGS[base]
+def _sampled_full(base, heads, blocks_per_head=6, **overrides):
+    w = I.make_workload(base, **overrides) if overrides else I.CONFIGS[base]
     say(f"[full] generating {w.name}")
     inp = I.generate(w)
     out = run_gpu(w, inp, with_lse=True)
@@ -240,6 +244,10 @@ def test_full_size_c1_sampled():
 
 def test_full_size_c2_sampled():
     _sampled_full("C2", [(0, 0), (0, 5), (0, 11)])
+
+
+def test_full_size_c2_low_bit_pv_sampled():
+    _sampled_full("C2", [(0, 0), (0, 11)], qk_mode="fp8pv", name="C2 fp8 P.V")
 
 
 def test_full_size_c3_sampled():

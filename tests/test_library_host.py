@@ -47,7 +47,8 @@ def test_buffer_sizes_c2(B):
 @pytest.mark.parametrize("kw,status", [
     (dict(d=96), -1), (dict(topk=0), -1), (dict(topk=17), -1), (dict(N=0), -1),
     (dict(block=32), -1), (dict(dtype=7), -1), (dict(qk_mode=5), -1), (dict(smooth_k=2), -1),
-    (dict(eps=-1.0), -1), (dict(dtype=0, qk_mode=1), -2), (dict(d=64, dtype=1, qk_mode=0), -2),
+    (dict(eps=-1.0), -1), (dict(dtype=0, qk_mode=1), -2), (dict(dtype=0, qk_mode=2), -2),
+    (dict(d=64, dtype=1, qk_mode=0), -2), (dict(d=64, dtype=1, qk_mode=2), -2),
     (dict(N=64 * 4097, topk=4), -2),
 ])
 def test_invalid_params_are_rejected_before_any_launch(B, kw, status):
@@ -109,6 +110,23 @@ def test_backward_reports_unsupported(B):
     assert e.value.status == B.SLA2_ERR_UNSUPPORTED
     assert B.lib.sla2_status_string(-2) == b"unsupported"
     assert B.sla2_buffer_sizes(p)["workspace_bwd"] == 0
+    # the backward is 16-bit: a low-bit P.V forward has none
+    p8 = B.make_params(1, 2, 1024, 128, 4, "bf16", "fp8pv")
+    with pytest.raises(B.SLA2Error) as e:
+        B.sla2_attention_bwd(p8, {"workspace": 256 * 1024}, None, None, None, None, None, stream=0)
+    assert e.value.status == B.SLA2_ERR_UNSUPPORTED
+    assert B.sla2_buffer_sizes(p8)["workspace_bwd"] == 0
+
+
+def test_low_bit_pv_workspace_holds_e4m3_v_tiles_and_exponents(B):
+    # C2 shape: bf16 V^T tiles (100.7 MB) become e4m3 tiles (50.3 MB) plus one exponent byte per
+    # (block, channel) (786 KB); everything else is the same
+    s8 = B.sla2_buffer_sizes(B.make_params(1, 12, 32760, 128, 15, "bf16", "fp8"))
+    s8pv = B.sla2_buffer_sizes(B.make_params(1, 12, 32760, 128, 15, "bf16", "fp8pv"))
+    tiles = 12 * 512 * 128 * 64
+    assert s8["workspace"] - s8pv["workspace"] == tiles - 12 * 512 * 128
+    for key in ("q8", "k8", "q_scale", "k_scale", "o", "lse", "h", "z"):
+        assert s8[key] == s8pv[key]
 
 
 def test_backward_needs_the_forward_buffers(B):
