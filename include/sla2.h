@@ -208,8 +208,11 @@ int sla2_attention_bwd(const sla2_params *p, const sla2_tensors *t, const void *
  *   which = 0: v_mfma_f32_16x16x32_bf16, a/b = 64 lanes x 8 bf16 (16 bytes per lane)
  *   which = 1: v_mfma_f32_16x16x128_f8f6f4 with e4m3 operands, 64 lanes x 32 bytes
  *   which = 2: v_mfma_f64_16x16x4_f64, a/b = 64 lanes x 1 double
+ *   which = 3: v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 operands as for 1, each followed by
+ *              64 lanes x one 32-bit scale word (E8M0 exponent bytes); the instruction takes
+ *              byte 2 of A's word and byte 0 of B's (2304 bytes per operand)
  * a, b: device arrays of the lane-major operand registers; d: device array of the lane-major
- * accumulator registers of the result (C = 0): float[64*4] for which = 0 and 1,
+ * accumulator registers of the result (C = 0): float[64*4] for which = 0, 1 and 3,
  * double[64*4] for which = 2.  Returns SLA2_ERR_INVALID_ARG for other values of `which`. */
 int sla2_selftest_mfma(int which, const void *a, const void *b, void *d, void *stream);
 

@@ -834,37 +834,4 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------------
-// Diagnostic: one wave, one matrix-core instruction, C = 0.
-// ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void selftest_mfma_kernel(int which, const u32x4* a, const u32x4* b, float4* d) {
-  const int l = threadIdx.x;
-  f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (which == 2) {
-    const f64x4 r64 = mfma_f64(reinterpret_cast<const double*>(a)[l], reinterpret_cast<const double*>(b)[l],
-                               f64x4{0.0, 0.0, 0.0, 0.0});
-    double* d64 = reinterpret_cast<double*>(d);
-    d64[4 * l + 0] = r64[0];
-    d64[4 * l + 1] = r64[1];
-    d64[4 * l + 2] = r64[2];
-    d64[4 * l + 3] = r64[3];
-    return;
-  }
-  if (which == 0) {
-    r = mfma_bf16(__builtin_bit_cast(bf16x8, a[l]), __builtin_bit_cast(bf16x8, b[l]), r);
-  } else {
-    const u32x4 a0 = a[2 * l], a1 = a[2 * l + 1], b0 = b[2 * l], b1 = b[2 * l + 1];
-    const i32x8 ao = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    const i32x8 bo = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    r = mfma_fp8(ao, bo, r);
-  }
-  d[l] = make_float4(r[0], r[1], r[2], r[3]);
-}
-
-hipError_t launch_selftest_mfma(int which, const void* a, const void* b, void* d, hipStream_t s) {
-  hipLaunchKernelGGL(selftest_mfma_kernel, dim3(1), dim3(64), 0, s, which, (const u32x4*)a, (const u32x4*)b,
-                     (float4*)d);
-  return hipGetLastError();
-}
-
 }  // namespace sla2

@@ -87,6 +87,46 @@ def test_mfma_fp8_operand_layout_and_scale():
     assert rel <= 2.0 ** -12
 
 
+def test_mfma_fp8_scaled_operand_layout():
+    """The scaled e4m3 product of the low-bit P.V path: lane l's E8M0 scale applies to row
+    l % 16 of A and column l % 16 of B (every lane of a row carries the same exponent, as in the
+    kernel), and the selected byte of the scale word is the one used."""
+    import torch
+    from oracle import fp8_e4m3 as F8
+    from sparse_linear_attention_pool_amd import binding as Bn
+    rng = np.random.default_rng(2)
+    ca = rng.integers(0, 256, (16, 128)).astype(np.uint8)
+    cb = rng.integers(0, 256, (128, 16)).astype(np.uint8)
+    ca[(ca & 0x7F) == 0x7F] = 0x38
+    cb[(cb & 0x7F) == 0x7F] = 0x38
+    ea = rng.integers(-12, 13, 16)
+    eb = rng.integers(-12, 13, 16)
+    a = np.zeros((64, 36), np.uint8)
+    b = np.zeros((64, 36), np.uint8)
+    for l in range(64):
+        a[l, :32] = ca[l % 16, 32 * (l // 16):32 * (l // 16) + 32]
+        b[l, :32] = cb[32 * (l // 16):32 * (l // 16) + 32, l % 16]
+    wa = rng.integers(0, 256, (64, 4)).astype(np.uint8)   # unused bytes hold noise
+    wb = rng.integers(0, 256, (64, 4)).astype(np.uint8)
+    for l in range(64):
+        wa[l, 2] = 127 + ea[l % 16]
+        wb[l, 0] = 127 + eb[l % 16]
+    ab = np.concatenate([a[:, :32].reshape(-1), wa.reshape(-1)])
+    bb = np.concatenate([b[:, :32].reshape(-1), wb.reshape(-1)])
+    dd = torch.zeros((64, 4), dtype=torch.float32, device="cuda")
+    Bn.sla2_selftest_mfma(3, torch.from_numpy(ab).cuda(), torch.from_numpy(bb).cuda(), dd)
+    d = dd.cpu().numpy()
+    ref = np.ldexp(F8.decode(ca), ea[:, None]) @ np.ldexp(F8.decode(cb), eb[None, :])
+    absum = np.abs(np.ldexp(F8.decode(ca), ea[:, None])) @ np.abs(np.ldexp(F8.decode(cb), eb[None, :]))
+    got = np.zeros((16, 16))
+    for l in range(64):
+        for r in range(4):
+            got[4 * (l // 16) + r, l % 16] = d[l, r]
+    rel = np.max(np.abs(got - ref) / (absum + 1e-30))
+    say(f"    scaled fp8 mfma: max |err| / sum|a||b| = {rel:.3e}")
+    assert rel <= 2.0 ** -12
+
+
 def test_mfma_f64_operand_layout():
     import torch
     from sparse_linear_attention_pool_amd import binding as Bn
