@@ -81,6 +81,19 @@ def test_backward_small(base, kw):
     _check(w, inp, out, [(b, h) for b in range(w.B) for h in range(w.H)])
 
 
+def test_backward_lists_longer_than_a_wave():
+    """k_sel 70 of 256 blocks: the query side reads its LUT row from memory (k_sel > 64) and most
+    key blocks are routed from more than 64 query blocks (up to 91 here), so the key side reads
+    its inverse list from memory too."""
+    w = I.make_workload("C4", N=16350, grid=None, H=1, seed=46, sparse_frac=70 / 256, name="long LUT and inverse lists")
+    assert w.topk == 70
+    inp = I.generate(w, with_dout=True)
+    out = _run(w, inp)
+    cnt = np.bincount(out["lut"][0, 0].ravel(), minlength=w.T)
+    assert cnt.max() > 64
+    _check(w, inp, out, [(0, 0)])
+
+
 def test_backward_full_size_c4_sampled():
     """The C4 fine-tuning shape (N=32760, H=12, 26 of 512 key blocks routed) on two heads."""
     w = I.CONFIGS["C4"]
