@@ -204,6 +204,18 @@ def test_lut_rows_longer_than_a_wave(mode):
         check_head(w, inp, out, 0, h, topk=70, check_stats=(h == 0), query_blocks=[0, 1, 100, 177, T - 2, T - 1])
 
 
+@pytest.mark.parametrize("N", [57000, 128000, 262144])
+def test_router_tiers_up_to_the_largest_sequence(N):
+    # T = 891, 2000 and 4096 blocks: the Top-k kernel's 16-, 32- and 64-slot tiers (16, 8 and 4
+    # rows per workgroup as the score rows outgrow the LDS); 3% routed, so k_sel reaches 123 and
+    # the forward reads its LUT rows from memory.  Router, quantiser and sampled query blocks.
+    w = I.make_workload("C2", grid=None, N=N, H=1, seed=47, name=f"router tiers N={N}")
+    inp = I.generate(w)
+    out = run_gpu(w, inp)
+    T = w.T
+    check_head(w, inp, out, 0, 0, check_stats=False, query_blocks=[0, T // 2, T - 1])
+
+
 def test_smoothing_off_and_topk_one():
     w = I.make_workload("C2", grid=(2, 16, 64), seed=41, name="fp8 smooth_k=0 topk=1")
     inp = I.generate(w)

@@ -97,6 +97,18 @@ def test_soft_topk_every_block_and_one_block():
         _check(w, inp, 0.03, soft, lam, lut, topk=k_sel)
 
 
+@pytest.mark.parametrize("N", [57000, 128000, 262144])
+def test_soft_topk_large_sequences(N):
+    """T = 891, 2000, 4096: the soft phase's 16-, 32- and 64-slot tiers (8 or 4 rows per
+    workgroup); 96 sampled rows checked."""
+    w = I.make_workload("C2", grid=None, N=N, H=1, seed=48, name=f"soft tiers N={N}")
+    inp = I.generate(w)
+    T = (N + 63) // 64
+    rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).integers(0, T, 94)]))
+    soft, lam, lut = _run_soft(w, inp, 0.001)
+    _check(w, inp, 0.001, soft, lam, lut, rows=rows)
+
+
 def test_soft_topk_full_size_c2():
     """All 6,144 rows of the C2 router (12 heads x 512 query blocks, 512 key blocks each)."""
     w = I.CONFIGS["C2"]
