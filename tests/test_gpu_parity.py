@@ -216,6 +216,19 @@ def test_router_tiers_up_to_the_largest_sequence(N):
     check_head(w, inp, out, 0, 0, check_stats=False, query_blocks=[0, T // 2, T - 1])
 
 
+@pytest.mark.parametrize("mode", ["native", "fp8", "fp8pv"])
+def test_without_per_block_stats_matches_oracle(mode):
+    # bf16 modes without h, z buffers: the precompute skips storing them and accumulates h_sum
+    # in its matrix-core accumulators directly (the variant the benchmark runs)
+    w = I.make_workload("C1" if mode == "native" else "C2", grid=(5, 9, 41), H=2, seed=49,
+                        qk_mode=(None if mode == "native" else mode), name=f"no h/z buffers, {mode}")
+    inp = I.generate(w)
+    out = run_gpu(w, inp, per_block_stats=False)
+    assert "h" not in out
+    for h in range(w.H):
+        check_head(w, inp, out, 0, h)   # h_sum and z_sum too; per-block h, z absent
+
+
 def test_smoothing_off_and_topk_one():
     w = I.make_workload("C2", grid=(2, 16, 64), seed=41, name="fp8 smooth_k=0 topk=1")
     inp = I.generate(w)
