@@ -96,13 +96,14 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   return s;
 }
 
-// The tile of key block j (K, phi(K~) codes, V^T) into the LDS stage at `stage`.
-template <bool FP8, int NT, bool PV8>
+// The tile of key block j (K, phi(K~) codes, V^T) into the LDS stage at `stage`; without the
+// keys (WITH_K false) for the linear branch alone.
+template <bool FP8, int NT, bool PV8, bool WITH_K = true>
 __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, int j, int tid, uint8_t* stage) {
   using L = FwdLds<FP8, NT, PV8>;
   constexpr int D = 128;
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 1 KB of each group
-  static_for<L::KLOADS>([&](auto P) {
+  if constexpr (WITH_K) static_for<L::KLOADS>([&](auto P) {
     const int qd = tid + NT * P;
     uint8_t* dst = stage + 16 * NT * P + wofs;
     if constexpr (FP8) {
@@ -392,6 +393,74 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   ksc = ksc_next;
 }
 
+// One unrouted block for the direct form of the linear branch (more than half of the blocks
+// routed): accl^T += V^T A^T with A = 448^2 phi(q).phi(K~_s) over its keys, the same products
+// as the routed part above.  Its phi codes and V^T tile are in LDS stage STG; the copy of the
+// next unrouted block (jn >= 0) into the other stage starts first.
+template <bool FP8, int QT, bool PV8, int STG>
+__device__ __forceinline__ void lin_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem0, uint8_t* smem1,
+                                              int jn, int l16, int g, int tid, const QueryOps<QT>& qo,
+                                              const TileSrc& src) {
+  constexpr int NT = 256 / QT;
+  using L = FwdLds<FP8, NT, PV8>;
+  const uint8_t* stage = STG == 0 ? smem0 : smem1;
+  uint8_t* next = STG == 0 ? smem1 : smem0;
+  if (jn >= 0) dma_tile<FP8, NT, PV8, false>(A, src, jn, tid, next);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 Ph[QT][4];
+  static_for<4>([&](auto mt) {
+    const i32x8 pr = lds_fp8_row(stage + L::POFF, 16 * mt + l16, g);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) Ph[qt][mt] = mfma_fp8(pr, qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+  });
+  if constexpr (PV8) {
+    i32x8 a8[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      uint32_t aw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        aw[mt] = pack_fp8x4(clamp_fp8(Ph[qt][mt][0] * 0x1p-10f), clamp_fp8(Ph[qt][mt][1] * 0x1p-10f),
+                            clamp_fp8(Ph[qt][mt][2] * 0x1p-10f), clamp_fp8(Ph[qt][mt][3] * 0x1p-10f));
+      a8[qt] = i32x8{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], 0, 0, 0, 0};
+    }
+    const u32x2 ve = *reinterpret_cast<const u32x2*>(stage + L::VEOFF + 8 * l16);
+    static_for<8>([&](auto dt) {
+      const int row = 16 * dt + l16;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 64 + 16 * (g ^ ((row >> 2) & 3)));
+      const i32x8 vop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+      const int vs = dt < 4 ? (int)ve.x : (int)ve.y;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        st.accl[qt][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, a8[qt], st.accl[qt][dt], 0, 0,
+                                                                           dt & 3, vs, 0, 127 + 10);
+    });
+  } else {
+    // A of key half s (keys 32s + 16h + 4g + rr) as the bf16 B operand, as for P above
+    bf16x8 aop[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const uint32_t aw[4] = {pack_bf16x2(Ph[qt][2 * sh][0], Ph[qt][2 * sh][1]),
+                                pack_bf16x2(Ph[qt][2 * sh][2], Ph[qt][2 * sh][3]),
+                                pack_bf16x2(Ph[qt][2 * sh + 1][0], Ph[qt][2 * sh + 1][1]),
+                                pack_bf16x2(Ph[qt][2 * sh + 1][2], Ph[qt][2 * sh + 1][3])};
+        aop[qt][sh] = __builtin_bit_cast(bf16x8, aw);
+      }
+    static_for<16>([&](auto k) {
+      constexpr int dt = k % 8, sh = k / 8;
+      const int row = 16 * dt + l16;
+      const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
+                                                                                 16 * ((4 * sh + g) ^ (row & 7))));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) st.accl[qt][dt] = mfma_bf16(v, aop[qt][sh], st.accl[qt][dt]);
+    });
+  }
+  wait_dma();
+  lds_barrier();
+}
+
 // phi(q) = softmax over the 128 features of query row q (bf16 input): this lane's features
 // 32s + 8g + e (s < 4, e < 8), f[s][e].
 __device__ __forceinline__ void phi_q_values(const uint16_t* qrow, int g, float (&f)[4][8]) {
@@ -551,6 +620,57 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
                                          cq, last_partial && r + 1 == topk - 1, src);
   }
 
+  // With more than half of the blocks routed, the complement H_tot - (routed part) would be a
+  // small difference of two large terms, amplifying the rounding of the routed part; the
+  // unrouted part is then summed directly over the unrouted blocks instead (the same products
+  // as the routed part above), and H_tot is not used.
+  const bool direct = 2 * topk > A.T && topk < A.T;
+  if (direct) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.accl[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the unrouted blocks, ascending: a bitmap of the LUT row (in stage 1's key region, which
+    // no copy below touches), then a ballot compaction into a list (stage 0's key region)
+    static_assert(4096 * 2 <= L::KTILE, "the list of unrouted blocks fits in a key region");
+    uint32_t* bits = reinterpret_cast<uint32_t*>(smem1);   // 128 words: T <= 4096
+    int* wcnt = reinterpret_cast<int*>(smem1 + 512);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(smem0);
+    if (tid < 128) bits[tid] = 0u;
+    lds_barrier();
+    for (int x = tid; x < topk; x += NT) {
+      const int j = lutG[x];
+      atomicOr(bits + (j >> 5), 1u << (j & 31));
+    }
+    lds_barrier();
+    int nun = 0;
+    for (int j0 = 0; j0 < A.T; j0 += NT) {
+      const int j = j0 + tid;
+      const bool un = j < A.T && ((bits[j >> 5] >> (j & 31)) & 1u) == 0u;
+      const uint64_t b = __builtin_amdgcn_ballot_w64(un);
+      if (lane == 0) wcnt[w] = __popcll(b);
+      lds_barrier();
+      int off = nun;
+      for (int ww = 0; ww < w; ++ww) off += wcnt[ww];
+      if (un) ulist[off + __popcll(b & ((1ull << lane) - 1ull))] = (uint16_t)j;
+      for (int ww = 0; ww < NT / 64; ++ww) nun += wcnt[ww];
+      lds_barrier();
+    }
+    // nun = T - topk >= 1; every copy below stays in the phi and V^T regions of the stages
+    int u = __builtin_amdgcn_readfirstlane((int)ulist[0]);
+    dma_tile<FP8, NT, PV8, false>(A, src, u, tid, smem1);
+    wait_dma();
+    lds_barrier();
+    for (int n = 0; n < nun; n += 2) {
+      const int u1 = n + 1 < nun ? __builtin_amdgcn_readfirstlane((int)ulist[n + 1]) : -1;
+      lin_iteration<FP8, QT, PV8, 1>(A, st, smem0, smem1, u1, l16, g, tid, qo, src);
+      if (n + 1 < nun) {
+        const int u2 = n + 2 < nun ? __builtin_amdgcn_readfirstlane((int)ulist[n + 2]) : -1;
+        lin_iteration<FP8, QT, PV8, 0>(A, st, smem0, smem1, u2, l16, g, tid, qo, src);
+      }
+    }
+  }
+
   // ---------------- epilogue ----------------
   // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
@@ -580,13 +700,20 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     const float inv_den = topk < A.T ? 1.f / (rows4_sum(den) + A.eps) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
+      // numerator over the unrouted blocks: phi(q) H_tot minus the routed part, or (direct)
+      // the unrouted part itself
       f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int hr = 16 * dt + l16;
-      const uint8_t* hrow = Hs + hr * 256;
+      float lsign = -kCodes2;
+      if (!direct) {
+        const int hr = 16 * dt + l16;
+        const uint8_t* hrow = Hs + hr * 256;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
-        ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.phb[qt][s], ol);
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
+          ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.phb[qt][s], ol);
+        }
+      } else {
+        lsign = kCodes2;
       }
       const f32x4 a4 = *reinterpret_cast<const f32x4*>(alphaS + 16 * dt + 4 * g);
       const float av[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -594,7 +721,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         ov[rr] = av[rr] * (st.acc[qt][dt][rr] * inv_l) +
-                 (1.f - av[rr]) * (fmaf(-kCodes2, st.accl[qt][dt][rr], ol[rr]) * inv_den);
+                 (1.f - av[rr]) * (fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den);
       if (qok[qt]) {
         u32x2 sv;
         sv.x = pack_bf16x2(ov[0], ov[1]);
@@ -606,7 +733,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             sv4[rr] = st.acc[qt][dt][rr] * inv_l;
-            lv4[rr] = fmaf(-kCodes2, st.accl[qt][dt][rr], ol[rr]) * inv_den;
+            lv4[rr] = fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den;
           }
           u32x2 s2, l2;
           s2.x = pack_bf16x2(sv4[0], sv4[1]);

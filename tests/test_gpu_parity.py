@@ -229,6 +229,21 @@ def test_without_per_block_stats_matches_oracle(mode):
         check_head(w, inp, out, 0, h)   # h_sum and z_sum too; per-block h, z absent
 
 
+@pytest.mark.parametrize("mode", ["native", "fp8"])
+@pytest.mark.parametrize("k_sel", [47, 48, 70])
+def test_large_routed_shares(mode, k_sel):
+    # 94 blocks: k_sel 47 keeps the complement form of the linear branch; 48 and 70 (more than
+    # half routed) sum the unrouted blocks directly, 70 with the LUT row read from memory.
+    # (The low-bit P.V mode is held to the bar up to 27% routed, in the k_sel 70 of 256 case:
+    # above that the e4m3 V of its linear-branch products exceeds it; see the design notes.)
+    w = I.make_workload("C1" if mode == "native" else "C2", grid=None, N=6000, H=2, seed=51,
+                        qk_mode=(None if mode == "native" else mode), name=f"k_sel {k_sel} of 94, {mode}")
+    inp = I.generate(w)
+    out = run_gpu(w, inp, topk=k_sel, per_block_stats=False)
+    for h in range(w.H):
+        check_head(w, inp, out, 0, h, topk=k_sel)
+
+
 def test_smoothing_off_and_topk_one():
     w = I.make_workload("C2", grid=(2, 16, 64), seed=41, name="fp8 smooth_k=0 topk=1")
     inp = I.generate(w)
