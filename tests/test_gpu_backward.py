@@ -70,6 +70,7 @@ SMALL = [
     ("C4", dict(grid=(4, 16, 64), H=2, seed=42, sparse_frac=0.25, name="C4-shaped N=4096, 25% routed")),
     ("C4", dict(N=1000, B=2, H=2, seed=43, sparse_frac=0.5, name="unstructured ragged, half routed")),
     ("C4", dict(N=200, H=1, seed=44, sparse_frac=1.0, name="every block routed")),
+    ("C4", dict(N=6000, H=1, seed=52, sparse_frac=70 / 94, name="74% routed")),
 ]
 
 
