@@ -169,8 +169,9 @@ int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *st
  * h_sum, z_sum, k_mean, the workspace and, for SLA2_F32, h and z; writes o and, if non-NULL,
  * lse.  The linear statistics of query block i are those of its unrouted blocks, formed as
  * the totals minus the routed part: H_i = h_sum - sum over routed j of h_j, Z_i likewise (with
- * more than half of the blocks routed, SLA2_BF16 sums phi(Q_i) H_i over the unrouted blocks
- * directly instead, since that difference would be small next to its terms).
+ * more than half of the blocks routed, a third for SLA2_QK_PV_FP8_E4M3, SLA2_BF16 sums
+ * phi(Q_i) H_i over the unrouted blocks directly instead, since that difference would be small
+ * next to its terms).
  * SLA2_F32 gathers the routed h_j, z_j; SLA2_BF16 evaluates phi(q) times the routed part of
  * H by re-association, as the sum over the routed keys s of (phi(q).phi(K~_s)) V_s (SLA page,
  * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and takes

@@ -21,6 +21,7 @@
 
 #include "sla2_device.hpp"
 #include "sla2_internal.hpp"
+#include "sla2_lds.hpp"
 
 namespace sla2 {
 
@@ -32,6 +33,7 @@ struct FwdArgs {
   const float* q_scale;   // [BH, T]
   const float* k_scale;
   const uint16_t* vt;     // [BH, T, D, 64] bf16, or e4m3 bytes with low-bit P.V
+  const uint16_t* v;      // bf16 [BH, N, D]: V rows, read by the low-bit mode's unrouted-block loop
   const uint8_t* vexp;    // low-bit P.V: [BH, T, D] biased exponents of the V scales
   const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of 448 phi(K~), features permuted
   const int32_t* lut;     // [BH, T, topk]
@@ -75,6 +77,7 @@ struct FwdLds {
 struct TileSrc {
   __amdgpu_buffer_rsrc_t k, phik8, vt, hbf;   // k: e4m3 codes of K~ (FP8) or bf16 K (native)
   __amdgpu_buffer_rsrc_t vexp;                // low-bit P.V: exponents of the V scales
+  __amdgpu_buffer_rsrc_t vrows;               // low-bit P.V: the bf16 V rows of this head
 };
 
 __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
@@ -88,9 +91,11 @@ __device__ __forceinline__ TileSrc tile_src(const FwdArgs& A, int bh) {
   if (A.vexp != nullptr) {   // e4m3 V^T tiles: one byte per element
     s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)A.vt + head), 0, bytes8, 0x00020000);
     s.vexp = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vexp + (size_t)bh * A.T * D), 0, A.T * D, 0x00020000);
+    s.vrows = __builtin_amdgcn_make_buffer_rsrc((void*)(A.v + (size_t)bh * A.N * D), 0, A.N * D * 2, 0x00020000);
   } else {
     s.vt = __builtin_amdgcn_make_buffer_rsrc((void*)(A.vt + head), 0, 2 * bytes8, 0x00020000);
     s.vexp = s.vt;
+    s.vrows = s.vt;
   }
   s.hbf = __builtin_amdgcn_make_buffer_rsrc((void*)(A.hbf + (size_t)bh * D * D), 0, 2 * D * D, 0x00020000);
   return s;
@@ -130,6 +135,31 @@ __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, i
       const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
       lds_dma(src.vt, stage + L::VOFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (2 * kBlock * D));
     });
+  }
+}
+
+// What the unrouted-block loop reads of key block j: the phi codes and V.  bf16 modes take the
+// V^T tile; the low-bit P.V mode takes the bf16 V rows from the input (256-byte rows, chunk k of
+// row r at chunk k ^ (r % 16), in the stage's V region and after it: 16 KB), so that the linear
+// branch keeps bf16 V there.  Rows past N load row N-1 (their phi codes are zero).
+template <bool FP8, int NT, bool PV8>
+__device__ __forceinline__ void dma_lin(const FwdArgs& A, const TileSrc& src, int j, int tid, uint8_t* stage) {
+  if constexpr (PV8) {
+    using L = FwdLds<FP8, NT, PV8>;
+    constexpr int D = 128;
+    static_assert(L::VOFF + 64 * 256 <= L::STAGE, "bf16 V rows fit after the phi codes");
+    const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
+    static_for<L::PLOADS>([&](auto P) {
+      const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
+      lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
+    });
+    static_for<64 * 256 / (16 * NT)>([&](auto P) {
+      const int qd = tid + NT * P, row = qd >> 4, pc = qd & 15;
+      const int tok = min(kBlock * j + row, A.N - 1);
+      lds_dma(src.vrows, stage + L::VOFF + 16 * NT * P + wofs, tok * (2 * D) + 16 * (pc ^ (row & 15)), 0);
+    });
+  } else {
+    dma_tile<FP8, NT, PV8, false>(A, src, j, tid, stage);
   }
 }
 
@@ -393,10 +423,11 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   ksc = ksc_next;
 }
 
-// One unrouted block for the direct form of the linear branch (more than half of the blocks
-// routed): accl^T += V^T A^T with A = 448^2 phi(q).phi(K~_s) over its keys, the same products
-// as the routed part above.  Its phi codes and V^T tile are in LDS stage STG; the copy of the
-// next unrouted block (jn >= 0) into the other stage starts first.
+// One unrouted block for the direct form of the linear branch (a large share of the blocks
+// routed): accl^T += V^T A^T with A = 448^2 phi(q).phi(K~_s) over its keys, the products of the
+// routed part above, in bf16 (V^T tiles, or in the low-bit P.V mode the bf16 V rows through
+// transposing reads).  Its tile is in LDS stage STG; the copy of the next unrouted block
+// (jn >= 0) into the other stage starts first.
 template <bool FP8, int QT, bool PV8, int STG>
 __device__ __forceinline__ void lin_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem0, uint8_t* smem1,
                                               int jn, int l16, int g, int tid, const QueryOps<QT>& qo,
@@ -405,7 +436,7 @@ __device__ __forceinline__ void lin_iteration(const FwdArgs& A, FwdState<QT>& st
   using L = FwdLds<FP8, NT, PV8>;
   const uint8_t* stage = STG == 0 ? smem0 : smem1;
   uint8_t* next = STG == 0 ? smem1 : smem0;
-  if (jn >= 0) dma_tile<FP8, NT, PV8, false>(A, src, jn, tid, next);
+  if (jn >= 0) dma_lin<FP8, NT, PV8>(A, src, jn, tid, next);
   __builtin_amdgcn_sched_barrier(0);
   f32x4 Ph[QT][4];
   static_for<4>([&](auto mt) {
@@ -413,50 +444,33 @@ __device__ __forceinline__ void lin_iteration(const FwdArgs& A, FwdState<QT>& st
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) Ph[qt][mt] = mfma_fp8(pr, qo.phq8[qt], f32x4{0.f, 0.f, 0.f, 0.f});
   });
-  if constexpr (PV8) {
-    i32x8 a8[QT];
+  // A of key half s (keys 32s + 16h + 4g + rr) as the bf16 B operand, as for P above
+  bf16x8 aop[QT][2];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      uint32_t aw[4];
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        aw[mt] = pack_fp8x4(clamp_fp8(Ph[qt][mt][0] * 0x1p-10f), clamp_fp8(Ph[qt][mt][1] * 0x1p-10f),
-                            clamp_fp8(Ph[qt][mt][2] * 0x1p-10f), clamp_fp8(Ph[qt][mt][3] * 0x1p-10f));
-      a8[qt] = i32x8{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3], 0, 0, 0, 0};
+    for (int sh = 0; sh < 2; ++sh) {
+      const uint32_t aw[4] = {pack_bf16x2(Ph[qt][2 * sh][0], Ph[qt][2 * sh][1]),
+                              pack_bf16x2(Ph[qt][2 * sh][2], Ph[qt][2 * sh][3]),
+                              pack_bf16x2(Ph[qt][2 * sh + 1][0], Ph[qt][2 * sh + 1][1]),
+                              pack_bf16x2(Ph[qt][2 * sh + 1][2], Ph[qt][2 * sh + 1][3])};
+      aop[qt][sh] = __builtin_bit_cast(bf16x8, aw);
     }
-    const u32x2 ve = *reinterpret_cast<const u32x2*>(stage + L::VEOFF + 8 * l16);
-    static_for<8>([&](auto dt) {
+  static_for<16>([&](auto k) {
+    constexpr int dt = k % 8, sh = k / 8;
+    bf16x8 v;
+    if constexpr (PV8) {   // V rows: keys 32sh + 4g + rr and 32sh + 16 + 4g + rr of feature 16dt + l16
+      const u32x2 a = lds_read_tr16_sw256(stage + L::VOFF, 32 * sh + 4 * g, 16 * dt, l16);
+      const u32x2 b = lds_read_tr16_sw256(stage + L::VOFF, 32 * sh + 16 + 4 * g, 16 * dt, l16);
+      v = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+    } else {
       const int row = 16 * dt + l16;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 64 + 16 * (g ^ ((row >> 2) & 3)));
-      const i32x8 vop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-      const int vs = dt < 4 ? (int)ve.x : (int)ve.y;
+      v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
+                                                                     16 * ((4 * sh + g) ^ (row & 7))));
+    }
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        st.accl[qt][dt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, a8[qt], st.accl[qt][dt], 0, 0,
-                                                                           dt & 3, vs, 0, 127 + 10);
-    });
-  } else {
-    // A of key half s (keys 32s + 16h + 4g + rr) as the bf16 B operand, as for P above
-    bf16x8 aop[QT][2];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const uint32_t aw[4] = {pack_bf16x2(Ph[qt][2 * sh][0], Ph[qt][2 * sh][1]),
-                                pack_bf16x2(Ph[qt][2 * sh][2], Ph[qt][2 * sh][3]),
-                                pack_bf16x2(Ph[qt][2 * sh + 1][0], Ph[qt][2 * sh + 1][1]),
-                                pack_bf16x2(Ph[qt][2 * sh + 1][2], Ph[qt][2 * sh + 1][3])};
-        aop[qt][sh] = __builtin_bit_cast(bf16x8, aw);
-      }
-    static_for<16>([&](auto k) {
-      constexpr int dt = k % 8, sh = k / 8;
-      const int row = 16 * dt + l16;
-      const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + L::VOFF + row * 128 +
-                                                                                 16 * ((4 * sh + g) ^ (row & 7))));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.accl[qt][dt] = mfma_bf16(v, aop[qt][sh], st.accl[qt][dt]);
-    });
-  }
+    for (int qt = 0; qt < QT; ++qt) st.accl[qt][dt] = mfma_bf16(v, aop[qt][sh], st.accl[qt][dt]);
+  });
   wait_dma();
   lds_barrier();
 }
@@ -624,7 +638,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // small difference of two large terms, amplifying the rounding of the routed part; the
   // unrouted part is then summed directly over the unrouted blocks instead (the same products
   // as the routed part above), and H_tot is not used.
-  const bool direct = 2 * topk > A.T && topk < A.T;
+  // (the low-bit P.V mode switches at a third: its routed-part products take e4m3 V, whose
+  // rounding the complement amplifies sooner; its direct loop reads bf16 V rows)
+  const bool direct = (PV8 ? 3 * topk > A.T : 2 * topk > A.T) && topk < A.T;
   if (direct) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
@@ -658,7 +674,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     }
     // nun = T - topk >= 1; every copy below stays in the phi and V^T regions of the stages
     int u = __builtin_amdgcn_readfirstlane((int)ulist[0]);
-    dma_tile<FP8, NT, PV8, false>(A, src, u, tid, smem1);
+    dma_lin<FP8, NT, PV8>(A, src, u, tid, smem1);
     wait_dma();
     lds_barrier();
     for (int n = 0; n < nun; n += 2) {
@@ -914,6 +930,7 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.k_scale = t.k_scale;
     A.vt = ws.vt;
     A.vexp = g.pv8 ? ws.vexp : nullptr;
+    A.v = (const uint16_t*)t.v;
     A.phik8 = ws.phik8;
     A.zrout = ws.zrout;
     A.lut = t.lut;

@@ -192,8 +192,8 @@ def test_every_block_routed_is_softmax_attention(mode):
 @pytest.mark.parametrize("mode", ["bf16", "fp8", "fp8pv"])
 def test_lut_rows_longer_than_a_wave(mode):
     # k_sel > 64: the forward reads the LUT row from memory instead of one register.  27% of
-    # the blocks routed, a ragged last block; the complement form of the linear branch stays
-    # well conditioned at this share (see the design notes for shares near 75%)
+    # the blocks routed (the complement form of the linear branch in every mode), a ragged
+    # last block
     base = "C1" if mode == "bf16" else "C2"
     w = I.make_workload(base, grid=None, N=16350, H=2, seed=42, qk_mode=("fp8pv" if mode == "fp8pv" else None),
                         name=f"k_sel 70 of 256 blocks, {mode}")
@@ -229,13 +229,12 @@ def test_without_per_block_stats_matches_oracle(mode):
         check_head(w, inp, out, 0, h)   # h_sum and z_sum too; per-block h, z absent
 
 
-@pytest.mark.parametrize("mode", ["native", "fp8"])
-@pytest.mark.parametrize("k_sel", [47, 48, 70])
+@pytest.mark.parametrize("mode,k_sel", [(m, k) for m in ("native", "fp8") for k in (47, 48, 70)] +
+                         [("fp8pv", k) for k in (31, 32, 47, 70)])
 def test_large_routed_shares(mode, k_sel):
-    # 94 blocks: k_sel 47 keeps the complement form of the linear branch; 48 and 70 (more than
-    # half routed) sum the unrouted blocks directly, 70 with the LUT row read from memory.
-    # (The low-bit P.V mode is held to the bar up to 27% routed, in the k_sel 70 of 256 case:
-    # above that the e4m3 V of its linear-branch products exceeds it; see the design notes.)
+    # 94 blocks.  bf16 P.V: k_sel 47 keeps the complement form of the linear branch, 48 and 70
+    # (more than half routed) sum the unrouted blocks directly.  Low-bit P.V switches at a
+    # third (31: complement, 32 and up: direct, with bf16 V rows).  70: LUT row from memory.
     w = I.make_workload("C1" if mode == "native" else "C2", grid=None, N=6000, H=2, seed=51,
                         qk_mode=(None if mode == "native" else mode), name=f"k_sel {k_sel} of 94, {mode}")
     inp = I.generate(w)
