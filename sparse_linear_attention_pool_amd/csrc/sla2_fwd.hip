@@ -1,18 +1,20 @@
 // SLA2 fused forward: for each query block i, over the routed key blocks j in LUT order,
 //   S = Q_i K_j^T / sqrt(d) (FP8 e4m3 codes times the two block scales, or bf16),
 //   online softmax (running max and sum, exp2 with log2(e) folded into the scale),
-//   acc += P V_j (bf16 matrix cores);
+//   acc += P V_j (bf16 matrix cores, or e4m3 P and V with power-of-two scales in the low-bit
+//   P.V mode);
 // then O_s = acc / l and the linear branch over the unrouted blocks,
 //   O_l = phi(Q_i) H_i / (phi(Q_i) Z_i + eps), H_i = h_sum - sum_{j routed} h_j, Z_i likewise,
 // and O = alpha * O_s + (1 - alpha) * O_l.  The fp32 kernel gathers the routed h_j, z_j.  The
 // matrix-core kernel never reads h_j: it adds phi(Q_i) times the routed part of H by
 // re-association, sum_{j routed} (phi(Q_i) phi(K~_j)^T) V_j, over the same key and V^T tiles as
-// the sparse branch, and takes Z_R(i) = sum_{j routed} z_j from the precompute.
+// the sparse branch, and takes Z_R(i) = sum_{j routed} z_j from the precompute.  With a large
+// share of the blocks routed it sums phi(Q_i) H_i over the unrouted blocks directly instead.
 //
 // Pages: "SLA2: Sparse-Linear Attention with Learnable Routing and QAT", section 3 (sparse
 // attention only where M = 1 on FlashAttention-style computation; linear branch from the
-// M = 0 statistics; O = alpha * O_s + (1 - alpha) * O_l), section 5 (low-bit Q.K^T with
-// scales), section 6 (M = 1 blocks: sparse scores and values; M = 0 blocks: linear
+// M = 0 statistics; O = alpha * O_s + (1 - alpha) * O_l), section 5 (low-bit Q.K^T, and P
+// and V, with scales), section 6 (M = 1 blocks: sparse scores and values; M = 0 blocks: linear
 // statistics); "SLA: Beyond Sparsity in Diffusion Transformers...", section 3 figure
 // (O_s = diag(l)^-1 O_acc, O_l = phi(Q_i) H_i / (phi(Q_i) Z_i)), section 4 (online softmax
 // with a running max, 1e-5 in the linear denominator), section 7 (the loop walks a LUT of
