@@ -412,8 +412,10 @@ __device__ __forceinline__ double key_score(uint64_t key) {
   return __longlong_as_double((long long)u);
 }
 
-template <int R, int MAXS, int D, bool SOFT>
-__global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__ qhat,
+// NW waves per workgroup: 4, or 8 where the keys of one workgroup fill most of the LDS (so
+// that the CU still runs two waves per SIMD).
+template <int R, int MAXS, int D, bool SOFT, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void topk_kernel(const double* __restrict__ qhat,
                                                       const double* __restrict__ khatT, int T, int topk,
                                                       double inv_sqrt_d, int32_t* __restrict__ lut,
                                                       uint8_t* __restrict__ mask, double tau,
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__
       static_for<HS>([&](auto s) { dst[s] = kb[(size_t)(4 * (half * HS + s)) * T + j]; });
     };
     if (w < ntiles) load_half(kv[0], w, 0);
-    for (int tt = w; tt < ntiles; tt += 4) {
+    for (int tt = w; tt < ntiles; tt += NW) {
       load_half(kv[1], tt, 1);
       // two accumulators (even / odd steps) keep two independent chains in flight
       f64x4 acc0 = f64x4{0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__
         acc0 = mfma_f64(qa[2 * s], kv[0][2 * s], acc0);
         acc1 = mfma_f64(qa[2 * s + 1], kv[0][2 * s + 1], acc1);
       });
-      if (tt + 4 < ntiles) load_half(kv[0], tt + 4, 0);
+      if (tt + NW < ntiles) load_half(kv[0], tt + NW, 0);
       static_for<HS / 2>([&](auto s) {
         acc0 = mfma_f64(qa[HS + 2 * s], kv[1][2 * s], acc0);
         acc1 = mfma_f64(qa[HS + 2 * s + 1], kv[1][2 * s + 1], acc1);
@@ -518,8 +520,9 @@ __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__
   };
 
   // J rows of a wave are searched together, so that their independent steps overlap.
-  constexpr int J = (MAXS <= 8) ? R / 4 : 1;
-  for (int r0 = w * J; r0 < R; r0 += 4 * J) {
+  constexpr int J = (MAXS <= 8) ? R / NW : 1;
+  static_assert(J >= 1, "at least one row per wave");
+  for (int r0 = w * J; r0 < R; r0 += NW * J) {
     uint32_t hi[J][MAXS];
     uint32_t thr[J];
     bool done[J];
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void topk_kernel(const double* __restrict__
   }
 
   if constexpr (SOFT) {
-    for (int r = w; r < R; r += 4) {
+    for (int r = w; r < R; r += NW) {
       if (i0 + r >= T) break;
       double p[MAXS];
       static_for<MAXS>([&](auto s) {
@@ -582,24 +585,25 @@ struct SoftOut {
   float* lambda;
 };
 
-template <int R, int MAXS, int D, bool SOFT>
+template <int R, int MAXS, int D, bool SOFT, int NW = 4>
 static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
                           hipStream_t s) {
   const size_t lds = (size_t)R * g.T * sizeof(uint64_t);
   static bool attr_set = false;   // dynamic LDS above the 64 KB default
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D, SOFT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D, SOFT, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)kTopkLdsBudget);
     attr_set = true;
   }
   dim3 grid((g.T + R - 1) / R, g.BH);
-  hipLaunchKernelGGL((topk_kernel<R, MAXS, D, SOFT>), grid, dim3(256), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
+  hipLaunchKernelGGL((topk_kernel<R, MAXS, D, SOFT, NW>), grid, dim3(64 * NW), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
                      1.0 / sqrt((double)g.D), t.lut, t.mask, so.tau, so.mask, so.lambda);
 }
 
 // Rows per workgroup R: 16 (one matrix-core tile) when the keys fit in the LDS budget, else
 // 8 or 4.  Candidate slots per lane MAXS: the smallest of 4, 8, 16, 24, 32, 64 that is at
-// least ceil(T / 64).  T <= 4096 leaves the pairs below.
+// least ceil(T / 64).  T <= 4096 leaves the pairs below.  The hard 16-row tiers above 8 slots
+// (T > 512, keys of 64 KB and more) run 8 waves per workgroup.
 template <int D, bool SOFT>
 static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
                         hipStream_t s) {
@@ -611,9 +615,9 @@ static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspac
   if (SOFT && S > 8 && R > 8) R = 8;
   if (R == 16 && S <= 4) launch_topk_s<16, 4, D, SOFT>(g, t, ws, so, s);
   else if (R == 16 && S <= 8) launch_topk_s<16, 8, D, SOFT>(g, t, ws, so, s);
-  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D, SOFT>(g, t, ws, so, s);
-  else if (R == 16 && S <= 24) launch_topk_s<16, 24, D, SOFT>(g, t, ws, so, s);
-  else if (R == 16) launch_topk_s<16, 32, D, SOFT>(g, t, ws, so, s);
+  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D, SOFT, 8>(g, t, ws, so, s);
+  else if (R == 16 && S <= 24) launch_topk_s<16, 24, D, SOFT, 8>(g, t, ws, so, s);
+  else if (R == 16) launch_topk_s<16, 32, D, SOFT, 8>(g, t, ws, so, s);
   else if (R == 8 && S <= 16) launch_topk_s<8, 16, D, SOFT>(g, t, ws, so, s);
   else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT>(g, t, ws, so, s);
   else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT>(g, t, ws, so, s);
