@@ -602,8 +602,9 @@ static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Worksp
 
 // Rows per workgroup R: 16 (one matrix-core tile) when the keys fit in the LDS budget, else
 // 8 or 4.  Candidate slots per lane MAXS: the smallest of 4, 8, 16, 24, 32, 64 that is at
-// least ceil(T / 64).  T <= 4096 leaves the pairs below.  The hard 16-row tiers above 8 slots
-// (T > 512, keys of 64 KB and more) run 8 waves per workgroup.
+// least ceil(T / 64).  T <= 4096 leaves the pairs below.  The hard tiers whose keys allow one
+// workgroup per CU (16 rows above 8 slots, and 8 rows) run 8 waves per workgroup; the soft
+// phase keeps 4 waves and 8 rows, which ran faster.
 template <int D, bool SOFT>
 static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
                         hipStream_t s) {
@@ -619,10 +620,10 @@ static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspac
   else if (R == 16 && S <= 24) launch_topk_s<16, 24, D, SOFT, 8>(g, t, ws, so, s);
   else if (R == 16) launch_topk_s<16, 32, D, SOFT, 8>(g, t, ws, so, s);
   else if (R == 8 && S <= 16) launch_topk_s<8, 16, D, SOFT>(g, t, ws, so, s);
-  else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT>(g, t, ws, so, s);
-  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT>(g, t, ws, so, s);
+  else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);
+  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);
   else if constexpr (SOFT) launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);   // 8 rows would spill
-  else if (R == 8) launch_topk_s<8, 64, D, SOFT>(g, t, ws, so, s);
+  else if (R == 8) launch_topk_s<8, 64, D, SOFT, 8>(g, t, ws, so, s);
   else launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);
 }
 
