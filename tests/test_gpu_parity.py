@@ -204,11 +204,13 @@ def test_lut_rows_longer_than_a_wave(mode):
         check_head(w, inp, out, 0, h, topk=70, check_stats=(h == 0), query_blocks=[0, 1, 100, 177, T - 2, T - 1])
 
 
-@pytest.mark.parametrize("N", [57000, 128000, 262144])
+@pytest.mark.parametrize("N", [57000, 90000, 128000, 150000, 262144])
 def test_router_tiers_up_to_the_largest_sequence(N):
-    # T = 891, 2000 and 4096 blocks: the Top-k kernel's 16-, 32- and 64-slot tiers (16, 8 and 4
-    # rows per workgroup as the score rows outgrow the LDS); 3% routed, so k_sel reaches 123 and
-    # the forward reads its LUT rows from memory.  Router, quantiser and sampled query blocks.
+    # T = 891, 1407, 2000, 2344 and 4096 blocks: the Top-k kernel's 16-slot tier at 16 rows per
+    # workgroup, its 24-, 32- and 64-slot tiers at 8 rows, and the 64-slot tier at 4 rows (fewer
+    # rows as the score rows outgrow the LDS; the 16- and 8-row tiers here run 8 waves); 3%
+    # routed, so k_sel reaches 123 and the forward reads its LUT rows from memory.  Router,
+    # quantiser and sampled query blocks.
     w = I.make_workload("C2", grid=None, N=N, H=1, seed=47, name=f"router tiers N={N}")
     inp = I.generate(w)
     out = run_gpu(w, inp)
