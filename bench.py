@@ -115,17 +115,62 @@ def cpu_baseline(w: I.Workload, inp: dict, heads: int):
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
     lut_flops = 0
+    refs = []
     for h in range(heads):
         r = O.forward_head(inp["q"][0, h], inp["k"][0, h], inp["v"][0, h], inp["alpha"][h], inp["wq"],
                            inp["wk"], topk=w.topk, qk_fp8=(w.qk_mode == "fp8"))
         lut_flops += A.sparse_flops_from_lut(r["lut"][None], w.N, w.d)
+        refs.append({"o": r["o"], "lut": r["lut"], "scores": r["scores"]})
     dt = time.perf_counter() - t0
     flops = lut_flops + A.linear_flops(1, heads, w.N, w.d)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS (effective)", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{heads} of {w.H} heads of the same workload (batch 0), full sequence, fp64 numpy",
             "host_cpus": os.cpu_count(),
-            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}, refs
+
+
+def pass_times(evs):
+    """Mean, median and min (ms) of each call's event interval over the recorded steps."""
+    names = ("route", "precompute", "fwd")
+    outp = {}
+    for c, name in enumerate(names):
+        x = np.array([e[c].elapsed_time(e[c + 1]) for e in evs])
+        outp[name] = {"mean": float(x.mean()), "median": float(np.median(x)), "min": float(x.min())}
+    return outp
+
+
+TIE_GAP = 1e-5   # rows whose k-th and (k+1)-th block scores are this close may route either way
+
+
+def parity_check(w: I.Workload, refs, lut_gpu, o_gpu):
+    """The timed run's LUT and O against the oracle, on every query block of the sampled heads:
+    LUT rows bit-exact outside tie rows; O within max-abs 2e-2 and mean-rel 1e-2 (bf16/FP8) or
+    max-abs 1e-4 (fp32) on the query blocks whose LUT row equals the oracle's."""
+    tol_abs = 2e-2 if w.dtype == "bf16" else 1e-4
+    tol_rel = 1e-2 if w.dtype == "bf16" else None
+    lut_diff = ties = 0
+    err_max = err_sum = ref_sum = 0.0
+    n_el = 0
+    for h, r in enumerate(refs):
+        g = lut_gpu[0, h]
+        srt = -np.sort(-r["scores"], axis=1)
+        tie = (srt[:, w.topk - 1] - srt[:, w.topk]) <= TIE_GAP if w.topk < w.T else np.zeros(w.T, bool)
+        same = np.all(g == r["lut"], axis=1)
+        ties += int(tie.sum())
+        lut_diff += int(np.sum(~same & ~tie))
+        rows = np.repeat(same, 64)[:w.N]
+        d = np.abs(o_gpu[0, h][rows].astype(np.float64) - r["o"][rows])
+        err_max = max(err_max, float(d.max()) if d.size else 0.0)
+        err_sum += float(d.sum())
+        ref_sum += float(np.abs(r["o"][rows]).sum())
+        n_el += d.size
+    mean_rel = err_sum / max(ref_sum, 1e-30)
+    ok = lut_diff == 0 and err_max <= tol_abs and (tol_rel is None or mean_rel <= tol_rel)
+    return {"heads": len(refs), "query_blocks": len(refs) * w.T, "lut_rows_diff": lut_diff,
+            "tie_rows": ties, "o_elements": n_el, "max_abs": float(f"{err_max:.4g}"),
+            "mean_rel": float(f"{mean_rel:.4g}"), "tol_max_abs": tol_abs, "tol_mean_rel": tol_rel,
+            "ok": bool(ok)}
 
 
 def main():
@@ -134,7 +179,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2", choices=sorted(I.CONFIGS))
-    ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=12,
+                    help="heads in the CPU oracle sample, also checked against the timed run (0 = skip)")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="steps timed after a 1 GiB cache-flushing fill each (0 = skip)")
     ap.add_argument("--backward", action="store_true",
                     help="also time sla2_attention_bwd (default for the C4 fine-tuning workload)")
     ap.add_argument("--pv-fp8", type=int, default=1,
@@ -203,13 +251,28 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    t_route = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_pre = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_fwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    warm = pass_times(evs)
+    t_route, t_pre, t_fwd = warm["route"]["mean"], warm["precompute"]["mean"], warm["fwd"]["mean"]
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms); "
         f"route {t_route:.4f} precompute {t_pre:.4f} fwd {t_fwd:.4f} ms")
-
+    # the timed run's outputs, before any other leg touches the buffers
     lut = bufs["lut"].cpu().numpy()
+    o_gpu = bufs["o"].float().cpu().numpy() if args.cpu_heads > 0 else None
+
+    # cold passes: a 1 GiB fill (four times the 256 MB MALL) before each step, so every pass
+    # starts from memory that is not in any cache; per-pass events as above
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_reps)]
+        for k in range(args.cold_reps):
+            flush.fill_(float(k))
+            step(evc[k])
+        torch.cuda.synchronize(dev)
+        cold = pass_times(evc)
+        del flush
+        log(f"[bench] cold (MALL flushed), median: route {cold['route']['median']:.4f} precompute "
+            f"{cold['precompute']['median']:.4f} fwd {cold['fwd']['median']:.4f} ms")
     f_sparse = A.sparse_flops_from_lut(lut, w.N, w.d)
     f_lin = A.linear_flops(w.B, w.H, w.N, w.d)
     f_eff = f_sparse + f_lin
@@ -228,7 +291,13 @@ def main():
         "precompute_GBps": round(kb["precompute"] / (t_pre * 1e-3) / 1e9, 1),
         "fwd_ms": round(float(t_fwd), 5),
         "fwd_routed_TFLOPS": round(achieved, 2),
+        "warm": {k: {s: round(float(v), 5) for s, v in st.items()} for k, st in warm.items()},
     }
+    if cold is not None:
+        passes["cold"] = {k: {s: round(float(v), 5) for s, v in st.items()} for k, st in cold.items()}
+        passes["cold_GBps_median"] = {
+            "route": round(kb["route"] / (cold["route"]["median"] * 1e-3) / 1e9, 1),
+            "precompute": round(kb["precompute"] / (cold["precompute"]["median"] * 1e-3) / 1e9, 1)}
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -328,10 +397,17 @@ def main():
         passes["soft_route_ms"] = round(float(t_soft), 5)
         passes["soft_route_tau"] = args.soft_tau
         log(f"[bench] sla2_route_soft (tau {args.soft_tau}): {t_soft:.4f} ms")
+    ok = True
     if args.cpu_heads > 0:
         log(f"[bench] timing the CPU oracle on {args.cpu_heads} heads")
-        out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_heads, w.H))
+        out["cpu_baseline"], refs = cpu_baseline(w, inp, min(args.cpu_heads, w.H))
+        out["parity"] = parity_check(w, refs, lut, o_gpu)
+        ok = out["parity"]["ok"]
+        log(f"[bench] parity of the timed run against the oracle: {out['parity']}")
     print(json.dumps(out), flush=True)
+    if not ok:
+        log("[bench] the timed run's output does not match the oracle")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -8,9 +8,9 @@ Counts what the method must compute, not what dense attention would:
   over every query (2*N*d^2), so 4*N*d^2 per (batch, head);
 * dense attention: 4*N^2*d per (batch, head).
 With 3% of 512 key blocks rounded to 15 and the linear branch at 4*N*d^2,
-the saving at N = 32760, d = 128 is 96.68%, which is the "about 96.7%
-computation savings after accounting for the linear branch" that the SLA2
-page gives for 97% sparsity (section 1).
+the saving at N = 32760, d = 128 is 96.68%.  That matches the roughly 96.7%
+saving the SLA2 page reports at 97% sparsity once the linear branch is
+counted (SLA2 page, section 1).
 """
 from __future__ import annotations
 

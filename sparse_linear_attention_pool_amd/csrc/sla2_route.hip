@@ -617,8 +617,7 @@ static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspac
   if (R == 16 && S <= 4) launch_topk_s<16, 4, D, SOFT>(g, t, ws, so, s);
   else if (R == 16 && S <= 8) launch_topk_s<16, 8, D, SOFT>(g, t, ws, so, s);
   else if (R == 16 && S <= 16) launch_topk_s<16, 16, D, SOFT, 8>(g, t, ws, so, s);
-  else if (R == 16 && S <= 24) launch_topk_s<16, 24, D, SOFT, 8>(g, t, ws, so, s);
-  else if (R == 16) launch_topk_s<16, 32, D, SOFT, 8>(g, t, ws, so, s);
+  else if (R == 16) launch_topk_s<16, 24, D, SOFT, 8>(g, t, ws, so, s);   // 16 rows fit only T <= 1280: S <= 20
   else if (R == 8 && S <= 16) launch_topk_s<8, 16, D, SOFT>(g, t, ws, so, s);
   else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);
   else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);

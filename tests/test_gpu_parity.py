@@ -322,6 +322,8 @@ def test_fp8_encoder_on_every_bf16_value():
 
 # ----------------------------------------------------------------------------- full sizes
 def _sampled_full(base, heads, blocks_per_head=6, **overrides):
+    """Full-size run; parity of the listed heads on `blocks_per_head` sampled query blocks
+    (always the first and the last), or on every query block when blocks_per_head is None."""
     w = I.make_workload(base, **overrides) if overrides else I.CONFIGS[base]
     say(f"[full] generating {w.name}")
     inp = I.generate(w)
@@ -329,8 +331,12 @@ def _sampled_full(base, heads, blocks_per_head=6, **overrides):
     T = w.T
     rng = np.random.default_rng(123)
     for (b, h) in heads:
-        qb = sorted(set([0, T - 1] + rng.integers(0, T, blocks_per_head - 2).tolist()))
-        say(f"  head ({b},{h}) query blocks {qb}")
+        if blocks_per_head is None:
+            qb = None
+            say(f"  head ({b},{h}) every query block")
+        else:
+            qb = sorted(set([0, T - 1] + rng.integers(0, T, blocks_per_head - 2).tolist()))
+            say(f"  head ({b},{h}) query blocks {qb}")
         check_head(w, inp, out, b, h, query_blocks=qb, check_stats=(h == heads[0][1]))
 
 
@@ -338,13 +344,15 @@ def test_full_size_c1_sampled():
     _sampled_full("C1", [(0, 0), (0, 7)])
 
 
-def test_full_size_c2_sampled():
-    _sampled_full("C2", [(0, 0), (0, 5), (0, 11)])
+def test_full_size_c2_every_block():
+    """The benchmark workload at its launch configuration: LUT, mask, quantiser codes and O of
+    all 12 heads x 512 query blocks against the oracle."""
+    _sampled_full("C2", [(0, h) for h in range(12)], blocks_per_head=None)
 
 
 def test_full_size_c2_low_bit_pv_sampled():
     _sampled_full("C2", [(0, 0), (0, 11)], qk_mode="fp8pv", name="C2 fp8 P.V")
 
 
-def test_full_size_c3_sampled():
-    _sampled_full("C3", [(0, 0), (0, 39)], blocks_per_head=4)
+def test_full_size_c3_two_heads_every_block():
+    _sampled_full("C3", [(0, 0), (0, 39)], blocks_per_head=None)
