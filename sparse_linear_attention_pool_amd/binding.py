@@ -22,8 +22,8 @@ SLA2_F32, SLA2_BF16 = 0, 1
 SLA2_QK_NATIVE, SLA2_QK_FP8_E4M3, SLA2_QK_PV_FP8_E4M3 = 0, 1, 2
 
 ENTRY_POINTS = ("sla2_buffer_sizes", "sla2_route", "sla2_linear_precompute", "sla2_attention_fwd",
-                "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_route_soft", "sla2_status_string",
-                "sla2_last_error")
+                "sla2_attention_bwd", "sla2_selftest_mfma", "sla2_route_soft", "sla2_route_noalloc",
+                "sla2_status_string", "sla2_last_error")
 
 
 class SLA2Error(RuntimeError):
@@ -62,7 +62,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(_LIB_PATH)
     P, T = ctypes.POINTER(Params), ctypes.POINTER(Tensors)
     lib.sla2_buffer_sizes.argtypes = [P, ctypes.POINTER(Sizes)]
-    for name in ("sla2_route", "sla2_linear_precompute", "sla2_attention_fwd"):
+    for name in ("sla2_route", "sla2_route_noalloc", "sla2_linear_precompute", "sla2_attention_fwd"):
         getattr(lib, name).argtypes = [P, T, ctypes.c_void_p]
     lib.sla2_attention_bwd.argtypes = [P, T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -73,7 +73,7 @@ def _load() -> ctypes.CDLL:
     lib.sla2_last_error.restype = ctypes.c_char_p
     lib.sla2_last_error.argtypes = []
     lib.sla2_route_soft.argtypes = [P, T, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    for name in ENTRY_POINTS[:7]:
+    for name in ENTRY_POINTS[:8]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -128,6 +128,12 @@ def _stream(stream) -> Optional[int]:
 def sla2_route(params: Params, tensors: dict, stream=None) -> None:
     tt = _tensors(tensors)
     _check("sla2_route", lib.sla2_route(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
+
+
+def sla2_route_noalloc(params: Params, tensors: dict, stream=None) -> None:
+    """sla2_route with the router's scratch in the library's device array (no workspace)."""
+    tt = _tensors(tensors)
+    _check("sla2_route_noalloc", lib.sla2_route_noalloc(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
 
 
 def sla2_route_soft(params: Params, tensors: dict, tau: float, soft_mask, lam, stream=None) -> None:

@@ -4,9 +4,17 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "sla2_internal.hpp"
+
+// Scratch of sla2_route_noalloc: the router's fp64 block sums, key-mean partials and projected
+// pooled rows, for callers that cannot allocate device memory.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never passes this name to a kernel (it
+// is a host-side stand-in there): it looks up the device address once per device and uses that.
+constexpr size_t kRouteScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
 
 namespace sla2 {
 namespace {
@@ -65,20 +73,35 @@ int check_params(const sla2_params* p, Geometry* g) {
 
 }  // namespace
 
-size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
-  const size_t BH = g.BH, T = g.T, D = g.D, P = g.P, P32 = (g.T + 31) / 32;
+// The router's part of the workspace (the first five regions of workspace_layout), used by
+// sla2_route and sla2_route_soft only.  Returns its size in bytes.
+size_t route_layout(const Geometry& g, Workspace* ws, char* base) {
+  const size_t BH = g.BH, T = g.T, D = g.D, P32 = (g.T + 31) / 32;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align256(off + bytes);
     return base ? base + o : nullptr;
   };
-  Workspace w;
+  Workspace w{};
   w.qsum = (double*)take(BH * T * D * sizeof(double));
   w.ksum = (double*)take(BH * T * D * sizeof(double));
   w.mu = (double*)take((BH * P32 * D + BH * D) * sizeof(double));
   w.qhat = (double*)take(BH * T * D * sizeof(double));
   w.khatT = (double*)take(BH * D * T * sizeof(double));
+  if (ws) *ws = w;
+  return off;
+}
+
+size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
+  const size_t BH = g.BH, T = g.T, D = g.D, P = g.P;
+  Workspace w;
+  size_t off = route_layout(g, &w, base);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return base ? base + o : nullptr;
+  };
   w.hpart = (float*)take(BH * P * D * D * sizeof(float));
   w.zpart = (float*)take(BH * P * D * sizeof(float));
   w.vt = (uint16_t*)take(g.bf16 ? BH * T * D * 64 * (g.pv8 ? 1 : sizeof(uint16_t)) : 0);
@@ -90,6 +113,33 @@ size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
   if (ws) *ws = w;
   return off;
 }
+
+namespace {
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 256;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device ordinal, once looked up
+
+// The device address of this GPU's copy of `scratch` (the current device's), looked up on the
+// first call on that device.
+int route_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(SLA2_ERR_UNSUPPORTED, "%s: device ordinal %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (ptr == nullptr) return fail(SLA2_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SLA2_OK;
+}
+
+}  // namespace
 
 }  // namespace sla2
 
@@ -165,6 +215,37 @@ int sla2_route(const sla2_params* p, const sla2_tensors* t, void* stream) {
     REQUIRE(t->q8, "q8");
     REQUIRE(t->q_scale, "q_scale");
   }
+  return hip_status(launch_route(g, *t, ws, (hipStream_t)stream), fn);
+}
+
+int sla2_route_noalloc(const sla2_params* p, const sla2_tensors* t, void* stream) {
+  const char* fn = "sla2_route_noalloc";
+  Geometry g;
+  int st = check_params(p, &g);
+  if (st != SLA2_OK) return st;
+  if (t == nullptr) return fail(SLA2_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
+  const size_t need = route_layout(g, nullptr, nullptr);
+  if (need > kRouteScratchBytes)
+    return fail(SLA2_ERR_UNSUPPORTED,
+                "%s: these sizes need %zu bytes of router scratch, more than the %zu this entry point holds "
+                "(about 32 * d bytes per query block of every head); use sla2_route with a workspace",
+                fn, need, kRouteScratchBytes);
+  REQUIRE(t->q, "q");
+  REQUIRE(t->k, "k");
+  REQUIRE(t->q_pool, "q_pool");
+  REQUIRE(t->k_pool, "k_pool");
+  REQUIRE(t->k_mean, "k_mean");
+  REQUIRE(t->lut, "lut");
+  REQUIRE(t->mask, "mask");
+  if (g.fp8) {
+    REQUIRE(t->q8, "q8");
+    REQUIRE(t->q_scale, "q_scale");
+  }
+  void* base = nullptr;
+  st = route_scratch(fn, &base);
+  if (st != SLA2_OK) return st;
+  Workspace ws;
+  route_layout(g, &ws, (char*)base);
   return hip_status(launch_route(g, *t, ws, (hipStream_t)stream), fn);
 }
 

@@ -44,6 +44,7 @@ struct Workspace {
 };
 
 size_t workspace_layout(const Geometry& g, Workspace* ws, char* base);
+size_t route_layout(const Geometry& g, Workspace* ws, char* base);
 
 // Views into the caller's backward workspace (layout fixed by bwd_workspace_layout()).  The
 // first three are written by the forward pass when it is given the backward workspace.
