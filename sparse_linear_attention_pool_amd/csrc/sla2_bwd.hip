@@ -428,7 +428,7 @@ __device__ __forceinline__ void q_dma(const QSrc& s, int j, int N, int tid, uint
   const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
   {
     const int row = tid >> 3, pc = tid & 7;
-    lds_dma(s.k8, st + qlds::K8 + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * 8192);
+    lds_dma(s.k8, st + qlds::K8 + wofs, row * 128 + 16 * fp8_chunk(row, pc), j * 8192);
   }
   static_for<2>([&](auto P) {
     const int qd = tid + kNT2 * P, row = qd >> 4, pc = qd & 15;
@@ -750,7 +750,7 @@ __device__ __forceinline__ void k_dma(const KSrc& s, int i, int N, int tid, uint
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wofs = 1024 * w;
   {
     const int row = tid >> 3, pc = tid & 7;
-    lds_dma(s.q8, st + klds::Q8 + wofs, row * 128 + 16 * (pc ^ (row & 7)), i * 8192);
+    lds_dma(s.q8, st + klds::Q8 + wofs, row * 128 + 16 * fp8_chunk(row, pc), i * 8192);
   }
   static_for<2>([&](auto P) {
     const int qd = tid + kNT2 * P, row = qd >> 4, pc = qd & 15;

@@ -138,8 +138,8 @@ __device__ __forceinline__ void lds_barrier() {
 // Tiles move from memory straight into LDS (buffer loads with the LDS destination): lane l
 // of a wave writes the 16 bytes at its wave's LDS pointer + 16 l, so each thread loads the
 // chunk that belongs at its LDS slot.  A swizzle of the LDS rows (chunk c of row r at
-// position c ^ (r & 7), or c ^ (r & 15) for 256-byte rows) is applied to the memory address
-// instead.  Callers keep every read inside the buffer.
+// position c ^ (r & 7), fp8_chunk(r, c) for e4m3 rows read by lds_fp8_row, or c ^ (r & 15) for
+// 256-byte rows) is applied to the memory address instead.  Callers keep every read inside the buffer.
 __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
@@ -147,12 +147,19 @@ __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* lds,
 // All of this wave's tile copies have landed in LDS (they count as vector-memory loads).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
 
-// 32 e4m3 codes of one 128-byte LDS row (logical chunks 2g and 2g+1): the A operand of a
-// 16x16x128 matrix-core product for row `row`.
+// Physical slot of 16-byte chunk c in row r of a tile of 128-byte e4m3 rows: c XOR the 3-bit
+// left rotation of r mod 8 (an involution, so the copy into LDS fetches chunk fp8_chunk(r, p)
+// for slot p).  Measured on gfx950, the two reads of lds_fp8_row (16 consecutive rows, chunks
+// 2g and 2g+1 for lane group g) then run at the full LDS read rate of 256 bytes per clock and
+// CU; with c XOR (r mod 8) every such read costs two passes.
+__device__ __forceinline__ int fp8_chunk(int row, int c) { return c ^ (((row << 1) | ((row >> 2) & 1)) & 7); }
+
+// 32 e4m3 codes of one 128-byte LDS row (logical chunks 2g and 2g+1, stored at fp8_chunk): the
+// A operand of a 16x16x128 matrix-core product for row `row`.
 __device__ __forceinline__ i32x8 lds_fp8_row(const uint8_t* base, int row, int g) {
   const uint8_t* r = base + row * 128;
-  const u32x4 a = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g) ^ (row & 7)));
-  const u32x4 b = *reinterpret_cast<const u32x4*>(r + 16 * ((2 * g + 1) ^ (row & 7)));
+  const u32x4 a = *reinterpret_cast<const u32x4*>(r + 16 * fp8_chunk(row, 2 * g));
+  const u32x4 b = *reinterpret_cast<const u32x4*>(r + 16 * fp8_chunk(row, 2 * g + 1));
   return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 

@@ -115,7 +115,7 @@ __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, i
     uint8_t* dst = stage + 16 * NT * P + wofs;
     if constexpr (FP8) {
       const int row = qd >> 3, pc = qd & 7;
-      lds_dma(src.k, dst, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
+      lds_dma(src.k, dst, row * 128 + 16 * fp8_chunk(row, pc), j * (kBlock * D));
     } else {
       const int row = qd >> 4, pc = qd & 15;
       const int tok = min(kBlock * j + row, A.N - 1);   // rows past N: any finite row, masked later
@@ -124,7 +124,7 @@ __device__ __forceinline__ void dma_tile(const FwdArgs& A, const TileSrc& src, i
   });
   static_for<L::PLOADS>([&](auto P) {
     const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
-    lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
+    lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * fp8_chunk(row, pc), j * (kBlock * D));
   });
   if constexpr (PV8) {
     static_for<L::VLOADS>([&](auto P) {
@@ -153,7 +153,7 @@ __device__ __forceinline__ void dma_lin(const FwdArgs& A, const TileSrc& src, in
     const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);
     static_for<L::PLOADS>([&](auto P) {
       const int qd = tid + NT * P, row = qd >> 3, pc = qd & 7;
-      lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * (pc ^ (row & 7)), j * (kBlock * D));
+      lds_dma(src.phik8, stage + L::POFF + 16 * NT * P + wofs, row * 128 + 16 * fp8_chunk(row, pc), j * (kBlock * D));
     });
     static_for<64 * 256 / (16 * NT)>([&](auto P) {
       const int qd = tid + NT * P, row = qd >> 4, pc = qd & 15;
