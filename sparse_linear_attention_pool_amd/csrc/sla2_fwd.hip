@@ -528,6 +528,111 @@ __device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
   return i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3], (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
 }
 
+// Epilogue of the fused forward for this wave's queries: O_s = acc / l, the linear branch
+// O_l = (phi(q) H_tot - routed part) / (phi(q).(Z_tot - Z_R) + eps) (or the unrouted part itself
+// in the direct form), O = alpha O_s + (1 - alpha) O_l, and the optional lse and backward stores.
+// The bf16 LDS image of H^T has rows 0..63 at Hlo and rows 64..127 at Hhi (256-byte rows, chunk
+// k of row r at chunk k ^ (r % 16)).
+template <bool FP8, int QT>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& A, const FwdState<QT>& st, const QueryOps<QT>& qo,
+                                             const uint8_t* Hlo, const uint8_t* Hhi, bool direct,
+                                             const float* alphaS, const float* zrS, int bh, const int (&qrow)[QT],
+                                             const bool (&qok)[QT], int l16, int g, int topk) {
+  constexpr int D = 128;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = rows4_sum(st.l_run[qt]);
+    constexpr float kCodes2 = 1.f / (kPhiCodeScale * kPhiCodeScale);   // undo the code scales
+    const float inv_l = 1.f / l_tot;
+    // denominator over the unrouted blocks: phi(q).(Z_tot - Z_R), with the bf16 phi(q)
+    float den = 0.f;
+    {
+      const float* zt = A.z_sum + (size_t)bh * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 bw = __builtin_bit_cast(u32x4, qo.phb[qt][s]);
+        const uint32_t ww[4] = {bw.x, bw.y, bw.z, bw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int a = 32 * s + 8 * g + 2 * e;
+          den = fmaf(bf16_lo(ww[e]), zt[a] - zrS[a], den);
+          den = fmaf(bf16_hi(ww[e]), zt[a + 1] - zrS[a + 1], den);
+        }
+      }
+    }
+    // with every block routed the linear branch is an empty sum, 0 (the complement form would
+    // leave only rounding, amplified by 1/eps)
+    const float inv_den = topk < A.T ? 1.f / (rows4_sum(den) + A.eps) : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      // numerator over the unrouted blocks: phi(q) H_tot minus the routed part, or (direct)
+      // the unrouted part itself
+      f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
+      float lsign = -kCodes2;
+      if (!direct) {
+        const int hr = 16 * dt + l16;
+        const uint8_t* hrow = (dt < 4 ? Hlo : Hhi) + (hr & 63) * 256;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
+          ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.phb[qt][s], ol);
+        }
+      } else {
+        lsign = kCodes2;
+      }
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(alphaS + 16 * dt + 4 * g);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      float ov[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        ov[rr] = av[rr] * (st.acc[qt][dt][rr] * inv_l) +
+                 (1.f - av[rr]) * (fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den);
+      if (qok[qt]) {
+        u32x2 sv;
+        sv.x = pack_bf16x2(ov[0], ov[1]);
+        sv.y = pack_bf16x2(ov[2], ov[3]);
+        const size_t e0 = ((size_t)bh * A.N + qrow[qt]) * D + 16 * dt + 4 * g;
+        *reinterpret_cast<u32x2*>(A.o + e0) = sv;
+        if (A.os != nullptr) {   // the two branches, for the backward pass
+          float sv4[4], lv4[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            sv4[rr] = st.acc[qt][dt][rr] * inv_l;
+            lv4[rr] = fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den;
+          }
+          u32x2 s2, l2;
+          s2.x = pack_bf16x2(sv4[0], sv4[1]);
+          s2.y = pack_bf16x2(sv4[2], sv4[3]);
+          l2.x = pack_bf16x2(lv4[0], lv4[1]);
+          l2.y = pack_bf16x2(lv4[2], lv4[3]);
+          *reinterpret_cast<u32x2*>(A.os + e0) = s2;
+          *reinterpret_cast<u32x2*>(A.ol + e0) = l2;
+        }
+      }
+    }
+    if (A.os != nullptr && g == 0 && qok[qt]) A.inv_den[(size_t)bh * A.T * kBlock + qrow[qt]] = inv_den;
+    if (A.lse != nullptr) {
+      // native mode scored the raw keys: log-sum-exp over K~ = K - mu is lower by q.mu/sqrt(d)
+      float shift = 0.f;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 wv = __builtin_bit_cast(u32x4, qo.qb[qt][s]);
+          const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+          const float* mu = A.k_mean + (size_t)bh * D + 32 * s + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            shift = fmaf(bf16_lo(ww[e]), mu[2 * e], shift);
+            shift = fmaf(bf16_hi(ww[e]), mu[2 * e + 1], shift);
+          }
+        }
+        shift = rows4_sum(shift) * (1.f / sqrtf((float)D));
+      }
+      if (g == 0 && qok[qt]) A.lse[(size_t)bh * A.N + qrow[qt]] = (st.m_run[qt] + log2f(l_tot)) * kLn2 - shift;
+    }
+  }
+}
+
 // One workgroup of 4/QT waves per (head, query block).  Wave w owns queries
 // 16 QT w + 16 qt + (0..15), qt < QT, and computes S^T = K_j Q^T so that each lane holds one
 // query (l % 16) of each tile and 16 of the block's keys (16mt + 4(l/16) + rr): the softmax
@@ -692,98 +797,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // ---------------- epilogue ----------------
   // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = rows4_sum(st.l_run[qt]);
-    constexpr float kCodes2 = 1.f / (kPhiCodeScale * kPhiCodeScale);   // undo the code scales
-    const float inv_l = 1.f / l_tot;
-    // denominator over the unrouted blocks: phi(q).(Z_tot - Z_R), with the bf16 phi(q)
-    float den = 0.f;
-    {
-      const float* zt = A.z_sum + (size_t)bh * D;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 bw = __builtin_bit_cast(u32x4, qo.phb[qt][s]);
-        const uint32_t ww[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int a = 32 * s + 8 * g + 2 * e;
-          den = fmaf(bf16_lo(ww[e]), zt[a] - zrS[a], den);
-          den = fmaf(bf16_hi(ww[e]), zt[a + 1] - zrS[a + 1], den);
-        }
-      }
-    }
-    // with every block routed the linear branch is an empty sum, 0 (the complement form would
-    // leave only rounding, amplified by 1/eps)
-    const float inv_den = topk < A.T ? 1.f / (rows4_sum(den) + A.eps) : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      // numerator over the unrouted blocks: phi(q) H_tot minus the routed part, or (direct)
-      // the unrouted part itself
-      f32x4 ol = f32x4{0.f, 0.f, 0.f, 0.f};
-      float lsign = -kCodes2;
-      if (!direct) {
-        const int hr = 16 * dt + l16;
-        const uint8_t* hrow = Hs + hr * 256;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(hrow + 16 * ((4 * s + g) ^ (hr & 15)));
-          ol = mfma_bf16(__builtin_bit_cast(bf16x8, a), qo.phb[qt][s], ol);
-        }
-      } else {
-        lsign = kCodes2;
-      }
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(alphaS + 16 * dt + 4 * g);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-      float ov[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        ov[rr] = av[rr] * (st.acc[qt][dt][rr] * inv_l) +
-                 (1.f - av[rr]) * (fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den);
-      if (qok[qt]) {
-        u32x2 sv;
-        sv.x = pack_bf16x2(ov[0], ov[1]);
-        sv.y = pack_bf16x2(ov[2], ov[3]);
-        const size_t e0 = ((size_t)bh * A.N + qrow[qt]) * D + 16 * dt + 4 * g;
-        *reinterpret_cast<u32x2*>(A.o + e0) = sv;
-        if (A.os != nullptr) {   // the two branches, for the backward pass
-          float sv4[4], lv4[4];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            sv4[rr] = st.acc[qt][dt][rr] * inv_l;
-            lv4[rr] = fmaf(lsign, st.accl[qt][dt][rr], ol[rr]) * inv_den;
-          }
-          u32x2 s2, l2;
-          s2.x = pack_bf16x2(sv4[0], sv4[1]);
-          s2.y = pack_bf16x2(sv4[2], sv4[3]);
-          l2.x = pack_bf16x2(lv4[0], lv4[1]);
-          l2.y = pack_bf16x2(lv4[2], lv4[3]);
-          *reinterpret_cast<u32x2*>(A.os + e0) = s2;
-          *reinterpret_cast<u32x2*>(A.ol + e0) = l2;
-        }
-      }
-    }
-    if (A.os != nullptr && g == 0 && qok[qt]) A.inv_den[(size_t)bh * A.T * kBlock + qrow[qt]] = inv_den;
-    if (A.lse != nullptr) {
-      // native mode scored the raw keys: log-sum-exp over K~ = K - mu is lower by q.mu/sqrt(d)
-      float shift = 0.f;
-      if constexpr (!FP8) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 wv = __builtin_bit_cast(u32x4, qo.qb[qt][s]);
-          const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-          const float* mu = A.k_mean + (size_t)bh * D + 32 * s + 8 * g;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            shift = fmaf(bf16_lo(ww[e]), mu[2 * e], shift);
-            shift = fmaf(bf16_hi(ww[e]), mu[2 * e + 1], shift);
-          }
-        }
-        shift = rows4_sum(shift) * (1.f / sqrtf((float)D));
-      }
-      if (g == 0 && qok[qt]) A.lse[(size_t)bh * A.N + qrow[qt]] = (st.m_run[qt] + log2f(l_tot)) * kLn2 - shift;
-    }
-  }
+  fwd_epilogue<FP8, QT>(A, st, qo, Hs, Hs + 64 * 256, direct, alphaS, zrS, bh, qrow, qok, l16, g, topk);
 }
 
 // ---------------------------------------------------------------------------------------
