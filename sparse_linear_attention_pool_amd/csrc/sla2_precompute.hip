@@ -386,16 +386,15 @@ __global__ __launch_bounds__(256) void precompute_f32_kernel(
 // h_sum / z_sum: sum of the chunk partials.  A workgroup owns 256 consecutive entries (64
 // quads) of one head; thread (quad q, part u) adds the partials p = u, u + 4, ... of its quad
 // with 16-byte loads, then the 4 parts are combined in fixed order.
-__global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restrict__ hpart,
-                                                          const float* __restrict__ zpart, int P, int D,
-                                                          float* __restrict__ h_sum,
-                                                          float* __restrict__ z_sum,
-                                                          uint16_t* __restrict__ hbf) {
+__device__ __forceinline__ void reduce_sums_block(int blk, int bh, const float* __restrict__ hpart,
+                                                  const float* __restrict__ zpart, int P, int D,
+                                                  float* __restrict__ h_sum, float* __restrict__ z_sum,
+                                                  uint16_t* __restrict__ hbf) {
   __shared__ f32x4 red[4][64];
-  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int q = tid & 63, u = tid >> 6;
   const int DD = D * D;
-  const int e0 = blockIdx.x * 256 + 4 * q;
+  const int e0 = blk * 256 + 4 * q;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (e0 < DD) {
 #pragma unroll 16
@@ -414,7 +413,7 @@ __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restric
       *reinterpret_cast<u32x2*>(hbf + (size_t)bh * DD + c * D + 8 * ((a >> 3) ^ (c & 15)) + (a & 7)) = w2;
     }
   }
-  if (blockIdx.x == 0) {
+  if (blk == 0) {
     // z_sum: thread (c, part v) adds partials p = v, v + 256/D, ...; parts combined in order
     __shared__ float zred[256];
     const int parts = 256 / D, c = tid % D, v = tid / D;
@@ -430,12 +429,26 @@ __global__ __launch_bounds__(256) void reduce_sums_kernel(const float* __restric
   }
 }
 
-// Z_R(i) = sum of z_j over the routed blocks j of query-block row i, in LUT order: one
-// workgroup per (row, head), thread c owns feature c.  The forward pass needs it for the
-// denominator of the linear branch over the unrouted blocks, phi(q).(Z_tot - Z_R).
-__global__ __launch_bounds__(128) void zroute_kernel(const float* __restrict__ zblk, const int32_t* __restrict__ lut,
-                                                     int T, int topk, float* __restrict__ zrout) {
-  const int i = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+// The tail of the precompute in one launch: workgroups x < nred reduce the chunk partials
+// (entries 256 x .. 256 x + 255 of head y); with zblk given, workgroups x >= nred form
+//   Z_R(i) = sum of z_j over the routed blocks j of query-block row i, in LUT order,
+// for rows i = 2 (x - nred) + tid / 128, thread c = tid % 128 owning feature c (d = 128).  The
+// forward pass needs Z_R for the denominator of the linear branch over the unrouted blocks,
+// phi(q).(Z_tot - Z_R).  The two parts are independent and run side by side.
+__global__ __launch_bounds__(256) void precompute_tail_kernel(const float* __restrict__ hpart,
+                                                              const float* __restrict__ zpart, int P, int D,
+                                                              int nred, float* __restrict__ h_sum,
+                                                              float* __restrict__ z_sum, uint16_t* __restrict__ hbf,
+                                                              const float* __restrict__ zblk,
+                                                              const int32_t* __restrict__ lut, int T, int topk,
+                                                              float* __restrict__ zrout) {
+  const int bh = blockIdx.y;
+  if ((int)blockIdx.x < nred) {
+    reduce_sums_block(blockIdx.x, bh, hpart, zpart, P, D, h_sum, z_sum, hbf);
+    return;
+  }
+  const int i = 2 * (blockIdx.x - nred) + (threadIdx.x >> 7), c = threadIdx.x & 127;
+  if (i >= T) return;
   const int32_t* row = lut + ((size_t)bh * T + i) * topk;
   float s = 0.f;
 #pragma unroll 8
@@ -475,16 +488,19 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
                        (const float*)t.v, t.k_mean, g.N, g.T, g.P, (float*)t.h, t.z, ws.hpart,
                        ws.zpart);
   }
-  hipLaunchKernelGGL(reduce_sums_kernel, dim3((g.D * g.D + 255) / 256, g.BH), dim3(256), 0, s,
-                     ws.hpart, ws.zpart, g.P, g.D, t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr);
-  if (g.bf16) hipLaunchKernelGGL(zroute_kernel, dim3(g.T, g.BH), dim3(128), 0, s, ws.zblk, t.lut, g.T, g.topk, ws.zrout);
+  const int nred = (g.D * g.D + 255) / 256;
+  const int nz = g.bf16 ? (g.T + 1) / 2 : 0;   // Z_R rows, two per workgroup (bf16 modes, d = 128)
+  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred + nz, g.BH), dim3(256), 0, s, ws.hpart, ws.zpart, g.P, g.D,
+                     nred, t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr, ws.zblk, t.lut, g.T, g.topk,
+                     ws.zrout);
   return hipGetLastError();
 }
 
 hipError_t launch_sum_parts(const float* parts, const float* zparts, int P, int D, int BH, float* out,
                             float* zout, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_sums_kernel, dim3((D * D + 255) / 256, BH), dim3(256), 0, s, parts, zparts, P, D,
-                     out, zout, (uint16_t*)nullptr);
+  const int nred = (D * D + 255) / 256;
+  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred, BH), dim3(256), 0, s, parts, zparts, P, D, nred, out, zout,
+                     (uint16_t*)nullptr, (const float*)nullptr, (const int32_t*)nullptr, 0, 0, (float*)nullptr);
   return hipGetLastError();
 }
 
