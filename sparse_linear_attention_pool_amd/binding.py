@@ -101,21 +101,70 @@ def sla2_buffer_sizes(params: Params) -> Dict[str, int]:
     return {f: int(getattr(s, f)) for f in SIZE_FIELDS}
 
 
-def _ptr(x) -> Optional[int]:
+# element type each tensor field must have: "el" is the input dtype (bf16 or fp32); None takes
+# any (byte buffers)
+_F32, _I32, _U8, _EL = "float32", "int32", "uint8", "el"
+_FIELD_DTYPE = {"q": _EL, "k": _EL, "v": _EL, "o": _EL, "h": _EL, "wq": _F32, "wk": _F32, "alpha": _F32,
+                "q_pool": _F32, "k_pool": _F32, "k_mean": _F32, "h_sum": _F32, "z_sum": _F32, "z": _F32,
+                "q_scale": _F32, "k_scale": _F32, "lse": _F32, "lut": _I32, "mask": _U8, "q8": _U8, "k8": _U8,
+                "workspace": None, "workspace_bwd": None}
+
+
+def _bytes_needed(params: Params, name: str, sizes: Optional[Dict[str, int]] = None) -> int:
+    """Bytes the library reads or writes through tensor field `name` for these params."""
+    el = 2 if params.dtype == SLA2_BF16 else 4
+    tok = params.B * params.H * params.N * params.d * el
+    if name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        return tok
+    if name in ("alpha", "dalpha"):
+        return params.H * params.d * 4
+    if name in ("wq", "wk"):
+        return params.d * params.d * 4
+    T = (params.N + 63) // 64
+    if name == "soft_mask":
+        return params.B * params.H * T * T * 4
+    if name == "lambda":
+        return params.B * params.H * T * 4
+    return (sizes if sizes is not None else sla2_buffer_sizes(params))[name]
+
+
+def _ptr(x, params: Optional[Params] = None, name: str = "", dtype: Optional[str] = None,
+         sizes: Optional[Dict[str, int]] = None) -> Optional[int]:
+    """Device address of tensor x after checking, before anything is launched, that it is a
+    contiguous device tensor of the expected element type, holds at least the bytes the library
+    touches for `params`, and starts on a 16-byte boundary (the kernels use 16-byte loads and
+    LDS copies).  None passes as NULL; a plain int passes through as a raw device address, for
+    callers that manage the memory themselves."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    what = f"tensor '{name}'" if name else "tensor"
     if not x.is_contiguous():
-        raise ValueError("SLA2 tensors must be contiguous")
+        raise ValueError(f"{what} must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a device tensor (got {x.device})")
+    if dtype is not None and params is not None:
+        want = ("bfloat16" if params.dtype == SLA2_BF16 else "float32") if dtype == _EL else dtype
+        got = str(x.dtype).replace("torch.", "")
+        if got != want:
+            raise ValueError(f"{what} must be {want} (got {got})")
+    if params is not None and name:
+        need = _bytes_needed(params, name, sizes)
+        have = x.numel() * x.element_size()
+        if have < need:
+            raise ValueError(f"{what} holds {have} bytes; these params need {need}")
+    if x.data_ptr() % 16 != 0:
+        raise ValueError(f"{what} must start on a 16-byte boundary (address {x.data_ptr():#x})")
     return x.data_ptr()
 
 
-def _tensors(t: dict) -> Tensors:
+def _tensors(t: dict, params: Optional[Params] = None) -> Tensors:
     unknown = set(t) - set(TENSOR_FIELDS)
     if unknown:
         raise KeyError(f"unknown tensor names {sorted(unknown)}")
-    return Tensors(**{f: _ptr(t.get(f)) for f in TENSOR_FIELDS})
+    sizes = sla2_buffer_sizes(params) if params is not None else None
+    return Tensors(**{f: _ptr(t.get(f), params, f, _FIELD_DTYPE.get(f), sizes) for f in TENSOR_FIELDS})
 
 
 def _stream(stream) -> Optional[int]:
@@ -126,39 +175,42 @@ def _stream(stream) -> Optional[int]:
 
 
 def sla2_route(params: Params, tensors: dict, stream=None) -> None:
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_route", lib.sla2_route(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
 
 
 def sla2_route_noalloc(params: Params, tensors: dict, stream=None) -> None:
     """sla2_route with the router's scratch in the library's device array (no workspace)."""
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_route_noalloc", lib.sla2_route_noalloc(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
 
 
 def sla2_route_soft(params: Params, tensors: dict, tau: float, soft_mask, lam, stream=None) -> None:
     """sla2_route plus the SoftTop-k mask: soft_mask float32 [B,H,T,T], lam float32 [B,H,T]."""
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_route_soft", lib.sla2_route_soft(ctypes.byref(params), ctypes.byref(tt), float(tau),
-                                                  _ptr(soft_mask), _ptr(lam), _stream(stream)))
+                                                  _ptr(soft_mask, params, "soft_mask", _F32),
+                                                  _ptr(lam, params, "lambda", _F32), _stream(stream)))
 
 
 def sla2_linear_precompute(params: Params, tensors: dict, stream=None) -> None:
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_linear_precompute",
            lib.sla2_linear_precompute(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
 
 
 def sla2_attention_fwd(params: Params, tensors: dict, stream=None) -> None:
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_attention_fwd", lib.sla2_attention_fwd(ctypes.byref(params), ctypes.byref(tt), _stream(stream)))
 
 
 def sla2_attention_bwd(params: Params, tensors: dict, dout, dq, dk, dv, dalpha, stream=None) -> None:
-    tt = _tensors(tensors)
+    tt = _tensors(tensors, params)
     _check("sla2_attention_bwd",
-           lib.sla2_attention_bwd(ctypes.byref(params), ctypes.byref(tt), _ptr(dout), _ptr(dq), _ptr(dk),
-                                  _ptr(dv), _ptr(dalpha), _stream(stream)))
+           lib.sla2_attention_bwd(ctypes.byref(params), ctypes.byref(tt), _ptr(dout, params, "dout", _EL),
+                                  _ptr(dq, params, "dq", _EL), _ptr(dk, params, "dk", _EL),
+                                  _ptr(dv, params, "dv", _EL), _ptr(dalpha, params, "dalpha", _F32),
+                                  _stream(stream)))
 
 
 def backward(params: Params, inputs: dict, buffers: dict, dout, stream=None) -> dict:

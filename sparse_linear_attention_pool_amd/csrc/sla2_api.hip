@@ -114,6 +114,42 @@ size_t workspace_layout(const Geometry& g, Workspace* ws, char* base) {
   return off;
 }
 
+// Layout of the backward pass's scratch (sla2_sizes.workspace_bwd).
+size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
+  const size_t BH = g.BH, T = g.T, D = g.D, N = g.N;
+  const size_t pg = (g.T + kGChunk - 1) / kGChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return base ? base + o : nullptr;
+  };
+  BwdWorkspace w;
+  w.os = (uint16_t*)take(BH * N * D * 2);
+  w.ol = (uint16_t*)take(BH * N * D * 2);
+  w.inv_den = (float*)take(BH * T * 64 * 4);
+  w.q8t = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.phqdt = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.k8t = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.phkt = (uint16_t*)take(BH * T * D * 64 * 2);
+  w.htimg = (uint16_t*)take(BH * D * D * 2);
+  w.qrec = (float*)take(BH * T * kRec * 4);
+  w.dden = (float*)take(BH * T * 64 * 4);
+  w.inv = (int32_t*)take(BH * T * T * 4);
+  w.inv_cnt = (int32_t*)take(BH * T * 4);
+  w.dZ = (float*)take(BH * T * D * 4);
+  w.gpart = (float*)take(BH * pg * D * D * 4);
+  w.zpart = (float*)take(BH * pg * D * 4);
+  w.g_tot = (float*)take(BH * D * D * 4);
+  w.dZ_tot = (float*)take(BH * D * 4);
+  w.dalpha_part = (float*)take(BH * T * D * 4);
+  w.dkt = (float*)take(BH * T * 64 * D * 4);
+  w.colsum_part = (float*)take(BH * T * D * 4);
+  w.dk_mean = (float*)take(BH * D * 4);
+  if (ws) *ws = w;
+  return off;
+}
+
 namespace {
 
 std::mutex g_scratch_mu;

@@ -45,8 +45,6 @@ namespace {
 constexpr int kD = 128;
 constexpr int kNT = 256;
 constexpr int kTTile = kD * kBlock * 2;   // bytes of one transposed bf16 tile: 128 rows x 64
-constexpr int kRec = 256;                 // floats per query block in the key side's record
-constexpr int kGChunk = 8;                // query blocks per partial of G_tot
 constexpr int kQReadAhead = 1;            // feature tiles whose LDS operands are read ahead (query side)
 constexpr int kKReadAhead = 2;            // the same on the key side
 
@@ -1150,41 +1148,6 @@ __global__ __launch_bounds__(1024) void bwd_dalpha_kernel(BwdArgs A) {
 }
 
 }  // namespace
-
-size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base) {
-  const size_t BH = g.BH, T = g.T, D = g.D, N = g.N;
-  const size_t pg = (g.T + kGChunk - 1) / kGChunk;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = (off + bytes + 255) & ~(size_t)255;
-    return base ? base + o : nullptr;
-  };
-  BwdWorkspace w;
-  w.os = (uint16_t*)take(BH * N * D * 2);
-  w.ol = (uint16_t*)take(BH * N * D * 2);
-  w.inv_den = (float*)take(BH * T * 64 * 4);
-  w.q8t = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.phqdt = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.k8t = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.phkt = (uint16_t*)take(BH * T * D * 64 * 2);
-  w.htimg = (uint16_t*)take(BH * D * D * 2);
-  w.qrec = (float*)take(BH * T * kRec * 4);
-  w.dden = (float*)take(BH * T * 64 * 4);
-  w.inv = (int32_t*)take(BH * T * T * 4);
-  w.inv_cnt = (int32_t*)take(BH * T * 4);
-  w.dZ = (float*)take(BH * T * D * 4);
-  w.gpart = (float*)take(BH * pg * D * D * 4);
-  w.zpart = (float*)take(BH * pg * D * 4);
-  w.g_tot = (float*)take(BH * D * D * 4);
-  w.dZ_tot = (float*)take(BH * D * 4);
-  w.dalpha_part = (float*)take(BH * T * D * 4);
-  w.dkt = (float*)take(BH * T * 64 * D * 4);
-  w.colsum_part = (float*)take(BH * T * D * 4);
-  w.dk_mean = (float*)take(BH * D * 4);
-  if (ws) *ws = w;
-  return off;
-}
 
 hipError_t launch_bwd(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const BwdWorkspace& bw,
                       const void* dout, void* dq, void* dk, void* dv, float* dalpha, hipStream_t s) {

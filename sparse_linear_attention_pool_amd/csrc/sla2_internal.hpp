@@ -72,6 +72,9 @@ struct BwdWorkspace {
   float* dk_mean;       // [BH, D]
 };
 
+// backward workspace geometry (the backward kernels and the layout below share it)
+constexpr int kRec = 256;                 // floats per query block in the key side's record
+constexpr int kGChunk = 8;                // query blocks per partial of G_tot
 size_t bwd_workspace_layout(const Geometry& g, BwdWorkspace* ws, char* base);
 
 hipError_t launch_route(const Geometry& g, const sla2_tensors& t, const Workspace& ws, hipStream_t s);

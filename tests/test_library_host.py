@@ -157,3 +157,105 @@ def test_training_forward_rejects_a_misaligned_backward_workspace(B):
     with pytest.raises(B.SLA2Error) as e:
         B.sla2_attention_fwd(p, have, stream=0)
     assert e.value.status == B.SLA2_ERR_INVALID_ARG and "workspace_bwd" in str(e.value)
+
+
+class _DeviceTensorStandIn:
+    """What the binding reads of a torch device tensor, for checking its argument validation on a
+    machine without a GPU (nothing here is ever dereferenced)."""
+
+    def __init__(self, dtype, numel, address=1 << 20):
+        self.dtype, self._numel, self._address = dtype, numel, address
+        self.is_cuda, self.device = True, "cuda:0"
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return self._numel
+
+    def element_size(self):
+        import torch
+        return torch.empty(0, dtype=self.dtype).element_size()
+
+    def data_ptr(self):
+        return self._address
+
+
+def _fwd_tensors(B, p, **override):
+    import torch
+    el = torch.bfloat16
+    tok = p.B * p.H * p.N * p.d
+    sz = B.sla2_buffer_sizes(p)
+    t = {"q": _DeviceTensorStandIn(el, tok), "k": _DeviceTensorStandIn(el, tok), "v": _DeviceTensorStandIn(el, tok),
+         "alpha": _DeviceTensorStandIn(torch.float32, p.H * p.d),
+         "lut": _DeviceTensorStandIn(torch.int32, sz["lut"] // 4),
+         "workspace": _DeviceTensorStandIn(torch.uint8, sz["workspace"])}
+    t.update(override)
+    return t
+
+
+@pytest.mark.parametrize("field,bad,msg", [
+    ("q", "float32", "must be bfloat16"),
+    ("lut", "int64", "must be int32"),
+    ("q", "short", "holds"),
+    ("workspace", "short", "holds"),
+    ("v", "misaligned", "16-byte boundary"),
+    ("k", "host", "device tensor"),
+    ("alpha", "strided", "contiguous"),
+])
+def test_binding_rejects_bad_tensors_before_any_call(B, field, bad, msg, monkeypatch):
+    """Each tensor is checked (device, element type, size for these params, 16-byte alignment,
+    contiguity) in the binding, before the library is called."""
+    import torch
+    p = B.make_params(1, 2, 1000, 128, 3, "bf16", "fp8")
+    good = _fwd_tensors(B, p)
+    x = good[field]
+    if bad == "float32":
+        bad_t = _DeviceTensorStandIn(torch.float32, x.numel())
+    elif bad == "int64":
+        bad_t = _DeviceTensorStandIn(torch.int64, x.numel())
+    elif bad == "short":
+        bad_t = _DeviceTensorStandIn(x.dtype, x.numel() - 1)
+    elif bad == "misaligned":
+        bad_t = _DeviceTensorStandIn(x.dtype, x.numel(), address=(1 << 20) + 8)
+    elif bad == "host":
+        bad_t = torch.zeros(x.numel(), dtype=x.dtype)
+    else:
+        bad_t = torch.zeros(2, p.H * p.d, dtype=torch.float32).t()
+    called = []
+    monkeypatch.setattr(B, "lib", _RecordingLib(B.lib, called))
+    with pytest.raises(ValueError, match=msg):
+        B.sla2_linear_precompute(p, dict(good, **{field: bad_t}), stream=0)
+    assert called == []
+
+
+class _RecordingLib:
+    """The library with its compute entry points recorded instead of called."""
+
+    def __init__(self, lib, called):
+        self._lib, self._called = lib, called
+
+    def __getattr__(self, name):
+        if name in ("sla2_buffer_sizes", "sla2_last_error", "sla2_status_string"):
+            return getattr(self._lib, name)
+
+        def rec(*args):
+            self._called.append(name)
+            return 0
+        return rec
+
+
+def test_a_failing_hip_call_maps_to_err_hip(B):
+    """On a machine without a GPU the no-alloc router's first HIP call (the device query, before
+    anything is launched) fails; the library returns SLA2_ERR_HIP with HIP's message, and the
+    binding raises it with that status.  (Skipped where a GPU is present: the call would run.)"""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    p = B.make_params(1, 2, 1000, 128, 3, "bf16", "fp8")
+    fake = {f: 1 << 20 for f in ("q", "k", "q_pool", "k_pool", "k_mean", "lut", "mask", "q8", "q_scale")}
+    with pytest.raises(B.SLA2Error) as e:
+        B.sla2_route_noalloc(p, fake, stream=0)
+    assert e.value.status == B.SLA2_ERR_HIP == -3
+    assert "sla2_route_noalloc" in str(e.value) and "device" in str(e.value)
+    assert B.lib.sla2_status_string(B.SLA2_ERR_HIP) == b"HIP runtime error"
