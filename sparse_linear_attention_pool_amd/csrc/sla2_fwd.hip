@@ -531,12 +531,13 @@ __device__ __forceinline__ i32x8 phi_q_codes(const float (&f)[4][8]) {
 // Epilogue of the fused forward for this wave's queries: O_s = acc / l, the linear branch
 // O_l = (phi(q) H_tot - routed part) / (phi(q).(Z_tot - Z_R) + eps) (or the unrouted part itself
 // in the direct form), O = alpha O_s + (1 - alpha) O_l, and the optional lse and backward stores.
+// alphaS holds alpha of the head and zdS = Z_tot - Z_R(i), both per feature, in LDS.
 // The bf16 LDS image of H^T has rows 0..63 at Hlo and rows 64..127 at Hhi (256-byte rows, chunk
 // k of row r at chunk k ^ (r % 16)).
 template <bool FP8, int QT>
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& A, const FwdState<QT>& st, const QueryOps<QT>& qo,
                                              const uint8_t* Hlo, const uint8_t* Hhi, bool direct,
-                                             const float* alphaS, const float* zrS, int bh, const int (&qrow)[QT],
+                                             const float* alphaS, const float* zdS, int bh, const int (&qrow)[QT],
                                              const bool (&qok)[QT], int l16, int g, int topk) {
   constexpr int D = 128;
 #pragma unroll
@@ -546,18 +547,15 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& A, const FwdState<QT
     const float inv_l = 1.f / l_tot;
     // denominator over the unrouted blocks: phi(q).(Z_tot - Z_R), with the bf16 phi(q)
     float den = 0.f;
-    {
-      const float* zt = A.z_sum + (size_t)bh * D;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 bw = __builtin_bit_cast(u32x4, qo.phb[qt][s]);
-        const uint32_t ww[4] = {bw.x, bw.y, bw.z, bw.w};
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bw = __builtin_bit_cast(u32x4, qo.phb[qt][s]);
+      const uint32_t ww[4] = {bw.x, bw.y, bw.z, bw.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int a = 32 * s + 8 * g + 2 * e;
-          den = fmaf(bf16_lo(ww[e]), zt[a] - zrS[a], den);
-          den = fmaf(bf16_hi(ww[e]), zt[a + 1] - zrS[a + 1], den);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int a = 32 * s + 8 * g + 2 * e;
+        den = fmaf(bf16_lo(ww[e]), zdS[a], den);
+        den = fmaf(bf16_hi(ww[e]), zdS[a + 1], den);
       }
     }
     // with every block routed the linear branch is an empty sum, 0 (the complement form would
@@ -708,7 +706,8 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
       qo.phb[qt][s] = __builtin_bit_cast(bf16x8, bw);
     }
   }
-  const float zr = tid < D ? A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
+  // Z_tot - Z_R(i) per feature, for the epilogue's denominator (loaded now, with the first tile)
+  const float zd = tid < D ? A.z_sum[(size_t)bh * D + tid] - A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
 
   if (tid < D) alphaS[tid] = alv;   // read in the epilogue, after several barriers
   // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
@@ -729,8 +728,8 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // The first tile and every query-operand load complete here, before the loop: a wait for a
   // first use inside the loop could not tell them from the copies in flight there.
   wait_dma();
-  __shared__ float zrS[D];
-  if (tid < D) zrS[tid] = zr;
+  __shared__ float zdS[D];
+  if (tid < D) zdS[tid] = zd;
   lds_barrier();
 
   for (int r = 0; r < topk; r += 2) {
@@ -797,7 +796,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // ---------------- epilogue ----------------
   // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
-  fwd_epilogue<FP8, QT>(A, st, qo, Hs, Hs + 64 * 256, direct, alphaS, zrS, bh, qrow, qok, l16, g, topk);
+  fwd_epilogue<FP8, QT>(A, st, qo, Hs, Hs + 64 * 256, direct, alphaS, zdS, bh, qrow, qok, l16, g, topk);
 }
 
 // ---------------------------------------------------------------------------------------

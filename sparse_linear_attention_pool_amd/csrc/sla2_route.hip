@@ -17,25 +17,13 @@ namespace sla2 {
 
 // ---------------------------------------------------------------------------------------
 // Pool: one workgroup per (block i, head).  Column sums of the block's Q and K rows in fp64
-// (exact for bf16 inputs); in FP8 mode also the block's absmax scale and the e4m3 codes of
-// Q.  Rows past N count as zero and receive code 0.
+// (exact for bf16 inputs, so their order does not matter); in FP8 mode also the block's absmax
+// scale and the e4m3 codes of Q.  Rows past N count as zero and receive code 0.
+// Thread (c = tid % CPR, r0 = tid / CPR) loads the 16-byte chunk c of rows r0 + RPP p.  Its
+// fp64 column partials go to LDS, where thread j then sums column j % D of Q (j < D) or K over
+// the row groups.  The FP8 codes re-read the block's Q rows (from L2) once the scale is known,
+// rather than holding them in registers.
 // ---------------------------------------------------------------------------------------
-// fp64 sum over the lanes l, l ^ 32 (and l ^ 16, l ^ 48 when the rows are 16 lanes wide).
-template <int ROWLANES>
-__device__ __forceinline__ double rows_sum_f64(double v) {
-  u32x2 u = __builtin_bit_cast(u32x2, v);
-  auto a = __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
-  v = __builtin_bit_cast(double, u32x2{a[0], b[0]}) + __builtin_bit_cast(double, u32x2{a[1], b[1]});
-  if constexpr (ROWLANES == 16) {
-    u = __builtin_bit_cast(u32x2, v);
-    a = __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false);
-    b = __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false);
-    v = __builtin_bit_cast(double, u32x2{a[0], b[0]}) + __builtin_bit_cast(double, u32x2{a[1], b[1]});
-  }
-  return v;
-}
-
 template <typename Tin, int D, bool FP8>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                    int N, int T, double* __restrict__ qsum,
@@ -43,76 +31,74 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
                                                    float* __restrict__ q_scale) {
   constexpr int VEC = 16 / sizeof(Tin);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;           // chunks per row
-  constexpr int RPP = 256 / CPR;         // rows per pass
+  constexpr int RPP = 256 / CPR;         // rows per pass (= row groups)
   constexpr int PASSES = kBlock / RPP;
   static_assert(!FP8 || VEC == 8, "FP8 quantisation needs bf16 input");
-  static_assert(CPR == 16 || CPR == 32, "a wave holds four rows of 16 chunks or two of 32");
-  __shared__ double red[2][4][D];   // per wave: column sums of its rows
+  static_assert(2 * D <= 256, "one thread per column of Q and of K");
+  __shared__ double part[2][RPP][D];   // column partials of each row group (32 KB at D = 128, bf16)
   __shared__ float wmax[4];
 
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int c = tid % CPR, r0 = tid / CPR;
   const size_t head = (size_t)bh * N;
 
-  float qv[PASSES][VEC];
   double qs[VEC], ks[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) qs[e] = ks[e] = 0.0;
   float amax = 0.f;
 
+  u32x4 qw[PASSES], kw[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = kBlock * i + r0 + p * RPP;
-    float kv[VEC];
-    if (row < N) {
-      const uint4 qw = *reinterpret_cast<const uint4*>(q + (head + row) * D + c * VEC);
-      const uint4 kw = *reinterpret_cast<const uint4*>(k + (head + row) * D + c * VEC);
-      if constexpr (sizeof(Tin) == 2) {
-        const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
+    const bool ok = row < N;
+    const size_t off = (head + (ok ? row : 0)) * D + c * VEC;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(q + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(k + off);
+    qw[p] = ok ? a : u32x4{0, 0, 0, 0};
+    kw[p] = ok ? b : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[p][2 * e] = bf16_lo(qa[e]);
-          qv[p][2 * e + 1] = bf16_hi(qa[e]);
-          kv[2 * e] = bf16_lo(ka[e]);
-          kv[2 * e + 1] = bf16_hi(ka[e]);
-        }
-      } else {
-        const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
+  for (int p = 0; p < PASSES; ++p) {
+    float qv[VEC], kv[VEC];
+    if constexpr (sizeof(Tin) == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[p][e] = __uint_as_float(qa[e]);
-          kv[e] = __uint_as_float(ka[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        qv[2 * e] = bf16_lo(qw[p][e]);
+        qv[2 * e + 1] = bf16_hi(qw[p][e]);
+        kv[2 * e] = bf16_lo(kw[p][e]);
+        kv[2 * e + 1] = bf16_hi(kw[p][e]);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) qv[p][e] = kv[e] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        qv[e] = __uint_as_float(qw[p][e]);
+        kv[e] = __uint_as_float(kw[p][e]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      qs[e] += (double)qv[p][e];
+      qs[e] += (double)qv[e];
       ks[e] += (double)kv[e];
-      amax = fmaxf(amax, fabsf(qv[p][e]));
+      amax = fmaxf(amax, fabsf(qv[e]));
     }
   }
 
-  // column sums: over the rows of each wave in registers, then over the four waves in LDS
-  // (sums of bf16 values in fp64 are exact, so the order does not matter for bf16 inputs)
-  const size_t out = ((size_t)bh * T + i) * D;
-  const int w = tid >> 6;
+  // column sums: each row group's partials to LDS, then one thread per (tensor, column)
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    const double qw = rows_sum_f64<CPR>(qs[e]), kw = rows_sum_f64<CPR>(ks[e]);
-    if ((tid & 63) < CPR) {
-      red[0][w][c * VEC + e] = qw;
-      red[1][w][c * VEC + e] = kw;
-    }
+    part[0][r0][c * VEC + e] = qs[e];
+    part[1][r0][c * VEC + e] = ks[e];
   }
   __syncthreads();
-  if (tid < 2 * D) {
+  {
     const int which = tid / D, col = tid % D;
-    const double sm = (red[which][0][col] + red[which][1][col]) + (red[which][2][col] + red[which][3][col]);
-    (which ? ksum : qsum)[out + col] = sm;
+    if (which < 2) {
+      double sm = 0.0;
+#pragma unroll
+      for (int rg = 0; rg < RPP; ++rg) sm += part[which][rg][col];
+      (which ? ksum : qsum)[((size_t)bh * T + i) * D + col] = sm;
+    }
   }
 
   if constexpr (FP8) {
@@ -127,13 +113,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = kBlock * i + r0 + p * RPP;
+      const bool ok = row < N;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(q + (head + (ok ? row : 0)) * D + c * VEC);
+      const u32x4 w4 = ok ? a : u32x4{0, 0, 0, 0};   // rows past N: code 0
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(div_by_scale(qv[p][e], inv_s));
-      uint2 codes;
+      for (int e = 0; e < 4; ++e) {
+        y[2 * e] = clamp_fp8(div_by_scale(bf16_lo(w4[e]), inv_s));
+        y[2 * e + 1] = clamp_fp8(div_by_scale(bf16_hi(w4[e]), inv_s));
+      }
+      u32x2 codes;
       codes.x = pack_fp8x4(y[0], y[1], y[2], y[3]);
       codes.y = pack_fp8x4(y[4], y[5], y[6], y[7]);
-      *reinterpret_cast<uint2*>(q8 + ((size_t)bh * T * kBlock + row) * D + c * 8) = codes;
+      *reinterpret_cast<u32x2*>(q8 + ((size_t)bh * T * kBlock + row) * D + c * 8) = codes;
     }
   }
 }
