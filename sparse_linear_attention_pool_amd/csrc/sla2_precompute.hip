@@ -27,7 +27,7 @@ namespace sla2 {
 // Thread (c = tid % 16, r0 = tid / 16) holds columns 8c..8c+7 of rows r0 + 16p, p = 0..3
 // (a 16-lane row of a wave holds one token); the next block's K and V are loaded while the
 // current one is processed.
-// phi and V go to LDS row-major (row stride 68 words); the operands whose contraction index
+// phi and V go to LDS token-major (256-byte rows, rswz layout); the operands whose contraction index
 // runs down those rows (tokens) are read with the transposing LDS reads.  Wave w computes the
 // 4 x 4 tiles (a-tiles 4*(w/2).., c-tiles 4*(w%2)..) of D[a][c] = sum_t phi[t][a] V[t][c] with
 // v_mfma_f32_16x16x32_bf16 over 64 tokens.  phi is
@@ -35,8 +35,8 @@ namespace sla2 {
 // 2^-16 relative although the matrix cores take bf16; V is bf16 already.
 // ---------------------------------------------------------------------------------------
 // the 8-element operand of rows r0 .. r0 + 7 at column c0 + j (two transposing reads)
-__device__ __forceinline__ bf16x8 lds_op_tr16(const uint16_t* x, int ld, int r0, int c0, int i) {
-  const u32x2 a = lds_read_tr16(x, ld, r0, c0, i), b = lds_read_tr16(x, ld, r0 + 4, c0, i);
+__device__ __forceinline__ bf16x8 lds_op_tr16(const uint8_t* x, int r0, int c0, int i) {
+  const u32x2 a = lds_read_tr16_rswz(x, r0, c0, i), b = lds_read_tr16_rswz(x, r0 + 4, c0, i);
   return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
@@ -58,19 +58,16 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
     float* __restrict__ zpart, uint16_t* __restrict__ vt, uint8_t* __restrict__ phik8, float* __restrict__ zblk,
     uint8_t* __restrict__ vexp) {
   constexpr int D = 128;
-  constexpr int SW = 68;  // LDS row stride in 32-bit words (8-byte aligned rows for the transposing reads)
-  __shared__ uint32_t phiS[64 * SW];
-  __shared__ uint32_t phiLoS[64 * SW];
-  __shared__ uint32_t vS[64 * SW];
+  // token-major tiles of 256-byte rows in the rswz layout (sla2_lds.hpp): phi hi, phi lo, V
+  __shared__ __attribute__((aligned(16))) uint8_t phiS[64 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t phiLoS[64 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t vS[64 * 256];
   __shared__ float zred[16 * D];
   __shared__ float wred[4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int c = tid & 15, r0 = tid >> 4;
-  const uint16_t* phi16 = reinterpret_cast<const uint16_t*>(phiS);
-  const uint16_t* philo16 = reinterpret_cast<const uint16_t*>(phiLoS);
-  const uint16_t* v16 = reinterpret_cast<const uint16_t*>(vS);
 
   float mu[8];
   {
@@ -143,15 +140,9 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         pl[e] = pack_bf16x2(a0 - bf16_lo(pw[e]), a1 - bf16_hi(pw[e]));
       }
       const int r = r0 + 16 * p;
-      uint32_t* pd = phiS + r * SW + 4 * c;
-      uint32_t* pld = phiLoS + r * SW + 4 * c;
-      uint32_t* vd = vS + r * SW + 4 * c;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pd[e] = pw[e];
-        pld[e] = pl[e];
-        vd[e] = vw[p][e];
-      }
+      *reinterpret_cast<u32x4*>(rswz_chunk(phiS, r, c)) = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      *reinterpret_cast<u32x4*>(rswz_chunk(phiLoS, r, c)) = u32x4{pl[0], pl[1], pl[2], pl[3]};
+      *reinterpret_cast<u32x4*>(rswz_chunk(vS, r, c)) = vw[p];
     });
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
@@ -185,9 +176,11 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       static_for<4>([&](auto p) {
         const int r = r0 + 16 * p;
         float y[8];
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(rswz_chunk(phiS, r, c));
+        const u32x4 lv = *reinterpret_cast<const u32x4*>(rswz_chunk(phiLoS, r, c));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t hw = phiS[r * SW + 4 * c + e], lw = phiLoS[r * SW + 4 * c + e];
+          const uint32_t hw = hv[e], lw = lv[e];
           y[2 * e] = clamp_fp8((bf16_lo(hw) + bf16_lo(lw)) * kPhiCodeScale);
           y[2 * e + 1] = clamp_fp8((bf16_hi(hw) + bf16_hi(lw)) * kPhiCodeScale);
         }
@@ -221,11 +214,11 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       const int t0 = 32 * ks + 8 * g;
       bf16x8 Bv[4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) Bv[ni] = lds_op_tr16(v16, 2 * SW, t0, 16 * (nbase + ni), l16);
+      for (int ni = 0; ni < 4; ++ni) Bv[ni] = lds_op_tr16(vS, t0, 16 * (nbase + ni), l16);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const bf16x8 Ah = lds_op_tr16(phi16, 2 * SW, t0, 16 * (mbase + mi), l16);
-        const bf16x8 Al = lds_op_tr16(philo16, 2 * SW, t0, 16 * (mbase + mi), l16);
+        const bf16x8 Ah = lds_op_tr16(phiS, t0, 16 * (mbase + mi), l16);
+        const bf16x8 Al = lds_op_tr16(phiLoS, t0, 16 * (mbase + mi), l16);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           f32x4& dst = STORE ? acc[mi][ni] : hs[mi][ni];
@@ -263,7 +256,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         const int ct = 4 * pp + w, ch = 16 * ct + l16;
         float x[16];
         static_for<4>([&](auto mt) {
-          const u32x2 r4 = lds_read_tr16(v16, 2 * SW, 16 * mt + 4 * g, 16 * ct, l16);
+          const u32x2 r4 = lds_read_tr16_rswz(vS, 16 * mt + 4 * g, 16 * ct, l16);
           x[4 * mt + 0] = bf16_lo(r4.x);
           x[4 * mt + 1] = bf16_hi(r4.x);
           x[4 * mt + 2] = bf16_lo(r4.y);
@@ -289,8 +282,8 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
       static_for<4>([&](auto pp) {
         const int ct = 2 * pp + (w >> 1), s = w & 1, gg = g;
-        const u32x2 lo4 = lds_read_tr16(v16, 2 * SW, 32 * s + 4 * gg, 16 * ct, l16);
-        const u32x2 hi4 = lds_read_tr16(v16, 2 * SW, 32 * s + 16 + 4 * gg, 16 * ct, l16);
+        const u32x2 lo4 = lds_read_tr16_rswz(vS, 32 * s + 4 * gg, 16 * ct, l16);
+        const u32x2 hi4 = lds_read_tr16_rswz(vS, 32 * s + 16 + 4 * gg, 16 * ct, l16);
         *reinterpret_cast<u32x4*>(vtj + (size_t)(16 * ct + l16) * kBlock + 32 * s + 8 * gg) =
             u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
       });

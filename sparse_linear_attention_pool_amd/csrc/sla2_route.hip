@@ -84,11 +84,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // column sums: each row group's partials to LDS, then one thread per (tensor, column)
+  // column sums: each row group's partials to LDS, then one thread per (tensor, column).
+  // Column x of a row group sits at slot pslot(x): its 16-byte pair index XORed with bits 4-5
+  // of itself, so that the 16 lanes of a row group writing their 64-byte runs, and 32 lanes
+  // reading consecutive columns, each hit distinct banks.
+  auto pslot = [](int x) { const int pr = x >> 1; return 2 * (pr ^ ((pr >> 4) & 3)) + (x & 1); };
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    part[0][r0][c * VEC + e] = qs[e];
-    part[1][r0][c * VEC + e] = ks[e];
+    part[0][r0][pslot(c * VEC + e)] = qs[e];
+    part[1][r0][pslot(c * VEC + e)] = ks[e];
   }
   __syncthreads();
   {
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
     if (which < 2) {
       double sm = 0.0;
 #pragma unroll
-      for (int rg = 0; rg < RPP; ++rg) sm += part[which][rg][col];
+      for (int rg = 0; rg < RPP; ++rg) sm += part[which][rg][pslot(col)];
       (which ? ksum : qsum)[((size_t)bh * T + i) * D + col] = sm;
     }
   }
