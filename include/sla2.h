@@ -139,12 +139,12 @@ int sla2_route(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* sla2_route for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  Same arguments, results and errors as
- * sla2_route, except that the router's scratch (fp64 block sums, key-mean partials and the
- * projected pooled rows: about 32 * d bytes per query block of every head) comes from a 32 MiB
- * device array the library holds on each GPU it runs on until the process ends, not from
- * t->workspace, which is not read and may be NULL.  Sizes needing more return
- * SLA2_ERR_UNSUPPORTED before anything is launched (d = 128: B*H*ceil(N/64) up to about 8100
- * query blocks; the 12-head, 32760-token layer needs 6144).  Allocates nothing; the first call
+ * sla2_route, except that the router's scratch (fp64 block sums, key-mean partials, the
+ * projected pooled rows and the block scores: 32 * d + 8 * ceil(N/64) bytes per query block of
+ * every head) comes from a 64 MiB device array the library holds on each GPU it runs on until
+ * the process ends, not from t->workspace, which is not read and may be NULL.  Sizes needing
+ * more return SLA2_ERR_UNSUPPORTED before anything is launched (the 12-head, 32760-token layer
+ * at d = 128 needs 50 MB).  Allocates nothing; the first call
  * on a device looks up that device's copy of the array.  Every call on a GPU shares its copy,
  * so calls that overlap on one GPU (on other streams or threads) race; each call overwrites
  * everything of it that it reads, so nothing needs clearing between calls. */

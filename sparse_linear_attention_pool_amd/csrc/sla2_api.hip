@@ -9,11 +9,11 @@
 
 #include "sla2_internal.hpp"
 
-// Scratch of sla2_route_noalloc: the router's fp64 block sums, key-mean partials and projected
-// pooled rows, for callers that cannot allocate device memory.  Each GPU the library runs on
+// Scratch of sla2_route_noalloc: the router's fp64 block sums, key-mean partials, projected
+// pooled rows and score keys, for callers that cannot allocate device memory.  Each GPU the library runs on
 // holds its own copy until the process ends.  Host code never passes this name to a kernel (it
 // is a host-side stand-in there): it looks up the device address once per device and uses that.
-constexpr size_t kRouteScratchBytes = (size_t)32 << 20;
+constexpr size_t kRouteScratchBytes = (size_t)64 << 20;
 static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
 
 namespace sla2 {
@@ -73,7 +73,7 @@ int check_params(const sla2_params* p, Geometry* g) {
 
 }  // namespace
 
-// The router's part of the workspace (the first five regions of workspace_layout), used by
+// The router's part of the workspace (the first six regions of workspace_layout), used by
 // sla2_route and sla2_route_soft only.  Returns its size in bytes.
 size_t route_layout(const Geometry& g, Workspace* ws, char* base) {
   const size_t BH = g.BH, T = g.T, D = g.D, P32 = (g.T + 31) / 32;
@@ -89,6 +89,7 @@ size_t route_layout(const Geometry& g, Workspace* ws, char* base) {
   w.mu = (double*)take((BH * P32 * D + BH * D) * sizeof(double));
   w.qhat = (double*)take(BH * T * D * sizeof(double));
   w.khatT = (double*)take(BH * D * T * sizeof(double));
+  w.keys = (uint64_t*)take(BH * T * T * sizeof(uint64_t));
   if (ws) *ws = w;
   return off;
 }
@@ -264,7 +265,7 @@ int sla2_route_noalloc(const sla2_params* p, const sla2_tensors* t, void* stream
   if (need > kRouteScratchBytes)
     return fail(SLA2_ERR_UNSUPPORTED,
                 "%s: these sizes need %zu bytes of router scratch, more than the %zu this entry point holds "
-                "(about 32 * d bytes per query block of every head); use sla2_route with a workspace",
+                "(32 * d + 8 * ceil(N / 64) bytes per query block of every head); use sla2_route with a workspace",
                 fn, need, kRouteScratchBytes);
   REQUIRE(t->q, "q");
   REQUIRE(t->k, "k");

@@ -28,6 +28,7 @@ struct Workspace {
   double* mu;      // [BH, D]     token mean of K (fp64)
   double* qhat;    // [BH, T, D]  projected pooled Q
   double* khatT;   // [BH, D, T]  projected pooled K~, transposed
+  uint64_t* keys;  // [BH, T, T]  block scores as order-preserving 64-bit keys
   float* hpart;    // [BH, P, D, D] chunk partials of h_sum (transposed like h)
   float* zpart;    // [BH, P, D]
   uint16_t* vt;    // bf16 modes: [BH, T, D, 64] V of each key block, transposed, keys permuted;

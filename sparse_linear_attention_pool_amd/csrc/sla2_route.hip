@@ -151,28 +151,65 @@ __global__ __launch_bounds__(D) void kpart_kernel(const double* __restrict__ ksu
 // Project: one workgroup per (16 blocks, head, Q or K), 256 threads.
 // mu = (sum of all K) / N; q_bar = block mean of Q; k_bar = block mean of K - mu;
 // q_hat = q_bar W_q, k_hat = k_bar W_k in fp64 (W NULL = identity) on the fp64 matrix cores.
-// Wave w computes the 16 x 16 output tiles of columns 16 ct .. 16 ct + 15, ct = w, w + 4, ...
+// Wave w computes the 16 x 16 output tiles of columns 16 ct .. 16 ct + 15, ct = w + 4 t; at
+// d = 128 its two tiles run as two interleaved multiply chains.  Step s of lane group lk
+// takes input channel (d/4) lk + s, so a lane's W operand is a run of consecutive rows of W.
 // For K the transposed tile k_hat^T = W_k^T k_bar^T is formed (the same two operands in
 // swapped roles), so both outputs are stored in 128-byte rows.
+// Every load is issued before the arithmetic that waits on it: the block sums, the W operand
+// and (for K) the 32-block partials of the token sum, which are then added in increasing
+// order.  Three workgroups fit on a CU, so the whole grid of a 12-head layer is resident.
 // ---------------------------------------------------------------------------------------
 constexpr int kProjRows = 16;
 
+// A W element widened to fp64 where it is used: the empty asm keeps the compiler from
+// widening all of them as soon as they load (twice the registers, which then spill).
+__device__ __forceinline__ double w_at_use(float x) {
+  asm volatile("" : "+v"(x));
+  return (double)x;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void project_kernel(
+__global__ __launch_bounds__(256, 3) void project_kernel(
     const double* __restrict__ qsum, const double* __restrict__ ksum, const double* __restrict__ kpart,
     int N, int T, int smooth_k, const float* __restrict__ wq, const float* __restrict__ wk,
     float* __restrict__ q_pool, float* __restrict__ k_pool, float* __restrict__ k_mean,
     double* __restrict__ mu_out, double* __restrict__ qhat, double* __restrict__ khatT) {
   constexpr int R = kProjRows;
-  constexpr int KS = D / 4;   // matrix-core steps over the input channel
+  constexpr int KS = D / 4;          // matrix-core steps over the input channel
+  constexpr int CT = D / 64;         // output tiles per wave
+  constexpr int EPT = R * D / 256;   // pooled elements per thread
+  constexpr int PB = 16;             // token-sum partials loaded per batch
   __shared__ double mu_s[D];
   __shared__ double rows[R][D + 1];
   const int bh = blockIdx.y, i0 = blockIdx.x * R, which = blockIdx.z, tid = threadIdx.x;
   const int P32 = (T + 31) / 32;
+  const double* __restrict__ sums = which ? ksum : qsum;
+  const float* W = which ? wk : wq;
+  const int w = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
 
+  // block sums of this workgroup's rows: element x = tid + 256 e is row x / D, channel x % D
+  double bs[EPT];
+  static_for<EPT>([&](auto e) {
+    const int x = tid + 256 * e, i = min(i0 + x / D, T - 1);
+    bs[e] = sums[((size_t)bh * T + i) * D + x % D];
+  });
+  // W operand of both tiles: W[KS lk + s][16 ct + li]
+  float wf[CT][KS];
+  if (W != nullptr) {
+    static_for<CT>([&](auto t) {
+      static_for<KS>([&](auto s) { wf[t][s] = W[(KS * lk + s) * D + 16 * (w + 4 * t) + li]; });
+    });
+  }
   if (which == 1 && tid < D) {
     double sm = 0.0;
-    for (int p = 0; p < P32; ++p) sm += kpart[((size_t)bh * P32 + p) * D + tid];
+    for (int p0 = 0; p0 < P32; p0 += PB) {
+      double v[PB];
+      static_for<PB>([&](auto u) { v[u] = kpart[((size_t)bh * P32 + min(p0 + (int)u, P32 - 1)) * D + tid]; });
+      static_for<PB>([&](auto u) {
+        if (p0 + (int)u < P32) sm += v[u];
+      });
+    }
     const double m = smooth_k ? sm / (double)N : 0.0;
     mu_s[tid] = m;
     if (blockIdx.x == 0) {
@@ -181,26 +218,27 @@ __global__ __launch_bounds__(256) void project_kernel(
     }
   }
   __syncthreads();
-  for (int x = tid; x < R * D; x += 256) {
-    const int r = x / D, c = x % D, i = i0 + r;
+  static_assert(256 % D == 0, "every element of a thread is in channel tid % D");
+  const int c = tid % D;
+  const double muc = which ? mu_s[c] : 0.0;
+  static_for<EPT>([&](auto e) {
+    const int r = (tid + 256 * e) / D, i = i0 + r;
     double v = 0.0;
     if (i < T) {
       const int n = min(kBlock, N - kBlock * i);
       const size_t idx = ((size_t)bh * T + i) * D + c;
       if (which == 0) {
-        v = qsum[idx] / (double)n;
+        v = bs[e] / (double)n;
         q_pool[idx] = (float)v;
       } else {
-        v = ksum[idx] / (double)n - mu_s[c];
+        v = bs[e] / (double)n - muc;
         k_pool[idx] = (float)v;
       }
     }
     rows[r][c] = v;
-  }
+  });
   __syncthreads();
 
-  const float* W = which ? wk : wq;
-  const int w = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
   if (W == nullptr) {
     for (int x = tid; x < R * D; x += 256) {
       if (which == 0) {
@@ -213,25 +251,33 @@ __global__ __launch_bounds__(256) void project_kernel(
     }
     return;
   }
-  double xa[KS];   // pooled row li, input channels 4s + lk
-  static_for<KS>([&](auto s) { xa[s] = rows[li][4 * s + lk]; });
-  for (int ct = w; ct < D / 16; ct += 4) {
-    double wb[KS];   // W[4s + lk][16 ct + li]
-    static_for<KS>([&](auto s) { wb[s] = (double)W[(4 * s + lk) * D + 16 * ct + li]; });
-    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-    if (which == 0) {
-      static_for<KS>([&](auto s) { acc = mfma_f64(xa[s], wb[s], acc); });
-      // acc[r] = q_hat[i0 + 4 r + lk][16 ct + li]
+  // the pooled-row operand (row li, input channel KS lk + s) is read from LDS at each step
+  f64x4 acc[CT];
+  static_for<CT>([&](auto t) { acc[t] = f64x4{0.0, 0.0, 0.0, 0.0}; });
+  if (which == 0) {
+    static_for<KS>([&](auto s) {
+      const double xa = rows[li][KS * lk + s];
+      static_for<CT>([&](auto t) { acc[t] = mfma_f64(xa, w_at_use(wf[t][s]), acc[t]); });
+    });
+    // acc[t][r] = q_hat[i0 + 4 r + lk][16 ct + li]
+    static_for<CT>([&](auto t) {
       static_for<4>([&](auto r) {
         const int i = i0 + 4 * r + lk;
-        if (i < T) qhat[((size_t)bh * T + i) * D + 16 * ct + li] = acc[int(r)];
+        if (i < T) qhat[((size_t)bh * T + i) * D + 16 * (w + 4 * t) + li] = acc[t][int(r)];
       });
-    } else {
-      static_for<KS>([&](auto s) { acc = mfma_f64(wb[s], xa[s], acc); });
-      // acc[r] = k_hat[i0 + li][16 ct + 4 r + lk]
-      if (i0 + li < T) {
-        static_for<4>([&](auto r) { khatT[((size_t)bh * D + 16 * ct + 4 * r + lk) * T + i0 + li] = acc[int(r)]; });
-      }
+    });
+  } else {
+    static_for<KS>([&](auto s) {
+      const double xa = rows[li][KS * lk + s];
+      static_for<CT>([&](auto t) { acc[t] = mfma_f64(w_at_use(wf[t][s]), xa, acc[t]); });
+    });
+    // acc[t][r] = k_hat[i0 + li][16 ct + 4 r + lk]
+    if (i0 + li < T) {
+      static_for<CT>([&](auto t) {
+        static_for<4>([&](auto r) {
+          khatT[((size_t)bh * D + 16 * (w + 4 * t) + 4 * r + lk) * T + i0 + li] = acc[t][int(r)];
+        });
+      });
     }
   }
 }
@@ -372,23 +418,33 @@ __device__ __forceinline__ void soft_row(double (&p)[MAXS], int T, int topk, dou
 }
 
 // ---------------------------------------------------------------------------------------
-// Scores + Top-k: one workgroup per (R query blocks, head), 256 threads.
+// Scores, then Top-k, in two kernels.
 //
-// Phase 1: scores q_hat k_hat^T / sqrt(d) in fp64 on the matrix cores.  The A operand is the
-// 16 x D tile of q_hat rows (rows past R repeat earlier rows and are discarded); wave w takes
-// the 16-key tiles tt = w, w + 4, ..., loading the k_hat operand one half tile (D/2 channels)
-// ahead of the multiplies.  The scores are stored in LDS as order-preserving 64-bit keys.
+// Scores: one workgroup per (32 query blocks, 128 key blocks, head), 256 threads; a 12-head
+// layer of 512 blocks gives 768 workgroups, three per CU.  The scores q_hat k_hat^T / sqrt(d)
+// are formed in fp64 on the matrix cores: the A operands are the two 16 x D tiles of q_hat
+// rows, staged in LDS (rows past T repeat row T - 1 and are not stored); wave w takes key
+// tiles w and w + 4 of the workgroup's 8, and each quarter tile of the k_hat operand, loaded two
+// quarters ahead, serves both row tiles, which halves the k_hat reads of 16-row workgroups.
+// Each score goes to the workspace as an order-preserving 64-bit key.
 //
-// Phase 2: one wave per row.  The topk-th largest key is found by a bitwise binary search:
+// Top-k: one wave per row (four rows per workgroup), holding the row's keys in registers (key j
+// in slot j / 64 of lane j % 64).  The topk-th largest key is found by a bitwise binary search:
 // bit by bit from the top, a candidate threshold is kept when at least topk keys reach it
 // (counted with ballots); the search stops as soon as exactly topk keys reach the threshold.
 // The high 32 bits are searched first; the low 32 bits only when the high halves tie.
 // Keys equal to the final threshold are taken in increasing j until topk are chosen, which
 // gives the lower block index on ties.  The mask row and the ascending LUT row follow by
 // ballot compaction.
-//
-// Phase 3 (SOFT, for sla2_route_soft): one wave per row, the SoftTop-k mask and lambda of the
-// row (soft_row above) from the same fp64 scores, read back from LDS.
+// For topk <= 64 the search over all keys is narrowed first (prune_rows below): the maxima
+// of topk lanes are topk distinct keys, so the largest t (in steps of 2^16) that topk lane
+// maxima reach is a lower bound lb of the threshold.  The keys reaching lb are the only
+// candidates; when there are at most 64 they are compacted to one per lane (through LDS) and
+// the threshold is searched among them, one comparison per step instead of one per slot.
+// Every search starts below the common leading bits of its lower and upper bound, which the
+// threshold shares.  The result is the same threshold, so the same selection.
+// With SOFT (sla2_route_soft) the wave then forms the row's SoftTop-k mask and lambda
+// (soft_row above) from the same fp64 scores.
 // ---------------------------------------------------------------------------------------
 
 // Order-preserving map of a double to an unsigned key (-0.0 is taken as +0.0).
@@ -408,218 +464,328 @@ __device__ __forceinline__ double key_score(uint64_t key) {
   return __longlong_as_double((long long)u);
 }
 
-// NW waves per workgroup: 4, or 8 where the keys of one workgroup fill most of the LDS (so
-// that the CU still runs two waves per SIMD).
-template <int R, int MAXS, int D, bool SOFT, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void topk_kernel(const double* __restrict__ qhat,
-                                                      const double* __restrict__ khatT, int T, int topk,
-                                                      double inv_sqrt_d, int32_t* __restrict__ lut,
-                                                      uint8_t* __restrict__ mask, double tau,
-                                                      float* __restrict__ soft_mask, float* __restrict__ lambda) {
-  constexpr int KS = D / 4;    // matrix-core steps over the channels
-  constexpr int HS = KS / 2;   // steps per half tile
-  extern __shared__ uint64_t keys_s[];   // [R][T]
-  // consecutive row blocks of a head run on one XCD, which then holds that head's k_hat in L2
-  const int nrb = gridDim.x;
-  const int lid = xcd_remap(blockIdx.x + nrb * blockIdx.y, nrb * gridDim.y);
-  const int bh = lid / nrb, i0 = (lid % nrb) * R, tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  {
-    const int li = lane & 15, lk = lane >> 4;
-    const int arow = min(i0 + li % R, T - 1);
-    const double* qrow = qhat + ((size_t)bh * T + arow) * D + lk;
-    double qa[KS];
-    static_for<KS>([&](auto s) { qa[s] = qrow[4 * s]; });
-    const double* kb = khatT + ((size_t)bh * D + lk) * T;
-    const int ntiles = (T + 15) >> 4;
-    // half tiles: the k_hat operand of steps half*HS .. half*HS + HS - 1 of key tile tt
-    double kv[2][HS];
-    auto load_half = [&](double(&dst)[HS], int tt, int half) {
-      const int j = min(16 * tt + li, T - 1);
-      static_for<HS>([&](auto s) { dst[s] = kb[(size_t)(4 * (half * HS + s)) * T + j]; });
-    };
-    if (w < ntiles) load_half(kv[0], w, 0);
-    for (int tt = w; tt < ntiles; tt += NW) {
-      load_half(kv[1], tt, 1);
-      // two accumulators (even / odd steps) keep two independent chains in flight
-      f64x4 acc0 = f64x4{0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
-      static_for<HS / 2>([&](auto s) {
-        acc0 = mfma_f64(qa[2 * s], kv[0][2 * s], acc0);
-        acc1 = mfma_f64(qa[2 * s + 1], kv[0][2 * s + 1], acc1);
-      });
-      if (tt + NW < ntiles) load_half(kv[0], tt + NW, 0);
-      static_for<HS / 2>([&](auto s) {
-        acc0 = mfma_f64(qa[HS + 2 * s], kv[1][2 * s], acc0);
-        acc1 = mfma_f64(qa[HS + 2 * s + 1], kv[1][2 * s + 1], acc1);
-      });
-      const f64x4 acc = acc0 + acc1;
-      const int j = 16 * tt + li;
-      static_for<4>([&](auto r) {
-        const int row = 4 * r + lk;   // accumulator r holds tile row 4r + lane/16
-        if (row < R && j < T) keys_s[row * T + j] = score_key(acc[int(r)] * inv_sqrt_d);
-      });
-    }
-  }
-  __syncthreads();
+// Max / min of a 32-bit unsigned value over the wave, in a scalar register.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, dpp_u32<0x128>(v));   // row_ror:8
+  v = op(v, dpp_u32<0x124>(v));   // row_ror:4
+  v = op(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __builtin_amdgcn_readfirstlane(op(q[0], q[1]));
+}
 
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
+// Highest set bit of x (-1 for 0), and x with its bits p .. 0 cleared (none for p < 0).
+__device__ __forceinline__ int high_bit(uint32_t x) { return 31 - __clz((int)x); }
+__device__ __forceinline__ uint32_t keep_above(uint32_t x, int p) {
+  return p < 0 ? x : (p >= 31 ? 0u : x & (~0u << (p + 1)));
+}
 
-  // Finish row r from the threshold found on the high halves: search the low halves when the
-  // high halves tie at the boundary, then emit the LUT and mask rows.
-  auto finish_row = [&](int r, uint32_t thr_hi, bool exact) {
-    uint64_t key[MAXS];
-    static_for<MAXS>([&](auto s) {
-      const int j = 64 * s + lane;
-      key[s] = j < T ? keys_s[r * T + j] : 0ull;   // 0 is below every score key
+// Narrows the search of J rows (high halves hi of the keys, MAXS slots per lane), using 64
+// words of LDS per row at cscr.  On return a row is either resolved (done: thr is its
+// threshold, exact when exactly topk keys reach it) or left to the search over all keys from
+// bit top with thr holding the bits above.
+template <int J, int MAXS>
+__device__ __forceinline__ void prune_rows(const uint32_t (&hi)[J][MAXS], uint32_t (&thr)[J], int (&top)[J],
+                                           bool (&done)[J], bool (&exact)[J], int topk, uint32_t* cscr,
+                                           int lane, uint64_t lt_mask) {
+  // lower bound: the largest t (high 16 bits) reached by the maxima of at least topk lanes,
+  // searched from below the leading bits shared by the smallest and largest lane maximum
+  uint32_t m16[J], mx[J], t1[J];
+  int p1[J];
+  bool stop[J];
+  int pmax = -1;
+  static_for<J>([&](auto jj) {
+    uint32_t m = hi[jj][0];
+    static_for<MAXS - 1>([&](auto s) { m = m > hi[jj][s + 1] ? m : hi[jj][s + 1]; });
+    m16[jj] = m >> 16;
+    mx[jj] = wave_ext_u32<true>(m);
+    const uint32_t mn16 = wave_ext_u32<false>(m16[jj]);
+    p1[jj] = high_bit(mn16 ^ (mx[jj] >> 16));
+    t1[jj] = keep_above(mn16, p1[jj]);   // every lane maximum reaches it
+    stop[jj] = done[jj];
+    pmax = max(pmax, p1[jj]);
+  });
+  for (int bit = pmax; bit >= 0; --bit) {
+    bool all = true;
+    static_for<J>([&](auto jj) {
+      const uint32_t cand = t1[jj] | (1u << bit);
+      const int cnt = ballot_count(m16[jj] >= cand);
+      const bool take = !stop[jj] && bit <= p1[jj] && cnt >= topk;
+      t1[jj] = take ? cand : t1[jj];
+      stop[jj] = stop[jj] || (take && cnt == topk);
+      all = all && stop[jj];
     });
-    uint64_t thr = (uint64_t)thr_hi << 32;
-    if (!exact) {
-      // low 32 bits among the keys whose high half equals thr_hi; keys above it count as base
-      int base_cnt = 0;
-      uint32_t lo[MAXS];
-      static_for<MAXS>([&](auto s) {
-        const uint32_t hs = (uint32_t)(key[s] >> 32);
-        base_cnt += ballot_count(hs > thr_hi);
-        lo[s] = hs == thr_hi ? (uint32_t)key[s] : 0u;   // 0 never reaches a candidate
-      });
-      uint32_t thr_lo = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr_lo | (1u << bit);
-        uint64_t bl[MAXS];
-        static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(lo[s] >= cand); });
-        int cnt = base_cnt;
-        static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
-        if (cnt >= topk) {
-          thr_lo = cand;
-          if (cnt == topk) break;
-        }
-      }
-      thr |= thr_lo;
-    }
-    // keys above thr are all taken; keys equal to thr fill the rest in increasing j
-    int need = topk;
-    static_for<MAXS>([&](auto s) { need -= ballot_count(key[s] > thr); });
-    const size_t row = (size_t)bh * T + i0 + r;
+    if (all) break;
+  }
+  // the keys reaching lb, compacted in order of slot and lane (the first 64 of them)
+  uint32_t lb[J], cv[J];
+  int cnum[J];
+  static_for<J>([&](auto jj) {
+    lb[jj] = t1[jj] << 16;
     int base = 0;
     static_for<MAXS>([&](auto s) {
-      const int j = 64 * s + lane;
-      const uint64_t eq = __builtin_amdgcn_ballot_w64(key[s] == thr);
-      const int n_eq = __popcll(eq);
-      const int take = n_eq < need ? n_eq : need;
-      const bool on = key[s] > thr || (key[s] == thr && __popcll(eq & lt_mask) < take);
-      need -= take;
-      const uint64_t bmask = __builtin_amdgcn_ballot_w64(on);
-      if (on) lut[row * topk + base + __popcll(bmask & lt_mask)] = j;
-      base += __popcll(bmask);
-      if (j < T) mask[row * T + j] = on ? 1 : 0;
+      const bool on = hi[jj][s] >= lb[jj];
+      const uint64_t b = __builtin_amdgcn_ballot_w64(on);
+      const int pos = base + __popcll(b & lt_mask);
+      if (on && pos < 64) cscr[jj * 64 + pos] = hi[jj][s];
+      base += __popcll(b);
     });
-  };
-
-  // J rows of a wave are searched together, so that their independent steps overlap.
-  constexpr int J = (MAXS <= 8) ? R / NW : 1;
-  static_assert(J >= 1, "at least one row per wave");
-  for (int r0 = w * J; r0 < R; r0 += NW * J) {
-    uint32_t hi[J][MAXS];
-    uint32_t thr[J];
-    bool done[J];
+    cnum[jj] = base;
+  });
+  static_for<J>([&](auto jj) { cv[jj] = lane < cnum[jj] ? cscr[jj * 64 + lane] : 0u; });
+  // threshold among the candidates, searched from below the leading bits of lb and the row max
+  uint32_t th[J];
+  int p2[J];
+  bool ex[J], fin[J];
+  pmax = -1;
+  static_for<J>([&](auto jj) {
+    p2[jj] = high_bit(lb[jj] ^ mx[jj]);
+    th[jj] = keep_above(lb[jj], p2[jj]);
+    ex[jj] = cnum[jj] == topk;
+    fin[jj] = done[jj] || ex[jj] || cnum[jj] > 64;
+    if (!fin[jj]) pmax = max(pmax, p2[jj]);
+  });
+  for (int bit = pmax; bit >= 0; --bit) {
+    bool all = true;
     static_for<J>([&](auto jj) {
-      const int r = r0 + jj;
-      static_for<MAXS>([&](auto s) {
-        const int j = 64 * s + lane;
-        hi[jj][s] = (j < T && i0 + r < T) ? (uint32_t)(keys_s[r * T + j] >> 32) : 0u;
-      });
-      thr[jj] = 0;
-      done[jj] = i0 + r >= T;   // rows past T are skipped
+      const uint32_t cand = th[jj] | (1u << bit);
+      const int cnt = ballot_count(cv[jj] >= cand);
+      const bool take = !fin[jj] && bit <= p2[jj] && cnt >= topk;
+      th[jj] = take ? cand : th[jj];
+      const bool hit = take && cnt == topk;
+      ex[jj] = ex[jj] || hit;
+      fin[jj] = fin[jj] || hit;
+      all = all && fin[jj];
     });
-    // Largest high-half threshold reached by at least topk keys; a row is done once exactly
-    // topk keys reach its threshold (all ballots of a step are formed before they are counted).
-    for (int bit = 31; bit >= 0; --bit) {
-      bool all = true;
-      static_for<J>([&](auto jj) {
-        const uint32_t cand = thr[jj] | (1u << bit);
-        uint64_t bl[MAXS];
-        static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(hi[jj][s] >= cand); });
-        int cnt = 0;
-        static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
-        const bool take = !done[jj] && cnt >= topk;
-        thr[jj] = take ? cand : thr[jj];
-        done[jj] = done[jj] || (take && cnt == topk);
-        all = all && done[jj];
-      });
-      if (all) break;
+    if (all) break;
+  }
+  static_for<J>([&](auto jj) {
+    if (done[jj]) return;   // rows past T
+    if (cnum[jj] == topk) {
+      thr[jj] = lb[jj];
+      done[jj] = exact[jj] = true;
+    } else if (cnum[jj] <= 64) {
+      thr[jj] = th[jj];
+      exact[jj] = ex[jj];
+      done[jj] = true;
+    } else {
+      thr[jj] = keep_above(lb[jj], p2[jj]);
+      top[jj] = p2[jj];
     }
-    static_for<J>([&](auto jj) {
-      const int r = r0 + jj;
-      if (i0 + r < T) {
-        // a row left undone after bit 0 ties in its high halves at the boundary
-        finish_row(r, thr[jj], done[jj]);
+  });
+}
+
+constexpr int kScoreRows = 32;    // query blocks per scores workgroup (two matrix-core tiles)
+constexpr int kScoreKeys = 128;   // key blocks per scores workgroup
+
+template <int D>
+__global__ __launch_bounds__(256, 3) void scores_kernel(const double* __restrict__ qhat,
+                                                        const double* __restrict__ khatT, int T, int nrb, int ncb,
+                                                        double inv_sqrt_d, uint64_t* __restrict__ keys) {
+  constexpr int KS = D / 4;    // matrix-core steps over the channels
+  constexpr int QS = KS / 4;   // steps per quarter tile
+  constexpr int QP = D + 4;    // LDS row pitch of q_hat (doubles): rows li and li + 8 share banks
+  __shared__ double qs[kScoreRows * QP];
+  // consecutive workgroups (row blocks of one key range of one head) run on one XCD, whose L2
+  // then holds that part of k_hat
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / (nrb * ncb), cb = (lid / nrb) % ncb, i0 = (lid % nrb) * kScoreRows;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lk = lane >> 4;
+  // the workgroup's q_hat rows (rows past T repeat row T - 1; their scores are not stored)
+  for (int x = tid; x < kScoreRows * D / 2; x += 256) {
+    const int r = x / (D / 2), c = 2 * (x % (D / 2));
+    const double* src = qhat + ((size_t)bh * T + min(i0 + r, T - 1)) * D + c;
+    qs[r * QP + c] = src[0];
+    qs[r * QP + c + 1] = src[1];
+  }
+  const double* kb = khatT + (size_t)bh * D * T;   // the head's k_hat^T (a scalar base)
+  const int t_end = min((T + 15) >> 4, (cb + 1) * (kScoreKeys / 16));
+  // quarter tiles: the k_hat operand of steps q*QS .. q*QS + QS - 1 of key tile tt goes to
+  // buffer q, loaded two quarters ahead of its multiplies and used by both row tiles; step s
+  // adds a uniform 4 s T to the lane's offset lk T + j, so the loads share one offset register
+  double kv[4][QS];
+  auto load_quarter = [&](double(&dst)[QS], int tt, int q) {
+    const int voff = lk * T + min(16 * tt + li, T - 1);
+    static_for<QS>([&](auto s) { dst[s] = kb[(size_t)(4 * (q * QS + s)) * T + voff]; });
+  };
+  const int t0 = cb * (kScoreKeys / 16) + w;
+  if (t0 < t_end) {
+    load_quarter(kv[0], t0, 0);
+    load_quarter(kv[1], t0, 1);
+  }
+  __syncthreads();
+  const double* qa = qs + li * QP + lk;   // row li of the first row tile, channel 4 s + lk
+  for (int tt = t0; tt < t_end; tt += 4) {
+    // per row tile two accumulators (even / odd steps): four independent chains in flight
+    f64x4 a0 = f64x4{0.0, 0.0, 0.0, 0.0}, a1 = a0, b0 = a0, b1 = a0;
+    static_for<4>([&](auto q) {
+      // each quarter's LDS operand reads stay in that quarter (hoisting them all spills)
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (q < 2) load_quarter(kv[q + 2], tt, q + 2);
+      else if (tt + 4 < t_end) load_quarter(kv[q - 2], tt + 4, q - 2);
+      static_for<QS / 2>([&](auto s) {
+        constexpr int k0 = 4 * (q * QS + 2 * s), k1 = k0 + 4;
+        a0 = mfma_f64(qa[k0], kv[q][2 * s], a0);
+        b0 = mfma_f64(qa[16 * QP + k0], kv[q][2 * s], b0);
+        a1 = mfma_f64(qa[k1], kv[q][2 * s + 1], a1);
+        b1 = mfma_f64(qa[16 * QP + k1], kv[q][2 * s + 1], b1);
+      });
+    });
+    const f64x4 sa = a0 + a1, sb = b0 + b1;
+    const int j = 16 * tt + li;
+    static_for<4>([&](auto r) {
+      const int i = i0 + 4 * r + lk;   // accumulator r holds tile row 4r + lane/16
+      if (j < T) {
+        if (i < T) keys[((size_t)bh * T + i) * T + j] = score_key(sa[int(r)] * inv_sqrt_d);
+        if (i + 16 < T) keys[((size_t)bh * T + i + 16) * T + j] = score_key(sb[int(r)] * inv_sqrt_d);
       }
     });
-  }
-
-  if constexpr (SOFT) {
-    for (int r = w; r < R; r += NW) {
-      if (i0 + r >= T) break;
-      double p[MAXS];
-      static_for<MAXS>([&](auto s) {
-        const int j = 64 * s + lane;
-        p[s] = j < T ? key_score(keys_s[r * T + j]) : 0.0;   // already divided by sqrt(d)
-      });
-      const size_t row = (size_t)bh * T + i0 + r;
-      soft_row<MAXS>(p, T, topk, 1.0, tau, soft_mask + row * T, lambda + row, lane);
-    }
   }
 }
 
-// LDS for the score keys of one workgroup: R rows of T keys.
-constexpr size_t kTopkLdsBudget = 160 * 1024;
+// Emits one row of the LUT and the mask from the row's keys and the threshold found on their
+// high halves: the low halves are searched when the high halves tie at the boundary (exact
+// false); keys above the threshold are all taken, keys equal to it fill the rest in
+// increasing j.
+template <int MAXS>
+__device__ __forceinline__ void emit_row(const uint64_t (&key)[MAXS], uint32_t thr_hi, bool exact, int T, int topk,
+                                         int32_t* __restrict__ lut_row, uint8_t* __restrict__ mask_row, int lane,
+                                         uint64_t lt_mask) {
+  uint64_t thr = (uint64_t)thr_hi << 32;
+  if (!exact) {
+    // low 32 bits among the keys whose high half equals thr_hi; keys above it count as base
+    int base_cnt = 0;
+    uint32_t lo[MAXS];
+    static_for<MAXS>([&](auto s) {
+      const uint32_t hs = (uint32_t)(key[s] >> 32);
+      base_cnt += ballot_count(hs > thr_hi);
+      lo[s] = hs == thr_hi ? (uint32_t)key[s] : 0u;   // 0 never reaches a candidate
+    });
+    uint32_t thr_lo = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr_lo | (1u << bit);
+      uint64_t bl[MAXS];
+      static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(lo[s] >= cand); });
+      int cnt = base_cnt;
+      static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
+      if (cnt >= topk) {
+        thr_lo = cand;
+        if (cnt == topk) break;
+      }
+    }
+    thr |= thr_lo;
+  }
+  int need = topk;
+  static_for<MAXS>([&](auto s) { need -= ballot_count(key[s] > thr); });
+  int base = 0;
+  static_for<MAXS>([&](auto s) {
+    const int j = 64 * s + lane;
+    const uint64_t eq = __builtin_amdgcn_ballot_w64(key[s] == thr);
+    const int n_eq = __popcll(eq);
+    const int take = n_eq < need ? n_eq : need;
+    const bool on = key[s] > thr || (key[s] == thr && __popcll(eq & lt_mask) < take);
+    need -= take;
+    const uint64_t bmask = __builtin_amdgcn_ballot_w64(on);
+    const int at = base + __popcll(bmask & lt_mask);
+    if (on && at < topk) lut_row[at] = j;   // exactly topk are on; the test only bounds the store
+    base += __popcll(bmask);
+    if (j < T) mask_row[j] = on ? 1 : 0;
+  });
+}
 
-// Soft-mask arguments of the fused SoftTop-k phase (unused by the plain router).
+// Waves per SIMD the select kernel is compiled for: six where a row's keys take few registers,
+// one for the soft mask over 4096 keys (whose fp64 scores fill the registers).
+template <int MAXS, bool SOFT>
+constexpr int select_waves() { return MAXS <= 8 ? 6 : (MAXS <= 24 ? 4 : (MAXS <= 32 || !SOFT ? 2 : 1)); }
+
+template <int MAXS, bool SOFT>
+__global__ __launch_bounds__(256, (select_waves<MAXS, SOFT>())) void select_kernel(
+    const uint64_t* __restrict__ keys, long long rows, int T, int topk, int32_t* __restrict__ lut,
+    uint8_t* __restrict__ mask, double tau, float* __restrict__ soft_mask, float* __restrict__ lambda) {
+  __shared__ uint32_t cscr[4][64];   // candidate compaction, one row per wave
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + w;   // bh * T + i
+  if (row >= rows) return;                                // the whole wave
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const uint64_t* krow = keys + row * T;
+  uint64_t key[MAXS];
+  uint32_t hi[1][MAXS];
+  static_for<MAXS>([&](auto s) {
+    const int j = 64 * s + lane;
+    key[s] = j < T ? krow[j] : 0ull;   // 0 is below every score key
+    hi[0][s] = (uint32_t)(key[s] >> 32);
+  });
+  uint32_t thr[1] = {0u};   // bits of the high-half threshold decided so far
+  int top[1] = {31};        // highest bit still to decide
+  bool done[1] = {false}, exact[1] = {false};
+  if (topk <= 64) prune_rows<1, MAXS>(hi, thr, top, done, exact, topk, cscr[w], lane, lt_mask);
+  if (!done[0]) {
+    // largest high-half threshold reached by at least topk keys (all ballots of a step are
+    // formed before they are counted)
+    for (int bit = top[0]; bit >= 0; --bit) {
+      const uint32_t cand = thr[0] | (1u << bit);
+      uint64_t bl[MAXS];
+      static_for<MAXS>([&](auto s) { bl[s] = __builtin_amdgcn_ballot_w64(hi[0][s] >= cand); });
+      int cnt = 0;
+      static_for<MAXS>([&](auto s) { cnt += __popcll(bl[s]); });
+      if (cnt >= topk) {
+        thr[0] = cand;
+        if (cnt == topk) {
+          exact[0] = true;
+          break;
+        }
+      }
+    }
+  }
+  emit_row<MAXS>(key, thr[0], exact[0], T, topk, lut + row * topk, mask + row * T, lane, lt_mask);
+  if constexpr (SOFT) {
+    double p[MAXS];
+    static_for<MAXS>([&](auto s) {
+      const int j = 64 * s + lane;
+      p[s] = j < T ? key_score(key[s]) : 0.0;   // already divided by sqrt(d)
+    });
+    soft_row<MAXS>(p, T, topk, 1.0, tau, soft_mask + row * T, lambda + row, lane);
+  }
+}
+
+// Soft-mask arguments of the SoftTop-k step (unused by the plain router).
 struct SoftOut {
   double tau;
   float* mask;
   float* lambda;
 };
 
-template <int R, int MAXS, int D, bool SOFT, int NW = 4>
-static void launch_topk_s(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
+template <int MAXS, bool SOFT>
+static void launch_select(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
                           hipStream_t s) {
-  const size_t lds = (size_t)R * g.T * sizeof(uint64_t);
-  static bool attr_set = false;   // dynamic LDS above the 64 KB default
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)topk_kernel<R, MAXS, D, SOFT, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)kTopkLdsBudget);
-    attr_set = true;
-  }
-  dim3 grid((g.T + R - 1) / R, g.BH);
-  hipLaunchKernelGGL((topk_kernel<R, MAXS, D, SOFT, NW>), grid, dim3(64 * NW), lds, s, ws.qhat, ws.khatT, g.T, g.topk,
-                     1.0 / sqrt((double)g.D), t.lut, t.mask, so.tau, so.mask, so.lambda);
+  const long long rows = (long long)g.BH * g.T;
+  hipLaunchKernelGGL((select_kernel<MAXS, SOFT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ws.keys, rows,
+                     g.T, g.topk, t.lut, t.mask, so.tau, so.mask, so.lambda);
 }
 
-// Rows per workgroup R: 16 (one matrix-core tile) when the keys fit in the LDS budget, else
-// 8 or 4.  Candidate slots per lane MAXS: the smallest of 4, 8, 16, 24, 32, 64 that is at
-// least ceil(T / 64).  T <= 4096 leaves the pairs below.  The hard tiers whose keys allow one
-// workgroup per CU (16 rows above 8 slots, and 8 rows) run 8 waves per workgroup; the soft
-// phase keeps 4 waves and 8 rows, which ran faster.
+// The scores, then the row selection with MAXS slots per lane: the smallest of 4, 8, 16, 24,
+// 32, 64 that is at least ceil(T / 64) (T <= 4096).
 template <int D, bool SOFT>
 static void launch_topk(const Geometry& g, const sla2_tensors& t, const Workspace& ws, const SoftOut& so,
                         hipStream_t s) {
-  int R = 16;
-  while (R > 4 && (size_t)R * g.T * sizeof(uint64_t) > kTopkLdsBudget) R >>= 1;
+  const int nrb = (g.T + kScoreRows - 1) / kScoreRows, ncb = (g.T + kScoreKeys - 1) / kScoreKeys;
+  hipLaunchKernelGGL(scores_kernel<D>, dim3((unsigned)(nrb * ncb * g.BH)), dim3(256), 0, s, ws.qhat, ws.khatT, g.T,
+                     nrb, ncb, 1.0 / sqrt((double)g.D), ws.keys);
   const int S = (g.T + 63) / 64;
-  // the soft phase runs long fp64 chains per row: above 8 slots per lane, 8 rows per workgroup
-  // leave room for two workgroups per CU
-  if (SOFT && S > 8 && R > 8) R = 8;
-  if (R == 16 && S <= 4) launch_topk_s<16, 4, D, SOFT>(g, t, ws, so, s);
-  else if (R == 16 && S <= 8) launch_topk_s<16, 8, D, SOFT>(g, t, ws, so, s);
-  else if (R == 16 && S <= 16) launch_topk_s<16, 16, D, SOFT, 8>(g, t, ws, so, s);
-  else if (R == 16) launch_topk_s<16, 24, D, SOFT, 8>(g, t, ws, so, s);   // 16 rows fit only T <= 1280: S <= 20
-  else if (R == 8 && S <= 16) launch_topk_s<8, 16, D, SOFT>(g, t, ws, so, s);
-  else if (R == 8 && S <= 24) launch_topk_s<8, 24, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);
-  else if (R == 8 && S <= 32) launch_topk_s<8, 32, D, SOFT, SOFT ? 4 : 8>(g, t, ws, so, s);
-  else if constexpr (SOFT) launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);   // 8 rows would spill
-  else if (R == 8) launch_topk_s<8, 64, D, SOFT, 8>(g, t, ws, so, s);
-  else launch_topk_s<4, 64, D, SOFT>(g, t, ws, so, s);
+  if (S <= 4) launch_select<4, SOFT>(g, t, ws, so, s);
+  else if (S <= 8) launch_select<8, SOFT>(g, t, ws, so, s);
+  else if (S <= 16) launch_select<16, SOFT>(g, t, ws, so, s);
+  else if (S <= 24) launch_select<24, SOFT>(g, t, ws, so, s);
+  else if (S <= 32) launch_select<32, SOFT>(g, t, ws, so, s);
+  else launch_select<64, SOFT>(g, t, ws, so, s);
 }
 
 template <typename Tin, int D>

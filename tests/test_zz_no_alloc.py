@@ -56,7 +56,7 @@ def test_route_noalloc_matches_route_on_two_calls():
 
 def test_route_noalloc_rejects_sizes_beyond_its_scratch():
     from sparse_linear_attention_pool_amd import binding as Bn
-    w = I.CONFIGS["C3"]   # 40 x 1182 query blocks: far beyond the 32 MiB scratch
+    w = I.CONFIGS["C3"]   # 40 x 1182 query blocks: far beyond the 64 MiB scratch
     p = params_for(w)
     with pytest.raises(Bn.SLA2Error) as e:
         Bn.sla2_route_noalloc(p, {})
