@@ -25,8 +25,10 @@ namespace sla2 {
 // ---------------------------------------------------------------------------------------
 // bf16, d = 128: one workgroup per (chunk of kChunk key blocks, head), 256 threads.
 // Thread (c = tid % 16, r0 = tid / 16) holds columns 8c..8c+7 of rows r0 + 16p, p = 0..3
-// (a 16-lane row of a wave holds one token); the next block's K and V are loaded while the
-// current one is processed.
+// (a 16-lane row of a wave holds one token).  Block j's V is copied straight into LDS (tile
+// j % 2) while block j - 1 is processed, and its K into registers (set j % 2) while block j - 2
+// is: both copies have a whole block's work to land.  The block loop is unrolled by two so that
+// the tile and register set are fixed at compile time.
 // phi and V go to LDS token-major (256-byte rows, rswz layout); the operands whose contraction index
 // runs down those rows (tokens) are read with the transposing LDS reads.  Wave w computes the
 // 4 x 4 tiles (a-tiles 4*(w/2).., c-tiles 4*(w%2)..) of D[a][c] = sum_t phi[t][a] V[t][c] with
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
   // token-major tiles of 256-byte rows in the rswz layout (sla2_lds.hpp): phi hi, phi lo, V
   __shared__ __attribute__((aligned(16))) uint8_t phiS[64 * 256];
   __shared__ __attribute__((aligned(16))) uint8_t phiLoS[64 * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t vS[64 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t vS0[64 * 256];   // V of even blocks
+  __shared__ __attribute__((aligned(16))) uint8_t vS1[64 * 256];   // V of odd blocks
   __shared__ float zred[16 * D];
   __shared__ float wred[4];
 
@@ -88,22 +91,35 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
   float zs = 0.f;
 
   const int j_lo = chunk * kChunk, j_hi = min(T, j_lo + kChunk);
-  auto load_kv = [&](int j, u32x4 (&kw)[4], u32x4 (&vw)[4]) {
+  // rows past N load row 0 (phase 1 zeroes them): no select waits for the data here
+  auto load_k = [&](int j, u32x4 (&kd)[4]) {
     static_for<4>([&](auto p) {
       const int row = kBlock * j + r0 + 16 * p;
-      const bool ok = row < N;
-      const size_t off = ((size_t)bh * N + (ok ? row : 0)) * D + 8 * c;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(k + off);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(v + off);
-      kw[p] = ok ? a : u32x4{0, 0, 0, 0};
-      vw[p] = ok ? b : u32x4{0, 0, 0, 0};
+      kd[p] = *reinterpret_cast<const u32x4*>(k + ((size_t)bh * N + (row < N ? row : 0)) * D + 8 * c);
     });
   };
-  u32x4 kw[4], vw[4];
-  load_kv(j_lo, kw, vw);
+  // V rows of this head; copies past its N rows read as zeros (the buffer's range check)
+  const __amdgpu_buffer_rsrc_t vsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + (size_t)bh * N * D), 0, N * D * 2, 0x00020000);
+  const int wofs = 1024 * __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 1 KB of each 4 KB
+  auto dma_v = [&](int j, uint8_t* dst) {
+    static_for<4>([&](auto P) {
+      // LDS chunk qd = 16 row + pc holds column chunk pc ^ rswz(row) of token 64 j + row
+      const int qd = tid + 256 * P, row = qd >> 4, pc = qd & 15;
+      lds_dma(vsrc, dst + 4096 * P + wofs, (kBlock * j + row) * (2 * D) + 16 * (pc ^ rswz(row)), 0);
+    });
+  };
+  u32x4 kw[2][4];
+  dma_v(j_lo, vS0);
+  load_k(j_lo, kw[0]);
+  if (j_lo + 1 < j_hi) load_k(j_lo + 1, kw[1]);
+  // the first block needs these anyway; waiting here keeps the compiler's wait counts inside the
+  // loop those of its steady state (merged with this entry, they would drain the copies in flight)
+  wait_dma();
 
-  for (int j = j_lo; j < j_hi; ++j) {
-    // ---- phase 1: K~, exp, row sums; V and phi (hi/lo) to LDS; z partials; block maxima
+  auto block = [&](auto B, int j) {
+    uint8_t* const vS = B ? vS1 : vS0;
+    // ---- phase 1: K~, exp, row sums; phi (hi/lo) to LDS; z partials; block maxima
     float kt[4][8];
     bool valid[4];
     float amax = 0.f;
@@ -114,8 +130,8 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       valid[p] = kBlock * j + r0 + 16 * p < N;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kt[p][2 * e] = valid[p] ? bf16_lo(kw[p][e]) - mu[2 * e] : 0.f;
-        kt[p][2 * e + 1] = valid[p] ? bf16_hi(kw[p][e]) - mu[2 * e + 1] : 0.f;
+        kt[p][2 * e] = valid[p] ? bf16_lo(kw[B][p][e]) - mu[2 * e] : 0.f;
+        kt[p][2 * e + 1] = valid[p] ? bf16_hi(kw[B][p][e]) - mu[2 * e + 1] : 0.f;
       }
       float mx = kt[p][0];
 #pragma unroll
@@ -142,15 +158,21 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       const int r = r0 + 16 * p;
       *reinterpret_cast<u32x4*>(rswz_chunk(phiS, r, c)) = u32x4{pw[0], pw[1], pw[2], pw[3]};
       *reinterpret_cast<u32x4*>(rswz_chunk(phiLoS, r, c)) = u32x4{pl[0], pl[1], pl[2], pl[3]};
-      *reinterpret_cast<u32x4*>(rswz_chunk(vS, r, c)) = vw[p];
     });
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
     amax = wave_max(amax);
     if (lane == 0) wred[w] = amax;
-    // next block's K and V stream in while this one finishes
-    if (j + 1 < j_hi) load_kv(j + 1, kw, vw);
-    __syncthreads();
+    wait_dma();   // this wave's part of block j's V (and every older load) has landed
+    // barriers that only hand over LDS: a __syncthreads() here would also drain the copies
+    // started below before the next block
+    lds_barrier();
+    // block j + 1's V into the other tile (last read before the previous barrier) and block
+    // j + 2's K into the registers phase 1 just consumed.  Past the chunk's last block they copy
+    // that block again (from L2; nothing reads it): every path then issues the same copies, so
+    // the compiler's wait counts are those of the steady state.
+    dma_v(min(j + 1, j_hi - 1), B ? vS0 : vS1);
+    load_k(min(j + 2, j_hi - 1), kw[B]);
 
     // ---- phase 2: codes of K~ and phi, z, h tiles, V^T
     if constexpr (FP8) {
@@ -288,8 +310,18 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
             u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
       });
     }
-    __syncthreads();
+    lds_barrier();
+  };
+  // pairs of blocks with no exit between them, so that the only way back to an even block is
+  // through an odd one (the compiler's wait counts then assume that order); an odd count ends
+  // with one more even block
+  const int npair = (j_hi - j_lo) >> 1;
+  for (int q = 0; q < npair; ++q) {
+    block(std::integral_constant<int, 0>{}, j_lo + 2 * q);
+    block(std::integral_constant<int, 1>{}, j_lo + 2 * q + 1);
   }
+  if ((j_hi - j_lo) & 1) block(std::integral_constant<int, 0>{}, j_hi - 1);
+  wait_dma();   // no copy into this workgroup's LDS outlives it
 
   float* hp = hpart + ((size_t)bh * P + chunk) * D * D;
 #pragma unroll

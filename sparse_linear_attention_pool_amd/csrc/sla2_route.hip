@@ -21,8 +21,9 @@ namespace sla2 {
 // scale and the e4m3 codes of Q.  Rows past N count as zero and receive code 0.
 // Thread (c = tid % CPR, r0 = tid / CPR) loads the 16-byte chunk c of rows r0 + RPP p.  Its
 // fp64 column partials go to LDS, where thread j then sums column j % D of Q (j < D) or K over
-// the row groups.  The FP8 codes re-read the block's Q rows (from L2) once the scale is known,
-// rather than holding them in registers.
+// the row groups.  The FP8 codes come from the block's Q rows still held in registers as packed
+// bf16 (16 VGPRs): re-reading them once the scale was known missed L2 for a third of the rows
+// while the rest of the inputs streamed through.
 // ---------------------------------------------------------------------------------------
 template <typename Tin, int D, bool FP8>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
@@ -117,9 +118,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin* __restrict__ q, co
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = kBlock * i + r0 + p * RPP;
-      const bool ok = row < N;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(q + (head + (ok ? row : 0)) * D + c * VEC);
-      const u32x4 w4 = ok ? a : u32x4{0, 0, 0, 0};   // rows past N: code 0
+      const u32x4 w4 = qw[p];   // rows past N hold 0: code 0
       float y[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
