@@ -179,8 +179,13 @@ __global__ __launch_bounds__(256, 3) void project_kernel(
   constexpr int CT = D / 64;         // output tiles per wave
   constexpr int EPT = R * D / 256;   // pooled elements per thread
   constexpr int PB = 16;             // token-sum partials loaded per batch
+  // pooled rows in LDS: channel c of row r at r * RP + (c / KS) * (KS + 1) + c % KS, so that the
+  // 16 rows and the lane groups' runs of KS channels read in one step fall in distinct banks
+  constexpr int RP = D == 128 ? 134 : 70;
+  static_assert(4 * (KS + 1) <= RP, "row pitch holds the padded runs");
+  auto rix = [](int r, int c) { return r * RP + (c / KS) * (KS + 1) + c % KS; };
   __shared__ double mu_s[D];
-  __shared__ double rows[R][D + 1];
+  __shared__ double rows[R * RP];
   const int bh = blockIdx.y, i0 = blockIdx.x * R, which = blockIdx.z, tid = threadIdx.x;
   const int P32 = (T + 31) / 32;
   const double* __restrict__ sums = which ? ksum : qsum;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(256, 3) void project_kernel(
         k_pool[idx] = (float)v;
       }
     }
-    rows[r][c] = v;
+    rows[rix(r, c)] = v;
   });
   __syncthreads();
 
@@ -242,10 +247,10 @@ __global__ __launch_bounds__(256, 3) void project_kernel(
     for (int x = tid; x < R * D; x += 256) {
       if (which == 0) {
         const int r = x / D, c = x % D;
-        if (i0 + r < T) qhat[((size_t)bh * T + i0 + r) * D + c] = rows[r][c];
+        if (i0 + r < T) qhat[((size_t)bh * T + i0 + r) * D + c] = rows[rix(r, c)];
       } else {
         const int c = x / R, r = x % R;
-        if (i0 + r < T) khatT[((size_t)bh * D + c) * T + i0 + r] = rows[r][c];
+        if (i0 + r < T) khatT[((size_t)bh * D + c) * T + i0 + r] = rows[rix(r, c)];
       }
     }
     return;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(256, 3) void project_kernel(
   static_for<CT>([&](auto t) { acc[t] = f64x4{0.0, 0.0, 0.0, 0.0}; });
   if (which == 0) {
     static_for<KS>([&](auto s) {
-      const double xa = rows[li][KS * lk + s];
+      const double xa = rows[li * RP + lk * (KS + 1) + s];
       static_for<CT>([&](auto t) { acc[t] = mfma_f64(xa, w_at_use(wf[t][s]), acc[t]); });
     });
     // acc[t][r] = q_hat[i0 + 4 r + lk][16 ct + li]
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(256, 3) void project_kernel(
     });
   } else {
     static_for<KS>([&](auto s) {
-      const double xa = rows[li][KS * lk + s];
+      const double xa = rows[li * RP + lk * (KS + 1) + s];
       static_for<CT>([&](auto t) { acc[t] = mfma_f64(w_at_use(wf[t][s]), xa, acc[t]); });
     });
     // acc[t][r] = k_hat[i0 + li][16 ct + 4 r + lk]
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(256, 3) void scores_kernel(const double* __restrict
                                                         double inv_sqrt_d, uint64_t* __restrict__ keys) {
   constexpr int KS = D / 4;    // matrix-core steps over the channels
   constexpr int QS = KS / 4;   // steps per quarter tile
-  constexpr int QP = D + 4;    // LDS row pitch of q_hat (doubles): rows li and li + 8 share banks
+  constexpr int QP = D + 2;    // LDS row pitch of q_hat (doubles): 16 rows x 4 lane groups hit 64 banks
   __shared__ double qs[kScoreRows * QP];
   // consecutive workgroups (row blocks of one key range of one head) run on one XCD, whose L2
   // then holds that part of k_hat
