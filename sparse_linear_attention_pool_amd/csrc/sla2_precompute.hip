@@ -137,16 +137,18 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, kt[p][e]);
       mx = row16_max(mx);
+      const float mxl = mx * kLog2e;
       float sm = 0.f, ex[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        ex[e] = __builtin_amdgcn_exp2f((kt[p][e] - mx) * kLog2e);
+        ex[e] = __builtin_amdgcn_exp2f(fmaf(kt[p][e], kLog2e, -mxl));   // 2^((k - max) log2 e)
         sm += ex[e];
         amax = fmaxf(amax, fabsf(kt[p][e]));
       }
       sm = row16_sum(sm);
       const float inv = valid[p] ? 1.f / sm : 0.f;
       uint32_t pw[4], pl[4];
+      float y[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a0 = ex[2 * e] * inv, a1 = ex[2 * e + 1] * inv;
@@ -154,10 +156,18 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         zp[2 * e + 1] += a1;
         pw[e] = pack_bf16x2(a0, a1);
         pl[e] = pack_bf16x2(a0 - bf16_lo(pw[e]), a1 - bf16_hi(pw[e]));
+        y[2 * e] = clamp_fp8(a0 * kPhiCodeScale);
+        y[2 * e + 1] = clamp_fp8(a1 * kPhiCodeScale);
       }
       const int r = r0 + 16 * p;
       *reinterpret_cast<u32x4*>(rswz_chunk(phiS, r, c)) = u32x4{pw[0], pw[1], pw[2], pw[3]};
       *reinterpret_cast<u32x4*>(rswz_chunk(phiLoS, r, c)) = u32x4{pl[0], pl[1], pl[2], pl[3]};
+      // e4m3 codes of 448 phi from the fp32 values: features 8c..8c+7 = 32s + 8g' + e with
+      // s = c / 4, g' = c % 4 go to bytes 32g' + 8s + e of the row
+      u32x2 codes;
+      codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
+      codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + kBlock * j + r) * D + 32 * (c & 3) + 8 * (c >> 2)) = codes;
     });
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
@@ -190,27 +200,6 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
         const int row = kBlock * j + r0 + 16 * p;
         *reinterpret_cast<u32x2*>(k8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
-      });
-    }
-    {
-      // phi from its bf16 hi + lo parts in LDS (within 2^-16 of the fp32 value); features
-      // 8c..8c+7 = 32s + 8g' + e with s = c / 4, g' = c % 4 go to bytes 32g' + 8s + e
-      static_for<4>([&](auto p) {
-        const int r = r0 + 16 * p;
-        float y[8];
-        const u32x4 hv = *reinterpret_cast<const u32x4*>(rswz_chunk(phiS, r, c));
-        const u32x4 lv = *reinterpret_cast<const u32x4*>(rswz_chunk(phiLoS, r, c));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t hw = hv[e], lw = lv[e];
-          y[2 * e] = clamp_fp8((bf16_lo(hw) + bf16_lo(lw)) * kPhiCodeScale);
-          y[2 * e + 1] = clamp_fp8((bf16_hi(hw) + bf16_hi(lw)) * kPhiCodeScale);
-        }
-        u32x2 codes;
-        codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
-        codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
-        const int row = kBlock * j + r0 + 16 * p;
-        *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + row) * D + 32 * (c & 3) + 8 * (c >> 2)) = codes;
       });
     }
     if (tid < D) {
