@@ -206,11 +206,10 @@ def test_lut_rows_longer_than_a_wave(mode):
 
 @pytest.mark.parametrize("N", [57000, 90000, 128000, 150000, 262144])
 def test_router_tiers_up_to_the_largest_sequence(N):
-    # T = 891, 1407, 2000, 2344 and 4096 blocks: the Top-k kernel's 16-slot tier at 16 rows per
-    # workgroup, its 24-, 32- and 64-slot tiers at 8 rows, and the 64-slot tier at 4 rows (fewer
-    # rows as the score rows outgrow the LDS; the 16- and 8-row tiers here run 8 waves); 3%
-    # routed, so k_sel reaches 123 and the forward reads its LUT rows from memory.  Router,
-    # quantiser and sampled query blocks.
+    # T = 891, 1407, 2000, 2344 and 4096 blocks: the row selection's 16-, 24-, 32- and 64-slot
+    # instances (keys per lane; 2344 fills 37 of 64 slots) after the scores kernel's partial key
+    # ranges; 3% routed, so k_sel reaches 123: above 64 the selection skips its narrowing step,
+    # and the forward reads its LUT rows from memory.  Router, quantiser and sampled query blocks.
     w = I.make_workload("C2", grid=None, N=N, H=1, seed=47, name=f"router tiers N={N}")
     inp = I.generate(w)
     out = run_gpu(w, inp)

@@ -99,8 +99,9 @@ def test_soft_topk_every_block_and_one_block():
 
 @pytest.mark.parametrize("N", [57000, 75600, 128000, 262144])
 def test_soft_topk_large_sequences(N):
-    """T = 891, 1182, 2000, 4096: the soft phase's 16-, 24-, 32- and 64-slot tiers (8 or 4 rows
-    per workgroup; T = 1182 is the C3 sequence length); 96 sampled rows checked."""
+    """T = 891, 1182, 2000, 4096: the soft selection's 16-, 24-, 32- and 64-slot instances (the
+    64-slot one at one wave per SIMD; T = 1182 is the C3 sequence length); 96 sampled rows
+    checked."""
     w = I.make_workload("C2", grid=None, N=N, H=1, seed=48, name=f"soft tiers N={N}")
     inp = I.generate(w)
     T = (N + 63) // 64
