@@ -173,7 +173,8 @@ int sla2_route_soft(const sla2_params *p, const sla2_tensors *t, float tau, floa
  * SLA2_BF16, lut; writes h_sum, z_sum, h and z (when given), and in FP8 mode k8, k_scale.
  * For SLA2_BF16 it also stages into the workspace what the fused forward reads: V^T tiles,
  * e4m3 codes of 448 phi(K~), a bf16 image of h_sum^T and, per query block, the sum of z_j
- * over its routed blocks (hence the lut). */
+ * over its routed blocks (hence the lut).  So for SLA2_BF16 this call follows sla2_route; running
+ * its LUT-free part beside the router on a second stream was measured and gave no gain. */
 int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Fused sparse + linear + mix forward (SLA2 page, sections 3 and 6: sparse attention over
