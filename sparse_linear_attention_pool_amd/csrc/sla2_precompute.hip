@@ -91,13 +91,25 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
   float zs = 0.f;
 
   const int j_lo = chunk * kChunk, j_hi = min(T, j_lo + kChunk);
-  // rows past N load row 0 (phase 1 zeroes them): no select waits for the data here
+  // Memory goes through buffer descriptors of this head's tensors, with 32-bit offsets.  K rows
+  // past N read as zeros (phase 1 zeroes their K~), so no select waits for the data here; the
+  // range check covers the per-lane offset, so the row offset goes there.  The code and V^T
+  // stores, always in range, keep the block offset in a scalar register.
+  const __amdgpu_buffer_rsrc_t ksrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + (size_t)bh * N * D), 0, N * D * 2, 0x00020000);
+  const int koff = (r0 * D + 8 * c) * 2;   // row r0 + 16 p of block j: + (64 j + 16 p) * 2D bytes
   auto load_k = [&](int j, u32x4 (&kd)[4]) {
     static_for<4>([&](auto p) {
-      const int row = kBlock * j + r0 + 16 * p;
-      kd[p] = *reinterpret_cast<const u32x4*>(k + ((size_t)bh * N + (row < N ? row : 0)) * D + 8 * c);
+      kd[p] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, koff + (kBlock * j + 16 * p) * (2 * D), 0, 0);
     });
   };
+  const int tile8 = T * kBlock * D;   // bytes of one head's e4m3 codes (K8, phi)
+  const __amdgpu_buffer_rsrc_t phsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(phik8 + (size_t)bh * tile8), 0, tile8, 0x00020000);
+  const int phoff = r0 * D + 32 * (c & 3) + 8 * (c >> 2);
+  const __amdgpu_buffer_rsrc_t k8src = __builtin_amdgcn_make_buffer_rsrc(
+      FP8 ? (void*)(k8 + (size_t)bh * tile8) : (void*)phik8, 0, FP8 ? tile8 : 0, 0x00020000);
+  const int k8off = r0 * D + 8 * c;
   // V rows of this head; copies past its N rows read as zeros (the buffer's range check)
   const __amdgpu_buffer_rsrc_t vsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(v + (size_t)bh * N * D), 0, N * D * 2, 0x00020000);
@@ -156,8 +168,8 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         zp[2 * e + 1] += a1;
         pw[e] = pack_bf16x2(a0, a1);
         pl[e] = pack_bf16x2(a0 - bf16_lo(pw[e]), a1 - bf16_hi(pw[e]));
-        y[2 * e] = clamp_fp8(a0 * kPhiCodeScale);
-        y[2 * e + 1] = clamp_fp8(a1 * kPhiCodeScale);
+        y[2 * e] = a0 * kPhiCodeScale;   // phi <= 1: |y| <= 448, no saturation needed
+        y[2 * e + 1] = a1 * kPhiCodeScale;
       }
       const int r = r0 + 16 * p;
       *reinterpret_cast<u32x4*>(rswz_chunk(phiS, r, c)) = u32x4{pw[0], pw[1], pw[2], pw[3]};
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       u32x2 codes;
       codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
       codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
-      *reinterpret_cast<u32x2*>(phik8 + ((size_t)bh * T * kBlock + kBlock * j + r) * D + 32 * (c & 3) + 8 * (c >> 2)) = codes;
+      __builtin_amdgcn_raw_buffer_store_b64(codes, phsrc, phoff, (kBlock * j + 16 * p) * D, 0);   // row r
     });
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[r0 * D + 8 * c + e] = zp[e];
@@ -194,12 +206,13 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       static_for<4>([&](auto p) {
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = clamp_fp8(div_by_scale(kt[p][e], inv_s));
+        // |K~| <= bm and s = RN(bm / 448), so |y| <= 448 (1 + 2^-23), which e4m3 rounds to 448:
+        // no saturation needed
+        for (int e = 0; e < 8; ++e) y[e] = div_by_scale(kt[p][e], inv_s);
         u32x2 codes;
         codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
         codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
-        const int row = kBlock * j + r0 + 16 * p;
-        *reinterpret_cast<u32x2*>(k8 + ((size_t)bh * T * kBlock + row) * D + 8 * c) = codes;
+        __builtin_amdgcn_raw_buffer_store_b64(codes, k8src, k8off, (kBlock * j + 16 * p) * D, 0);   // row r0 + 16p
       });
     }
     if (tid < D) {
@@ -290,13 +303,16 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
       // key = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4).  Each 16-lane group
       // takes 16 columns of one (s, gg); the four groups of a wave take gg = 0..3 of the same
       // columns, so each column receives 64 contiguous bytes per store.
-      uint16_t* vtj = vt + ((size_t)bh * T + j) * D * kBlock;
+      const __amdgpu_buffer_rsrc_t vtsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vt + (size_t)bh * T * D * kBlock), 0, T * D * kBlock * 2, 0x00020000);
+      const int vtoff = ((16 * (w >> 1) + l16) * kBlock + 32 * (w & 1) + 8 * g) * 2;
       static_for<4>([&](auto pp) {
         const int ct = 2 * pp + (w >> 1), s = w & 1, gg = g;
         const u32x2 lo4 = lds_read_tr16_rswz(vS, 32 * s + 4 * gg, 16 * ct, l16);
         const u32x2 hi4 = lds_read_tr16_rswz(vS, 32 * s + 16 + 4 * gg, 16 * ct, l16);
-        *reinterpret_cast<u32x4*>(vtj + (size_t)(16 * ct + l16) * kBlock + 32 * s + 8 * gg) =
-            u32x4{lo4.x, lo4.y, hi4.x, hi4.y};
+        // vt[j][16 ct + l16][32 s + 8 gg ..]: the lane part in vtoff, block and pass in the scalar
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo4.x, lo4.y, hi4.x, hi4.y}, vtsrc, vtoff,
+                                               (j * D + 32 * pp) * (kBlock * 2), 0);
       });
     }
     lds_barrier();
