@@ -649,7 +649,18 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[L::STAGE];   // stage of even LUT entries
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[L::STAGE];   // stage of odd LUT entries
-  __shared__ float alphaS[D];
+  // alpha of the head and Z_tot - Z_R(i), per feature, for the epilogue.  When a stage is larger
+  // than the H^T image (native Q.K^T: 40 KB stages), they go to the spare end of the epilogue's
+  // stage after the loop, so that the workgroup takes exactly 80 KB of LDS and two fit a CU's
+  // 160 KB; otherwise they have arrays of their own, written before the loop.
+  constexpr bool kSpare = L::STAGE >= 128 * 256 + 2 * D * (int)sizeof(float);
+  float* alphaS;
+  float* zdS;
+  if constexpr (!kSpare) {
+    __shared__ float alphaArr[D], zdArr[D];
+    alphaS = alphaArr;
+    zdS = zdArr;
+  }
 
   const int lid = xcd_remap(blockIdx.x, A.nblocks);
   // uniform indices in scalar registers, so per-block scalars load through the scalar cache
@@ -709,7 +720,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // Z_tot - Z_R(i) per feature, for the epilogue's denominator (loaded now, with the first tile)
   const float zd = tid < D ? A.z_sum[(size_t)bh * D + tid] - A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
 
-  if (tid < D) alphaS[tid] = alv;   // read in the epilogue, after several barriers
+  if constexpr (!kSpare) {
+    if (tid < D) alphaS[tid] = alv;   // read in the epilogue, after several barriers
+  }
   // the last routed block is partial iff it is block T-1 and N is not a multiple of 64
   const bool last_partial = (lut_entry<LUT_REG>(lutv, lutG, topk - 1) == A.T - 1) && (A.N % kBlock != 0);
 
@@ -728,8 +741,9 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // The first tile and every query-operand load complete here, before the loop: a wait for a
   // first use inside the loop could not tell them from the copies in flight there.
   wait_dma();
-  __shared__ float zdS[D];
-  if (tid < D) zdS[tid] = zd;
+  if constexpr (!kSpare) {
+    if (tid < D) zdS[tid] = zd;
+  }
   lds_barrier();
 
   for (int r = 0; r < topk; r += 2) {
@@ -796,6 +810,17 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // ---------------- epilogue ----------------
   // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
+  if constexpr (kSpare) {
+    // past the H^T image: that region last held a tile consumed before the last barrier, and
+    // no copy is in flight
+    alphaS = reinterpret_cast<float*>((Hs == smem1 ? smem1 : smem0) + 128 * 256);
+    zdS = alphaS + D;
+    if (tid < D) {
+      alphaS[tid] = alv;
+      zdS[tid] = zd;
+    }
+    lds_barrier();
+  }
   fwd_epilogue<FP8, QT>(A, st, qo, Hs, Hs + 64 * 256, direct, alphaS, zdS, bh, qrow, qok, l16, g, topk);
 }
 
