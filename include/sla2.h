@@ -169,12 +169,12 @@ int sla2_route_soft(const sla2_params *p, const sla2_tensors *t, float tau, floa
                     float *lambda, void *stream);
 
 /* Linear-branch precompute (SLA page, sections 2-3: h_j = phi(K_j)^T V_j, z_j =
- * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v, k_mean and, for
- * SLA2_BF16, lut; writes h_sum, z_sum, h and z (when given), and in FP8 mode k8, k_scale.
- * For SLA2_BF16 it also stages into the workspace what the fused forward reads: V^T tiles,
- * e4m3 codes of 448 phi(K~), a bf16 image of h_sum^T and, per query block, the sum of z_j
- * over its routed blocks (hence the lut).  So for SLA2_BF16 this call follows sla2_route; running
- * its LUT-free part beside the router on a second stream was measured and gave no gain. */
+ * rowsum phi(K_j)^T) plus the FP8 quantisation of K~.  Reads k, v and k_mean (not the lut);
+ * writes h_sum, z_sum, h and z (when given), and in FP8 mode k8, k_scale.  For SLA2_BF16 it
+ * also stages into the workspace what the fused forward reads: V^T tiles, e4m3 codes of
+ * 448 phi(K~), z_j of every block and a bf16 image of h_sum^T.  It needs only sla2_route's
+ * k_mean (running it beside the router's Top-k on a second stream was measured and gave no
+ * gain: both fill the CUs' LDS). */
 int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Fused sparse + linear + mix forward (SLA2 page, sections 3 and 6: sparse attention over

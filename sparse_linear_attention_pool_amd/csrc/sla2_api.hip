@@ -329,7 +329,6 @@ int sla2_linear_precompute(const sla2_params* p, const sla2_tensors* t, void* st
     REQUIRE(t->k8, "k8");
     REQUIRE(t->k_scale, "k_scale");
   }
-  if (g.bf16) REQUIRE(t->lut, "lut");   // the column sums of phi(K~) over each row's routed blocks
   return hip_status(launch_precompute(g, *t, ws, (hipStream_t)stream), fn);
 }
 

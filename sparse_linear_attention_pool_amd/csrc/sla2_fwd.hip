@@ -40,7 +40,9 @@ struct FwdArgs {
   const uint8_t* phik8;   // [BH, T*64, D] e4m3 codes of 448 phi(K~), features permuted
   const int32_t* lut;     // [BH, T, topk]
   const uint16_t* hbf;    // [BH, D, D] bf16 LDS image of H^T = h_sum (see Workspace::hbf)
-  const float* zrout;     // [BH, T, D] Z_R(i): sum of z_j over the routed blocks of row i
+  const float* zblk;      // [BH, T, D] z_j of every key block
+  float* zrout;           // [BH, T, D] Z_R(i) = sum of z_j over the routed blocks of row i, stored
+                          // for the backward pass with os (else unused)
   const float* z_sum;     // [BH, D]
   const float* alpha;     // [H, D]
   const float* k_mean;    // [BH, D] (lse of the native mode is shifted to the smoothed keys)
@@ -211,9 +213,10 @@ template <bool FP8, bool LUT_REG, int QT, int STG, bool PV8>
 __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st, uint8_t* smem0, uint8_t* smem1, int lutv,
                                               float& ksc, const int32_t* lutG, int r,
                                               int topk, int bh, int l16, int g, int tid, const QueryOps<QT>& qo,
-                                              float cq, bool mask, const TileSrc& src) {
+                                              float cq, bool mask, const TileSrc& src, float& zacc) {
   constexpr int NT = 256 / QT;
   using L = FwdLds<FP8, NT, PV8>;
+  constexpr int D = 128;
   // the two stages are separate LDS objects and the stage roles are fixed per instantiation,
   // so the compiler can see that this block's reads never touch the copy in flight
   const uint8_t* stage = STG == 0 ? smem0 : smem1;
@@ -222,9 +225,11 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   // (block r-1) was consumed before the last barrier; it lands while this block is processed
   uint8_t* next = STG == 0 ? smem1 : smem0;
   float ksc_next = 1.f;
+  float znext = 0.f;   // z_j of the next block: a load that lands with its tile copy
   if (r + 1 < topk) {
     const int jn = lut_entry<LUT_REG>(lutv, lutG, r + 1);
     if constexpr (FP8) ksc_next = A.k_scale[(size_t)bh * A.T + jn];
+    if (tid < D) znext = A.zblk[((size_t)bh * A.T + jn) * D + tid];
     dma_tile<FP8, NT, PV8>(A, src, jn, tid, next);
   } else {
     dma_himage<NT>(src, tid, next);
@@ -423,6 +428,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   wait_dma();
   lds_barrier();
   ksc = ksc_next;
+  if (r + 1 < topk) zacc += znext;   // Z_R(i) in LUT order
 }
 
 // One unrouted block for the direct form of the linear branch (a large share of the blocks
@@ -687,6 +693,10 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   const TileSrc src = tile_src(A, bh);
   const int j0 = __builtin_amdgcn_readfirstlane(lutG[0]);
   float ksc = FP8 ? A.k_scale[(size_t)bh * A.T + j0] : 1.f;
+  // Z_R(i) = sum of z_j over the routed blocks, added in LUT order by threads tid < D (feature
+  // tid) as the loop walks the row: each z_j loads with its block's tile copy
+  float zacc = tid < D ? A.zblk[((size_t)bh * A.T + j0) * D + tid] : 0.f;
+  const float zsum = tid < D ? A.z_sum[(size_t)bh * D + tid] : 0.f;
   dma_tile<FP8, NT, PV8>(A, src, j0, tid, smem0);
 
   QueryOps<QT> qo;
@@ -717,9 +727,6 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
       qo.phb[qt][s] = __builtin_bit_cast(bf16x8, bw);
     }
   }
-  // Z_tot - Z_R(i) per feature, for the epilogue's denominator (loaded now, with the first tile)
-  const float zd = tid < D ? A.z_sum[(size_t)bh * D + tid] - A.zrout[((size_t)bh * A.T + i) * D + tid] : 0.f;
-
   if constexpr (!kSpare) {
     if (tid < D) alphaS[tid] = alv;   // read in the epilogue, after several barriers
   }
@@ -741,17 +748,14 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // The first tile and every query-operand load complete here, before the loop: a wait for a
   // first use inside the loop could not tell them from the copies in flight there.
   wait_dma();
-  if constexpr (!kSpare) {
-    if (tid < D) zdS[tid] = zd;
-  }
   lds_barrier();
 
   for (int r = 0; r < topk; r += 2) {
     fwd_iteration<FP8, LUT_REG, QT, 0, PV8>(A, st, smem0, smem1, lutv, ksc, lutG, r, topk, bh, l16, g, tid, qo, cq,
-                                       last_partial && r == topk - 1, src);
+                                       last_partial && r == topk - 1, src, zacc);
     if (r + 1 < topk)
       fwd_iteration<FP8, LUT_REG, QT, 1, PV8>(A, st, smem0, smem1, lutv, ksc, lutG, r + 1, topk, bh, l16, g, tid, qo,
-                                         cq, last_partial && r + 1 == topk - 1, src);
+                                         cq, last_partial && r + 1 == topk - 1, src, zacc);
   }
 
   // With more than half of the blocks routed, the complement H_tot - (routed part) would be a
@@ -810,17 +814,17 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
   // ---------------- epilogue ----------------
   // H^T (bf16 image copied during the last iteration) is in the stage after the last tile's
   const uint8_t* Hs = (topk & 1) ? smem1 : smem0;
+  // Z_tot - Z_R(i) per feature for the denominator; Z_R(i) also for the backward pass
+  if (tid < D && A.os != nullptr) A.zrout[((size_t)bh * A.T + i) * D + tid] = zacc;
   if constexpr (kSpare) {
     // past the H^T image: that region last held a tile consumed before the last barrier, and
     // no copy is in flight
     alphaS = reinterpret_cast<float*>((Hs == smem1 ? smem1 : smem0) + 128 * 256);
     zdS = alphaS + D;
-    if (tid < D) {
-      alphaS[tid] = alv;
-      zdS[tid] = zd;
-    }
-    lds_barrier();
+    if (tid < D) alphaS[tid] = alv;
   }
+  if (tid < D) zdS[tid] = zsum - zacc;
+  lds_barrier();
   fwd_epilogue<FP8, QT>(A, st, qo, Hs, Hs + 64 * 256, direct, alphaS, zdS, bh, qrow, qok, l16, g, topk);
 }
 
@@ -972,6 +976,7 @@ hipError_t launch_fwd(const Geometry& g, const sla2_tensors& t, const Workspace&
     A.vexp = g.pv8 ? ws.vexp : nullptr;
     A.v = (const uint16_t*)t.v;
     A.phik8 = ws.phik8;
+    A.zblk = ws.zblk;
     A.zrout = ws.zrout;
     A.lut = t.lut;
     A.hbf = ws.hbf;

@@ -459,31 +459,15 @@ __device__ __forceinline__ void reduce_sums_block(int blk, int bh, const float* 
   }
 }
 
-// The tail of the precompute in one launch: workgroups x < nred reduce the chunk partials
-// (entries 256 x .. 256 x + 255 of head y); with zblk given, workgroups x >= nred form
-//   Z_R(i) = sum of z_j over the routed blocks j of query-block row i, in LUT order,
-// for rows i = 2 (x - nred) + tid / 128, thread c = tid % 128 owning feature c (d = 128).  The
-// forward pass needs Z_R for the denominator of the linear branch over the unrouted blocks,
-// phi(q).(Z_tot - Z_R).  The two parts are independent and run side by side.
+// The tail of the precompute: workgroup x reduces entries 256 x .. 256 x + 255 of head y's chunk
+// partials (and writes the bf16 H^T image when hbf is given).  The per-row sums of z_j over the
+// routed blocks are formed by the forward pass as it walks each LUT row, so this pass never reads
+// the LUT.
 __global__ __launch_bounds__(256) void precompute_tail_kernel(const float* __restrict__ hpart,
                                                               const float* __restrict__ zpart, int P, int D,
-                                                              int nred, float* __restrict__ h_sum,
-                                                              float* __restrict__ z_sum, uint16_t* __restrict__ hbf,
-                                                              const float* __restrict__ zblk,
-                                                              const int32_t* __restrict__ lut, int T, int topk,
-                                                              float* __restrict__ zrout) {
-  const int bh = blockIdx.y;
-  if ((int)blockIdx.x < nred) {
-    reduce_sums_block(blockIdx.x, bh, hpart, zpart, P, D, h_sum, z_sum, hbf);
-    return;
-  }
-  const int i = 2 * (blockIdx.x - nred) + (threadIdx.x >> 7), c = threadIdx.x & 127;
-  if (i >= T) return;
-  const int32_t* row = lut + ((size_t)bh * T + i) * topk;
-  float s = 0.f;
-#pragma unroll 8
-  for (int x = 0; x < topk; ++x) s += zblk[((size_t)bh * T + row[x]) * 128 + c];
-  zrout[((size_t)bh * T + i) * 128 + c] = s;
+                                                              float* __restrict__ h_sum,
+                                                              float* __restrict__ z_sum, uint16_t* __restrict__ hbf) {
+  reduce_sums_block(blockIdx.x, blockIdx.y, hpart, zpart, P, D, h_sum, z_sum, hbf);
 }
 
 template <bool FP8, bool STORE, bool PV8 = false>
@@ -519,18 +503,16 @@ hipError_t launch_precompute(const Geometry& g, const sla2_tensors& t, const Wor
                        ws.zpart);
   }
   const int nred = (g.D * g.D + 255) / 256;
-  const int nz = g.bf16 ? (g.T + 1) / 2 : 0;   // Z_R rows, two per workgroup (bf16 modes, d = 128)
-  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred + nz, g.BH), dim3(256), 0, s, ws.hpart, ws.zpart, g.P, g.D,
-                     nred, t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr, ws.zblk, t.lut, g.T, g.topk,
-                     ws.zrout);
+  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred, g.BH), dim3(256), 0, s, ws.hpart, ws.zpart, g.P, g.D,
+                     t.h_sum, t.z_sum, g.bf16 ? ws.hbf : (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_sum_parts(const float* parts, const float* zparts, int P, int D, int BH, float* out,
                             float* zout, hipStream_t s) {
   const int nred = (D * D + 255) / 256;
-  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred, BH), dim3(256), 0, s, parts, zparts, P, D, nred, out, zout,
-                     (uint16_t*)nullptr, (const float*)nullptr, (const int32_t*)nullptr, 0, 0, (float*)nullptr);
+  hipLaunchKernelGGL(precompute_tail_kernel, dim3(nred, BH), dim3(256), 0, s, parts, zparts, P, D, out, zout,
+                     (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
