@@ -133,18 +133,28 @@ def compare(got: np.ndarray, ref: np.ndarray, max_abs: float, mean_rel: float = 
 PV8_DELTA = 3e-5   # relative gap between the kernel's fp32 scores / hardware exp2 and the oracle's fp64
 
 
-def pv8_flip_allowance(ref: dict, v: np.ndarray, lut: np.ndarray, d: int) -> np.ndarray:
-    """Per output element, what the low-bit P.V may differ by when a P code or a block's P
-    scale sits at a rounding boundary: the kernel forms the scores in fp32 and exp2 in hardware,
-    the oracle in fp64, so a P value within PV8_DELTA (relative) of an e4m3 rounding midpoint, or
-    a block max within PV8_DELTA of an integer, may be coded either way.  Each such key adds one
-    e4m3 step (2^-3 of its value) of p |V| / l.  Computed for the query blocks the oracle did."""
+def pv8_flip_allowance(ref: dict, v: np.ndarray, lut: np.ndarray, d: int, alpha: np.ndarray) -> np.ndarray:
+    """Per output element, what the low-bit P.V may differ by where a P code or a block's P scale
+    sits at a rounding boundary: the kernel forms the scores in fp32 and exp2 in hardware, the
+    oracle in fp64, so a P value within PV8_DELTA (relative) of an e4m3 rounding midpoint, or a
+    block max within PV8_DELTA of an integer (the block's P scale), may be coded either way.
+    Such a key k may contribute its other dequantised value: the allowance of element (q, f) is
+    alpha_f * sum over those keys of |p_alt - p| |V8_kf| / l_q, with p_alt the farthest of the
+    alternatives (the neighbouring code; at the other block scale, that scale's codes, saturation
+    at 448 included) and V8 the dequantised e4m3 V.  Zero for rows with no such key.  Computed
+    for the query blocks the oracle did."""
     from oracle import fp8_e4m3 as F8
     N = v.shape[0]
     T = O.num_blocks(N)
     allow = np.zeros((N, d))
-    va = np.abs(np.asarray(v, np.float64))
+    _, _, v8 = O.quantize_v_blocks(v)
+    va = np.abs(v8)
+    al = np.abs(np.asarray(alpha, np.float64))
     done = np.isfinite(ref["o"][:, 0])
+
+    def deq(xr, c):   # the oracle's dequantised P of log2 scores xr (relative) at block scale c
+        return F8.decode(F8.encode(np.exp2(xr - c + 8.0))) * np.exp2(c - 8.0)
+
     for i in range(T):
         rows = O.block_rows(i, N)
         if not done[rows].all():
@@ -154,19 +164,25 @@ def pv8_flip_allowance(ref: dict, v: np.ndarray, lut: np.ndarray, d: int) -> np.
         qd = F8.decode(ref["q8"][rows]) * np.float64(ref["q_scale"][i])
         kd = np.concatenate([F8.decode(ref["k8"][O.block_rows(j, N)]) * np.float64(ref["k_scale"][j]) for j in blocks])
         x = (qd @ kd.T) / np.sqrt(d) / np.log(2.0)
-        flag = np.zeros(x.shape, dtype=bool)
+        x = x - np.ceil(x.max(axis=1, keepdims=True))      # relative to the row's reference
+        dev = np.zeros(x.shape)                             # |p_alt - p| of each key
         col = 0
         for j in blocks:
             n_j = O.block_rows(j, N).stop - O.block_rows(j, N).start
             xb = x[:, col:col + n_j]
             M = xb.max(axis=1, keepdims=True)
-            y = np.exp2(xb - np.ceil(M) + 8.0)
-            flip = F8.encode(y * (1 - PV8_DELTA)) != F8.encode(y * (1 + PV8_DELTA))
-            scale_flip = np.ceil(M - PV8_DELTA * np.maximum(np.abs(M), 1)) != np.ceil(M + PV8_DELTA * np.maximum(np.abs(M), 1))
-            flag[:, col:col + n_j] = flip | scale_flip
+            c = np.ceil(M)
+            p0 = deq(xb, c)
+            tol = PV8_DELTA * np.maximum(np.abs(M), 1)
+            c_lo, c_hi = np.ceil(M - tol), np.ceil(M + tol)
+            worst = np.zeros(xb.shape)
+            for cc in (c_lo, c_hi):                         # the oracle's scale and, near an integer, the other
+                for f in (1.0 - PV8_DELTA, 1.0 + PV8_DELTA):  # either side of a code midpoint
+                    worst = np.maximum(worst, np.abs(deq(xb + np.log2(f), cc) - p0))
+            dev[:, col:col + n_j] = worst
             col += n_j
-        p = np.exp2(x - x.max(axis=1, keepdims=True))
-        allow[rows] = 2.0 ** -3 * ((flag * p) @ va[keys]) / p.sum(axis=1, keepdims=True)
+        l = np.exp2(x).sum(axis=1, keepdims=True)
+        allow[rows] = al[None, :] * ((dev @ va[keys]) / l)
     return allow
 
 
@@ -228,7 +244,7 @@ def check_head(w: I.Workload, inp: dict, out: dict, b: int, h: int, topk=None, s
     rows = np.isfinite(ref["o"][:, 0])
     tol = TOL_LOWP if w.dtype == "bf16" else TOL_F32
     if w.qk_mode == "fp8pv":
-        allow = pv8_flip_allowance(ref, inp["v"][b, h], out["lut"][b, h], w.d)
+        allow = pv8_flip_allowance(ref, inp["v"][b, h], out["lut"][b, h], w.d, inp["alpha"][h])
         compare(out["o"][b, h][rows], ref["o"][rows], what="o", allow=allow[rows], **tol)
     else:
         compare(out["o"][b, h][rows], ref["o"][rows], what="o", **tol)
