@@ -193,7 +193,9 @@ struct FwdState {
   f32x4 acc[QT][8];      // O_s^T: sum_s p_s V_s, features 16dt + 4g + rr
   f32x4 accl[QT][8];     // sum over routed keys of (phi(q).phi(k_s)) V_s, same layout
   float m_run[QT];       // running max (log2 units)
-  float l_run[QT];       // this lane's partial sum of p
+  float l_run[QT];       // low-bit P.V: this lane's partial sum of p
+  f32x4 lsum[QT];        // bf16 P.V: the sum of the bf16 P over the routed keys (every element
+                         // holds the sum for this lane's query), from products with a ones operand
 };
 
 // Operands of this lane's queries that stay in registers for the whole loop.
@@ -313,6 +315,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
       const float mnew = mx[qt] > st.m_run[qt] + 8.f ? (PV8 ? ceilf(mx[qt]) : mx[qt]) : st.m_run[qt];
       const float f = __builtin_amdgcn_exp2f(st.m_run[qt] - mnew);
       st.l_run[qt] *= f;
+      st.lsum[qt] *= f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) st.acc[qt][dt] *= f;
       st.m_run[qt] = mnew;
@@ -378,14 +381,13 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     // keys 32s + 16h + 4g + rr, as the bf16 B operands of the products below
     bf16x8 pop[QT][2], aop[QT][2];
     auto make_ops = [&](int qt, int s) {
-      float pv[8], av[8], psum = 0.f;
+      float pv[8], av[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           pv[4 * h + rr] = __builtin_amdgcn_exp2f(fmaf(S[qt][2 * s + h][rr], cj, -st.m_run[qt]));
           av[4 * h + rr] = Ph[qt][2 * s + h][rr];
-          psum += pv[4 * h + rr];
         }
       const uint32_t pw[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                               pack_bf16x2(pv[6], pv[7])};
@@ -393,7 +395,6 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
                               pack_bf16x2(av[6], av[7])};
       pop[qt][s] = __builtin_bit_cast(bf16x8, pw);
       aop[qt][s] = __builtin_bit_cast(bf16x8, aw);
-      st.l_run[qt] += psum;
     };
 
 #pragma unroll
@@ -412,6 +413,7 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
     // Steps k = 0..15 take key half s = k / 8 of feature tile dt = k % 8, so the two products
     // that accumulate into the same registers are eight steps apart.
     bf16x8 vq[16];
+    const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     static_for<kVReadAhead>([&](auto k) { vq[k] = vread(k % 8, k / 8); });
     static_for<16>([&](auto k) {
       if constexpr (k + kVReadAhead < 16) vq[k + kVReadAhead] = vread((k + kVReadAhead) % 8, (k + kVReadAhead) / 8);
@@ -420,6 +422,9 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
       for (int qt = 0; qt < QT; ++qt) {
         st.acc[qt][dt] = mfma_bf16(vq[k], pop[qt][sh], st.acc[qt][dt]);
         st.accl[qt][dt] = mfma_bf16(vq[k], aop[qt][sh], st.accl[qt][dt]);
+        // the row sum of P over key half sh: a ones A operand sums the 32 keys of the half,
+        // those of all four lane groups, on the matrix cores instead of the VALU
+        if constexpr (dt == 0) st.lsum[qt] = mfma_bf16(kOnes, pop[qt][sh], st.lsum[qt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -548,7 +553,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& A, const FwdState<QT
   constexpr int D = 128;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = rows4_sum(st.l_run[qt]);
+    const float l_tot = rows4_sum(st.l_run[qt]) + st.lsum[qt][0];   // one of the two is zero
     constexpr float kCodes2 = 1.f / (kPhiCodeScale * kPhiCodeScale);   // undo the code scales
     const float inv_l = 1.f / l_tot;
     // denominator over the unrouted blocks: phi(q).(Z_tot - Z_R), with the bf16 phi(q)
@@ -743,6 +748,7 @@ __global__ __launch_bounds__(256 / QT, 2) void fwd_mfma_kernel(FwdArgs A) {
     }
     st.m_run[qt] = -INFINITY;
     st.l_run[qt] = 0.f;
+    st.lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // The first tile and every query-operand load complete here, before the loop: a wait for a
