@@ -82,12 +82,14 @@ __device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
 }
 
 // ---------------------------------------------------------------- cross-lane
-// All-reduce over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+// All-reduce over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).  The max takes
+// v with both values of the swapped pair as one three-input max: fmaxf of the pair alone made the
+// compiler quiet both inputs first (two more instructions per stage).
 __device__ __forceinline__ float rows4_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = fmaxf(fmaxf(v, __uint_as_float(r[0])), __uint_as_float(r[1]));
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return fmaxf(fmaxf(v, __uint_as_float(s[0])), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float rows4_sum(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -301,9 +301,11 @@ __device__ __forceinline__ void fwd_iteration(const FwdArgs& A, FwdState<QT>& st
   bool raise_any = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float m = fmaxf(S[qt][0][0], S[qt][0][1]);
-    static_for<7>([&](auto u) {   // chained three-input maxima over the remaining 14 scores
-      constexpr int a = 2 + 2 * u, b = 3 + 2 * u;
+    // chained three-input maxima over the 16 scores, from -inf (a first two-input max made the
+    // compiler quiet both inputs first)
+    float m = -INFINITY;
+    static_for<8>([&](auto u) {
+      constexpr int a = 2 * u, b = 1 + 2 * u;
       m = fmaxf(fmaxf(m, S[qt][a / 4][a % 4]), S[qt][b / 4][b % 4]);
     });
     mx[qt] = rows4_max(m) * cj;
