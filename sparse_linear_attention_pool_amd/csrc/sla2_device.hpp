@@ -102,12 +102,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-// All-reduce within each 16-lane row: rotate by 8 and 4, then swap pairs and neighbours.
+// All-reduce within each 16-lane row: rotate by 8 and 4, then swap pairs and neighbours.  Each
+// stage is a three-input max with -inf as the third input: the two-input form made the compiler
+// quiet the moved value first, one more instruction per stage.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
-  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
-  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(fmaxf(v, -INFINITY), dpp<0x128>(v));   // row_ror:8
+  v = fmaxf(fmaxf(v, -INFINITY), dpp<0x124>(v));   // row_ror:4
+  v = fmaxf(fmaxf(v, -INFINITY), dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(fmaxf(v, -INFINITY), dpp<0xB1>(v));    // quad_perm [1,0,3,2]
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {

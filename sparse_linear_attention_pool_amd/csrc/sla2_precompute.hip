@@ -139,24 +139,27 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
     static_for<4>([&](auto p) {
+      // rows past N (read as zeros) get K~ = -mu here; they are left out where it matters: the
+      // block absmax and the K8 codes below take valid rows only, and their phi is zeroed by inv
       valid[p] = kBlock * j + r0 + 16 * p < N;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kt[p][2 * e] = valid[p] ? bf16_lo(kw[B][p][e]) - mu[2 * e] : 0.f;
-        kt[p][2 * e + 1] = valid[p] ? bf16_hi(kw[B][p][e]) - mu[2 * e + 1] : 0.f;
+        kt[p][2 * e] = bf16_lo(kw[B][p][e]) - mu[2 * e];
+        kt[p][2 * e + 1] = bf16_hi(kw[B][p][e]) - mu[2 * e + 1];
       }
       float mx = kt[p][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, kt[p][e]);
       mx = row16_max(mx);
       const float mxl = mx * kLog2e;
-      float sm = 0.f, ex[8];
+      float sm = 0.f, ex[8], am = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ex[e] = __builtin_amdgcn_exp2f(fmaf(kt[p][e], kLog2e, -mxl));   // 2^((k - max) log2 e)
         sm += ex[e];
-        amax = fmaxf(amax, fabsf(kt[p][e]));
+        am = fmaxf(am, fabsf(kt[p][e]));
       }
+      if (valid[p]) amax = fmaxf(amax, am);
       sm = row16_sum(sm);
       const float inv = valid[p] ? 1.f / sm : 0.f;
       uint32_t pw[4], pl[4];
@@ -210,8 +213,8 @@ __global__ __launch_bounds__(256, STORE ? 1 : 2) void precompute_bf16_kernel(
         // no saturation needed
         for (int e = 0; e < 8; ++e) y[e] = div_by_scale(kt[p][e], inv_s);
         u32x2 codes;
-        codes[0] = pack_fp8x4(y[0], y[1], y[2], y[3]);
-        codes[1] = pack_fp8x4(y[4], y[5], y[6], y[7]);
+        codes[0] = valid[p] ? pack_fp8x4(y[0], y[1], y[2], y[3]) : 0u;   // pad rows: code 0
+        codes[1] = valid[p] ? pack_fp8x4(y[4], y[5], y[6], y[7]) : 0u;
         __builtin_amdgcn_raw_buffer_store_b64(codes, k8src, k8off, (kBlock * j + 16 * p) * D, 0);   // row r0 + 16p
       });
     }
