@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
   // per-query record of the key side, and dden
   float* rec = A.qrec + ((size_t)bh * A.T + b) * kRec;
   if ((tid & 3) == 0) {
-    rec[x] = ok ? A.lse[trow] : 0.f;
+    rec[x] = ok ? A.lse[trow] : INFINITY;   // pad queries: P = 2^-inf = 0 on the key side
     rec[kBlock + x] = dq;   // 0 past N (dO is 0 there)
     A.dden[prow] = dden;
   }
@@ -487,11 +487,17 @@ __device__ __forceinline__ void q_iteration(const BwdArgs& A, f32x4 (&acc)[8], u
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int mt = 2 * s + h, key = 16 * mt + 4 * g + rr;
-          float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
-          if (key >= nvalid) p = 0.f;
+          const int mt = 2 * s + h;
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
           dv8[4 * h + rr] = p * (dP[mt][rr] - qo.dq_l) * fs;
         }
+      if (nvalid < kBlock) {   // the partial last block only: keys past N
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (16 * (2 * s + h) + 4 * g + rr >= nvalid) dv8[4 * h + rr] = 0.f;
+      }
       dso_[s] = pack8(dv8);
     };
     // operand reads run one key tile ahead of the products that use them
@@ -795,11 +801,13 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
 
   if (sparse) {
     const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
-    const int nq = min(kBlock, A.N - kBlock * i);
     // P and dS (times q_scale / sqrt(d), the factor of dK' = dS^T Q' / sqrt(d)) of query half s
     // (tiles 2s, 2s+1) as B operands, with the pair's lse and D_q at rows 16mt + 4g .. +3
     const float* rec = reinterpret_cast<const float*>(stg + klds::REC);
     const float cij = kLog2e * inv_sqrt_d * sq * ksc, fk = sq * inv_sqrt_d;
+    // P is 0 for pad keys (-inf added to the exponent) and pad queries (their recorded lse is
+    // +inf), with no per-element test
+    const float kbias = kok ? 0.f : -INFINITY;
     f32x4 S[4], dP[4], l4[2], d4[2];
     bf16x8 po[2], dso_[2];
     auto read_rec = [&](int s) {
@@ -813,11 +821,10 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
       float p8[8], d8[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int mt = 2 * s + h, q0 = 16 * mt + 4 * g;
+        const int mt = 2 * s + h;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cij, -l4[h][rr] * kLog2e));
-          if (q0 + rr >= nq || !kok) p = 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cij, fmaf(l4[h][rr], -kLog2e, kbias)));
           p8[4 * h + rr] = p;
           d8[4 * h + rr] = p * (dP[mt][rr] - d4[h][rr]) * fk;
         }
