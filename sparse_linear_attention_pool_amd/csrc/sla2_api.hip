@@ -405,7 +405,7 @@ int sla2_attention_bwd(const sla2_params* p, const sla2_tensors* t, const void* 
 }
 
 int sla2_selftest_mfma(int which, const void* a, const void* b, void* d, void* stream) {
-  if (which < 0 || which > 3) return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: which must be 0 to 3");
+  if (which < 0 || which > 4) return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: which must be 0 to 4");
   if (a == nullptr || b == nullptr || d == nullptr)
     return fail(SLA2_ERR_INVALID_ARG, "sla2_selftest_mfma: NULL operand");
   return hip_status(launch_selftest_mfma(which, a, b, d, (hipStream_t)stream), "sla2_selftest_mfma");

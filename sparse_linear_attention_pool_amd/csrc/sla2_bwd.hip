@@ -95,13 +95,6 @@ __device__ __forceinline__ bf16x8 op256(const uint8_t* base, int row, int s, int
                             *reinterpret_cast<const u32x4*>(base + row * 256 + 16 * ((4 * s + g) ^ (row & 15))));
 }
 
-// e4m3 (OCP: bias 7, no infinities, 0x7f / 0xff NaN never produced by the quantiser)
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  const float mag = e ? ldexpf(1.f + 0.125f * (float)m, (int)e - 7) : ldexpf((float)m, -9);
-  return (b & 0x80u) ? -mag : mag;
-}
-
 // Column of token x of a 64-block in the transposed tiles (the forward's V^T order): within
 // each 32-half, tokens 4gg + e sit at 8gg + e and tokens 16 + 4gg + e at 8gg + 4 + e.  A 16 x 16
 // product's output (token rows 4g + r of two adjacent 16-row tiles) then packs, without a
@@ -286,9 +279,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
 
   // e4m3 values of the Q and K~ codes (exact in bf16), transposed
   for (int which = 0; which < 2; ++which) {
-    const uint8_t* codes = (which == 0 ? A.q8 : A.k8) + prow * kD + c0;
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>((which == 0 ? A.q8 : A.k8) + prow * kD + c0);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) tr[(c0 + e) * kBlock + px] = f32_to_bf16(e4m3_value(codes[e]));
+    for (int q = 0; q < 8; ++q) {   // four codes per word
+      const f32x4 v = e4m3_decode4(codes[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tr[(c0 + 4 * q + e) * kBlock + px] = f32_to_bf16(v[e]);
+    }
     flush(which == 0 ? A.q8t : A.k8t);
   }
 

@@ -47,6 +47,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// The four e4m3 codes of w (byte k = code k) as floats, by the hardware conversion (OCP e4m3 on
+// gfx950, exact).  A GPU test pins it against the e4m3 definition on all 256 codes.
+__device__ __forceinline__ f32x4 e4m3_decode4(uint32_t w) {
+  return f32x4{__builtin_amdgcn_cvt_f32_fp8((int)w, 0), __builtin_amdgcn_cvt_f32_fp8((int)w, 1),
+               __builtin_amdgcn_cvt_f32_fp8((int)w, 2), __builtin_amdgcn_cvt_f32_fp8((int)w, 3)};
+}
+
 // Four floats -> four e4m3 codes (round to nearest even) in one dword, byte k = value k.
 // Callers clamp to +-448 first.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {

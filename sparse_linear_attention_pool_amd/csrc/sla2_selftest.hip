@@ -7,10 +7,16 @@ namespace sla2 {
 
 // which = 0: bf16 16x16x32; 1: e4m3 16x16x128; 2: fp64 16x16x4; 3: e4m3 16x16x128 with E8M0
 // scales, lane l's scale words after the 64 x 32 code bytes of a and of b, byte 2 of the word
-// selected for A (the form the low-bit P.V products use: op_sel picks the byte) and byte 0 for B.
+// selected for A (the form the low-bit P.V products use: op_sel picks the byte) and byte 0 for B;
+// 4: the e4m3 decode the kernels use, lane l decoding the four code bytes of word l of a.
 __global__ __launch_bounds__(64) void selftest_mfma_kernel(int which, const u32x4* a, const u32x4* b, float4* d) {
   const int l = threadIdx.x;
   f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (which == 4) {
+    r = e4m3_decode4(reinterpret_cast<const uint32_t*>(a)[l]);
+    d[l] = make_float4(r[0], r[1], r[2], r[3]);
+    return;
+  }
   if (which == 2) {
     const f64x4 r64 = mfma_f64(reinterpret_cast<const double*>(a)[l], reinterpret_cast<const double*>(b)[l],
                                f64x4{0.0, 0.0, 0.0, 0.0});

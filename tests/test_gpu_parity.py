@@ -319,6 +319,24 @@ def test_fp8_encoder_on_every_bf16_value():
     assert len(bad[0]) == 0, f"{len(bad[0])} codes differ, e.g. value {q[bad][:5]} gpu {got[bad][:5]} want {want[bad][:5]}"
 
 
+def test_fp8_decoder_on_every_code():
+    """The kernels' e4m3 decode (the hardware conversion) against the e4m3 definition on all 256
+    codes; the two NaN codes, which the quantiser never produces, decode to NaN."""
+    import torch
+    from oracle import fp8_e4m3 as F8
+    from sparse_linear_attention_pool_amd import binding as Bn
+    codes = np.arange(256, dtype=np.uint8)
+    a = torch.from_numpy(codes.copy()).cuda()
+    d = torch.zeros(256, dtype=torch.float32, device="cuda")
+    Bn.sla2_selftest_mfma(4, a, a, d)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy().astype(np.float64)
+    nan = (codes & 0x7F) == 0x7F
+    assert np.all(np.isnan(got[nan]))
+    want = F8.decode(codes[~nan])
+    assert np.array_equal(got[~nan], want), np.nonzero(got[~nan] != want)
+
+
 # ----------------------------------------------------------------------------- full sizes
 def _sampled_full(base, heads, blocks_per_head=6, **overrides):
     """Full-size run; parity of the listed heads on `blocks_per_head` sampled query blocks

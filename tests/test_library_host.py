@@ -267,3 +267,9 @@ def test_a_failing_hip_call_maps_to_err_hip(B):
     assert e.value.status == B.SLA2_ERR_HIP == -3
     assert "sla2_route_noalloc" in str(e.value) and "device" in str(e.value)
     assert B.lib.sla2_status_string(B.SLA2_ERR_HIP) == b"HIP runtime error"
+
+
+def test_selftest_rejects_unknown_modes_before_any_launch(B):
+    for which in (-1, 5):
+        assert B.lib.sla2_selftest_mfma(which, None, None, None, None) == B.SLA2_ERR_INVALID_ARG
+        assert b"which must be 0 to 4" in B.lib.sla2_last_error()
