@@ -476,6 +476,8 @@ __device__ __forceinline__ void q_iteration(const BwdArgs& A, f32x4 (&acc)[8], u
     // P^T and dS^T (times k_scale / sqrt(d), the factor of dQ' = dS K' / sqrt(d)) of key half s
     // (tiles 2s, 2s+1) as B operands
     const float cj = kLog2e * inv_sqrt_d * sq * ksc, fs = ksc * inv_sqrt_d;
+    // only fs P is needed here, so fs (> 0) enters the exponent: 2^(x - lse + log2 fs)
+    const float nl = __builtin_amdgcn_logf(fs) - qo.lse_l;
     f32x4 S[4], dP[4];
     bf16x8 dso_[2];
     auto half_ops = [&](int s) {
@@ -485,8 +487,8 @@ __device__ __forceinline__ void q_iteration(const BwdArgs& A, f32x4 (&acc)[8], u
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int mt = 2 * s + h;
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, -qo.lse_l));
-          dv8[4 * h + rr] = p * (dP[mt][rr] - qo.dq_l) * fs;
+          const float pf = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cj, nl));   // fs P
+          dv8[4 * h + rr] = pf * (dP[mt][rr] - qo.dq_l);
         }
       if (nvalid < kBlock) {   // the partial last block only: keys past N
 #pragma unroll
