@@ -188,14 +188,15 @@ int sla2_linear_precompute(const sla2_params *p, const sla2_tensors *t, void *st
  * next to its terms).
  * SLA2_F32 gathers the routed h_j, z_j; SLA2_BF16 evaluates phi(q) times the routed part of
  * H by re-association, as the sum over the routed keys s of (phi(q).phi(K~_s)) V_s (SLA page,
- * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and takes
- * the routed part of Z from the precompute.
+ * section 4), with phi(q) and phi(K~) as e4m3 codes of 448 phi (both phi <= 1), and sums
+ * the routed part of Z from the precompute's per-block z_j as it walks the LUT row.
  * SLA2_QK_PV_FP8_E4M3: the P.V products of both uses take e4m3 P (or phi-product codes) and
  * e4m3 V from the precompute, with their power-of-two scales applied by the matrix cores.
  * Training forward: when t->workspace_bwd is non-NULL (and the backward supports the params:
  * SLA2_BF16, SLA2_QK_FP8_E4M3, d = 128) the call also stores in it, per query, the sparse
- * output O_s, the linear output O_l (both bf16) and 1/(phi(q).Z_i + eps), which the backward
- * reads; a workspace_bwd that is not 256-byte aligned is SLA2_ERR_INVALID_ARG. */
+ * output O_s, the linear output O_l (both bf16) and 1/(phi(q).Z_i + eps), and per query block
+ * the routed part of Z (in the workspace), which the backward reads; a workspace_bwd that is
+ * not 256-byte aligned is SLA2_ERR_INVALID_ARG. */
 int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream);
 
 /* Backward pass (SLA2 page, appendix A: gradients of Q, K, V through phi(Q), phi(K) and the
@@ -208,8 +209,8 @@ int sla2_attention_fwd(const sla2_params *p, const sla2_tensors *t, void *stream
  * pages' backward is 16-bit, so a low-bit P.V forward has none here).
  * Reads what the three forward calls wrote for the same params and inputs: q, k, v, alpha,
  * k_mean, lut, mask, q8, q_scale, k8, k_scale, h_sum, z_sum, lse (so the forward must have
- * been given lse), the workspace, and the O_s, O_l and 1/den that a training forward (one given
- * this workspace_bwd) stored; h and z are not read.  Writes only workspace_bwd and the outputs.
+ * been given lse), the workspace, and the O_s, O_l, 1/den and routed part of Z that a training
+ * forward (one given this workspace_bwd) stored; h and z are not read.  Writes only workspace_bwd and the outputs.
  * The linear branch never forms H_i or dH_i per block: the query side re-associates the routed
  * part of dnum H_i^T over the routed key tiles, and each key block forms its dh_j as the total
  * minus one product per routing query block.
