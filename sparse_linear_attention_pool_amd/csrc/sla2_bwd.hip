@@ -152,7 +152,7 @@ struct BwdArgs {
   uint16_t* k8t;           // [BH, T, D, 64] e4m3 values of K8 transposed, vt_pos
   uint16_t* phkt;          // [BH, T, D, 64] phi(K~)^T, vt_pos (pad tokens 0)
   uint16_t* htimg;         // [BH, D, D] bf16 H_tot rows a (h_sum transposed), LDS image
-  float* qrec;             // [BH, T, 256] per query block: lse[64], D_q[64], zeros
+  float* qrec;             // [BH, T, 256] per query block: -lse log2(e) [64], D_q[64], zeros
   float* dden;             // [BH, 64T]
   int32_t* inv;            // [BH, T, T] query blocks routing to key block j, ascending
   int32_t* inv_cnt;        // [BH, T]
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
   // per-query record of the key side, and dden
   float* rec = A.qrec + ((size_t)bh * A.T + b) * kRec;
   if ((tid & 3) == 0) {
-    rec[x] = ok ? A.lse[trow] : INFINITY;   // pad queries: P = 2^-inf = 0 on the key side
+    rec[x] = ok ? -A.lse[trow] * kLog2e : -INFINITY;   // -lse log2(e); pad queries: P = 2^-inf = 0
     rec[kBlock + x] = dq;   // 0 past N (dO is 0 there)
     A.dden[prow] = dden;
   }
@@ -801,11 +801,11 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
   if (sparse) {
     const float inv_sqrt_d = 0.08838834764831845f;   // 1 / sqrt(128)
     // P and dS (times q_scale / sqrt(d), the factor of dK' = dS^T Q' / sqrt(d)) of query half s
-    // (tiles 2s, 2s+1) as B operands, with the pair's lse and D_q at rows 16mt + 4g .. +3
+    // (tiles 2s, 2s+1) as B operands, with the pair's -lse log2(e) and D_q at rows 16mt + 4g .. +3
     const float* rec = reinterpret_cast<const float*>(stg + klds::REC);
     const float cij = kLog2e * inv_sqrt_d * sq * ksc, fk = sq * inv_sqrt_d;
-    // P is 0 for pad keys (-inf added to the exponent) and pad queries (their recorded lse is
-    // +inf), with no per-element test
+    // P is 0 for pad keys (their scores start from -inf in the product's accumulator) and pad
+    // queries (their record holds -inf for -lse log2(e)), with no per-element test
     const float kbias = kok ? 0.f : -INFINITY;
     f32x4 S[4], dP[4], l4[2], d4[2];
     bf16x8 po[2], dso_[2];
@@ -823,7 +823,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
         const int mt = 2 * s + h;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cij, fmaf(l4[h][rr], -kLog2e, kbias)));
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[mt][rr], cij, l4[h][rr]));
           p8[4 * h + rr] = p;
           d8[4 * h + rr] = p * (dP[mt][rr] - d4[h][rr]) * fk;
         }
@@ -843,7 +843,7 @@ __device__ __forceinline__ void k_iteration(const BwdArgs& A, f32x4 (&acc)[16], 
     read_queries(std::integral_constant<int, 0>{});
     static_for<4>([&](auto mt) {
       if constexpr (mt + 1 < 4) read_queries(std::integral_constant<int, mt + 1>{});
-      S[mt] = mfma_fp8(qr[mt], ko.k8, f32x4{0.f, 0.f, 0.f, 0.f});
+      S[mt] = mfma_fp8(qr[mt], ko.k8, f32x4{kbias, kbias, kbias, kbias});
       dP[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) dP[mt] = mfma_bf16(da[mt][s], ko.v[s], dP[mt]);

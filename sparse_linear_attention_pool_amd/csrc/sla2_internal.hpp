@@ -58,7 +58,7 @@ struct BwdWorkspace {
   uint16_t* k8t;        // [BH, T, D, 64] e4m3 values of the K~ codes, transposed likewise
   uint16_t* phkt;       // [BH, T, D, 64] phi(K~), transposed likewise (pad tokens 0)
   uint16_t* htimg;      // [BH, D, D] bf16 h_sum transposed (rows a), in its LDS layout
-  float* qrec;          // [BH, T, 256] per query block: lse[64], D_q[64], zeros
+  float* qrec;          // [BH, T, 256] per query block: -lse log2(e) [64] (-inf past N), D_q[64], zeros
   float* dden;          // [BH, 64T]
   int32_t* inv;         // [BH, T, T] per key block: the query blocks routing to it, ascending
   int32_t* inv_cnt;     // [BH, T]
